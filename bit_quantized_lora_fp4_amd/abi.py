@@ -1,0 +1,288 @@
+"""ctypes binding of libfourtune.so (the C ABI declared in include/fourtune.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.
+PyTorch supplies device memory and the current HIP stream. Functions named like the
+C entry points take preallocated tensors; the short helpers below them allocate
+outputs and workspace with torch and call those.
+
+If the library is missing or cannot load, every call raises: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfourtune.so")
+
+FT_F32, FT_BF16 = 0, 1
+STATUS = {0: "FT_OK", 1: "FT_ERR_NULL", 2: "FT_ERR_SHAPE", 3: "FT_ERR_DTYPE", 4: "FT_ERR_ALIGN",
+          5: "FT_ERR_WORKSPACE", 6: "FT_ERR_UNSUPPORTED", 7: "FT_ERR_HIP"}
+
+c_i64, c_vp, c_sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+
+
+class FtMx4(ctypes.Structure):
+    _fields_ = [("codes", c_vp), ("scales", c_vp), ("rows", c_i64), ("cols", c_i64)]
+
+
+class FtLinear(ctypes.Structure):
+    _fields_ = [("r", FtMx4), ("lora_a", c_vp), ("lora_b", c_vp), ("stab_down", c_vp),
+                ("stab_up", c_vp), ("n", c_i64), ("k", c_i64), ("rank", c_i64),
+                ("stab_rank", c_i64)]
+
+
+class FourTuneError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        self.detail = detail
+
+
+_lib = None
+
+# name -> (restype, argtypes)
+_SIGS = {
+    "ft_mx4_codes_bytes": (c_sz, [c_i64, c_i64]),
+    "ft_mx4_scales_bytes": (c_sz, [c_i64, c_i64]),
+    "fourtune_quantize": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i64,
+                                         ctypes.POINTER(FtMx4), c_vp]),
+    "fourtune_linear_workspace_bytes": (c_sz, [c_i64, ctypes.POINTER(FtLinear)]),
+    "fourtune_linear_fwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), c_vp, ctypes.c_int, c_i64,
+                                           c_vp, ctypes.c_int, c_vp, ctypes.POINTER(FtMx4),
+                                           c_vp, c_sz, c_vp]),
+    "fourtune_linear_bwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), c_vp, ctypes.c_int, c_vp,
+                                           ctypes.c_int, c_vp, c_i64, c_vp, ctypes.c_int, c_vp,
+                                           c_vp, ctypes.POINTER(FtMx4), c_vp, c_sz, c_vp]),
+    "fourtune_mlp_workspace_bytes": (c_sz, [c_i64, ctypes.POINTER(FtLinear),
+                                            ctypes.POINTER(FtLinear)]),
+    "fourtune_mlp_fwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear), c_vp,
+                                        ctypes.c_int, c_i64, c_vp, ctypes.c_int, c_vp, c_vp, c_vp,
+                                        c_vp, c_vp, c_sz, c_vp]),
+    "fourtune_mlp_bwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear), c_vp,
+                                        ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_i64,
+                                        c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                        c_sz, c_vp]),
+    "fourtune_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "fourtune_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """Load libfourtune.so once; raise if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise FourTuneError(-1, f"{LIB_PATH} is not built; run "
+                                    "`python -m bit_quantized_lora_fp4_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def _check(status: int):
+    if status != 0:
+        raise FourTuneError(status, lib().fourtune_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the library must live on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FT_F32
+    if t.dtype == torch.bfloat16:
+        return FT_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+# ----------------------------------------------------------------------------- types
+@dataclass
+class Mx4:
+    """An MXFP4 tensor: codes [rows x cols/2] uint8, scales [ceil(rows/32) x cols/32] uint8."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    cols: int
+
+    @staticmethod
+    def empty(rows: int, cols: int, device="cuda") -> "Mx4":
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty(((rows + 31) // 32, cols // 32), dtype=torch.uint8, device=device)
+        return Mx4(codes, scales, rows, cols)
+
+    def struct(self) -> FtMx4:
+        return FtMx4(_ptr(self.codes), _ptr(self.scales), self.rows, self.cols)
+
+
+@dataclass
+class Linear:
+    """One W4A4G4 linear: Q(R) [n x k] and the bf16 low-rank factors A, B, L1, L2."""
+    rq: Mx4
+    A: torch.Tensor   # [r x k]
+    B: torch.Tensor   # [n x r]
+    L1: torch.Tensor  # [s x k]
+    L2: torch.Tensor  # [n x s]
+
+    @property
+    def n(self):
+        return self.rq.rows
+
+    @property
+    def k(self):
+        return self.rq.cols
+
+    @property
+    def rank(self):
+        return self.A.shape[0]
+
+    @property
+    def stab_rank(self):
+        return self.L1.shape[0]
+
+    def struct(self) -> FtLinear:
+        return FtLinear(self.rq.struct(), _ptr(self.A), _ptr(self.B), _ptr(self.L1),
+                        _ptr(self.L2), self.n, self.k, self.rank, self.stab_rank)
+
+
+# ----------------------------------------------------------------------------- C calls
+def ft_mx4_codes_bytes(rows: int, cols: int) -> int:
+    return lib().ft_mx4_codes_bytes(rows, cols)
+
+
+def ft_mx4_scales_bytes(rows: int, cols: int) -> int:
+    return lib().ft_mx4_scales_bytes(rows, cols)
+
+
+def fourtune_quantize(x: torch.Tensor, out: Mx4, stream=None, ld: Optional[int] = None):
+    rows, cols = x.shape
+    ld = x.stride(0) if ld is None else ld
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    s = out.struct()
+    _check(lib().fourtune_quantize(_ptr(x), _dt(x), rows, cols, ld, ctypes.byref(s),
+                                   _stream(stream)))
+
+
+def fourtune_linear_workspace_bytes(m: int, L: Linear) -> int:
+    s = L.struct()
+    return lib().fourtune_linear_workspace_bytes(m, ctypes.byref(s))
+
+
+def fourtune_linear_fwd(L: Linear, x: torch.Tensor, y: torch.Tensor, xl_saved: torch.Tensor,
+                        ws: torch.Tensor, xq_out: Optional[Mx4] = None, stream=None):
+    s = L.struct()
+    xq = xq_out.struct() if xq_out is not None else None
+    _check(lib().fourtune_linear_fwd(ctypes.byref(s), _ptr(x), _dt(x), x.shape[0], _ptr(y),
+                                     _dt(y), _ptr(xl_saved),
+                                     ctypes.byref(xq) if xq is not None else None,
+                                     _ptr(ws), ws.numel() if ws is not None else 0,
+                                     _stream(stream)))
+
+
+def fourtune_linear_bwd(L: Linear, dy: torch.Tensor, x: torch.Tensor, xl_saved: torch.Tensor,
+                        dx: torch.Tensor, d_lora_a: Optional[torch.Tensor],
+                        d_lora_b: Optional[torch.Tensor], ws: torch.Tensor,
+                        gq_out: Optional[Mx4] = None, stream=None):
+    s = L.struct()
+    gq = gq_out.struct() if gq_out is not None else None
+    _check(lib().fourtune_linear_bwd(ctypes.byref(s), _ptr(dy), _dt(dy), _ptr(x), _dt(x),
+                                     _ptr(xl_saved), x.shape[0], _ptr(dx), _dt(dx),
+                                     _ptr(d_lora_a), _ptr(d_lora_b),
+                                     ctypes.byref(gq) if gq is not None else None,
+                                     _ptr(ws), ws.numel() if ws is not None else 0,
+                                     _stream(stream)))
+
+
+def fourtune_mlp_workspace_bytes(m: int, fc1: Linear, fc2: Linear) -> int:
+    s1, s2 = fc1.struct(), fc2.struct()
+    return lib().fourtune_mlp_workspace_bytes(m, ctypes.byref(s1), ctypes.byref(s2))
+
+
+def fourtune_mlp_fwd(fc1: Linear, fc2: Linear, x: torch.Tensor, y: torch.Tensor,
+                     xl1_saved: torch.Tensor, pre_saved: torch.Tensor, hl2_saved: torch.Tensor,
+                     ws: torch.Tensor, h_debug: Optional[torch.Tensor] = None, stream=None):
+    s1, s2 = fc1.struct(), fc2.struct()
+    _check(lib().fourtune_mlp_fwd(ctypes.byref(s1), ctypes.byref(s2), _ptr(x), _dt(x),
+                                  x.shape[0], _ptr(y), _dt(y), _ptr(xl1_saved), _ptr(pre_saved),
+                                  _ptr(hl2_saved), _ptr(h_debug), _ptr(ws),
+                                  ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def fourtune_mlp_bwd(fc1: Linear, fc2: Linear, dy: torch.Tensor, x: torch.Tensor,
+                     xl1_saved: torch.Tensor, pre_saved: torch.Tensor, hl2_saved: torch.Tensor,
+                     dx: torch.Tensor, d_a1, d_b1, d_a2, d_b2, ws: torch.Tensor,
+                     dp_debug: Optional[torch.Tensor] = None, stream=None):
+    s1, s2 = fc1.struct(), fc2.struct()
+    _check(lib().fourtune_mlp_bwd(ctypes.byref(s1), ctypes.byref(s2), _ptr(dy), _dt(dy), _ptr(x),
+                                  _dt(x), _ptr(xl1_saved), _ptr(pre_saved), _ptr(hl2_saved),
+                                  x.shape[0], _ptr(dx), _dt(dx), _ptr(d_a1), _ptr(d_b1),
+                                  _ptr(d_a2), _ptr(d_b2), _ptr(dp_debug), _ptr(ws),
+                                  ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def fourtune_status_string(status: int) -> str:
+    return lib().fourtune_status_string(status).decode()
+
+
+def fourtune_last_error() -> str:
+    return lib().fourtune_last_error().decode()
+
+
+# ----------------------------------------------------------------------------- helpers
+def quantize(x: torch.Tensor, stream=None) -> Mx4:
+    out = Mx4.empty(x.shape[0], x.shape[1], device=x.device)
+    fourtune_quantize(x, out, stream=stream)
+    return out
+
+
+def make_linear(R: torch.Tensor, A: torch.Tensor, B: torch.Tensor, L1: torch.Tensor,
+                L2: torch.Tensor, stream=None) -> Linear:
+    """Quantize the frozen residual R once and bundle it with the low-rank factors."""
+    return Linear(quantize(R, stream=stream), A, B, L1, L2)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def linear_forward(L: Linear, x: torch.Tensor, y_dtype=torch.bfloat16, ws=None, xq_out=None,
+                   stream=None):
+    m = x.shape[0]
+    y = torch.empty((m, L.n), dtype=y_dtype, device=x.device)
+    xl = torch.empty((m, L.rank + L.stab_rank), dtype=torch.bfloat16, device=x.device)
+    ws = workspace(fourtune_linear_workspace_bytes(m, L), x.device) if ws is None else ws
+    fourtune_linear_fwd(L, x, y, xl, ws, xq_out=xq_out, stream=stream)
+    return y, xl
+
+
+def linear_backward(L: Linear, dy: torch.Tensor, x: torch.Tensor, xl: torch.Tensor,
+                    dx_dtype=torch.bfloat16, ws=None, gq_out=None, stream=None):
+    m = x.shape[0]
+    dx = torch.empty((m, L.k), dtype=dx_dtype, device=x.device)
+    da = torch.empty((L.rank, L.k), dtype=torch.float32, device=x.device)
+    db = torch.empty((L.n, L.rank), dtype=torch.float32, device=x.device)
+    ws = workspace(fourtune_linear_workspace_bytes(m, L), x.device) if ws is None else ws
+    fourtune_linear_bwd(L, dy, x, xl, dx, da, db, ws, gq_out=gq_out, stream=stream)
+    return dx, da, db

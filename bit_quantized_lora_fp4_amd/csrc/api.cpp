@@ -1,0 +1,341 @@
+// C ABI of the W4A4G4 linear layer: argument validation, workspace carving and kernel
+// launches on the caller's stream. No allocation, no synchronization, no global
+// mutable state besides the thread-local error text.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "fourtune.h"
+#include "launch.h"
+#include "gemm.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+ft_status fail(ft_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+ft_status ok() {
+  g_last_error[0] = '\0';
+  return FT_OK;
+}
+
+ft_status hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return FT_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(ft_dtype d) { return d == FT_F32 ? 4 : 2; }
+
+bool dtype_ok(ft_dtype d) { return d == FT_F32 || d == FT_BF16; }
+
+#define REQUIRE(cond, status, ...)            \
+  do {                                        \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define TRY(expr)                         \
+  do {                                    \
+    ft_status _s = (expr);                \
+    if (_s != FT_OK) return _s;           \
+  } while (0)
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- workspace carving
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = reinterpret_cast<T*>(base ? base + used : nullptr);
+    used += round_up(bytes, 256);
+    return p;
+  }
+};
+
+ft_status check_mx4(const ft_mx4* t, int64_t rows, int64_t cols, const char* name) {
+  REQUIRE(t != nullptr, FT_ERR_NULL, "%s: NULL ft_mx4", name);
+  REQUIRE(t->codes && t->scales, FT_ERR_NULL, "%s: NULL codes/scales", name);
+  REQUIRE(t->rows == rows && t->cols == cols, FT_ERR_SHAPE,
+          "%s: is [%lld x %lld], expected [%lld x %lld]", name, (long long)t->rows,
+          (long long)t->cols, (long long)rows, (long long)cols);
+  REQUIRE(aligned16(t->codes), FT_ERR_ALIGN, "%s: codes not 16-byte aligned", name);
+  return FT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ft_mx4_codes_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return (size_t)rows * (size_t)(cols / 2);
+}
+
+size_t ft_mx4_scales_bytes(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols < 0) return 0;
+  return (size_t)((rows + 31) / 32) * (size_t)(cols / 32);
+}
+
+const char* fourtune_status_string(ft_status s) {
+  switch (s) {
+    case FT_OK: return "ok";
+    case FT_ERR_NULL: return "null pointer";
+    case FT_ERR_SHAPE: return "bad shape";
+    case FT_ERR_DTYPE: return "bad dtype";
+    case FT_ERR_ALIGN: return "misaligned pointer";
+    case FT_ERR_WORKSPACE: return "workspace too small";
+    case FT_ERR_UNSUPPORTED: return "unsupported";
+    case FT_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* fourtune_last_error(void) { return g_last_error; }
+
+ft_status fourtune_quantize(const void* x, ft_dtype x_dt, int64_t rows, int64_t cols, int64_t ld,
+                            ft_mx4* out, void* stream) {
+  REQUIRE(dtype_ok(x_dt), FT_ERR_DTYPE, "quantize: unknown dtype %d", (int)x_dt);
+  REQUIRE(rows >= 0 && cols >= 0, FT_ERR_SHAPE, "quantize: negative size");
+  REQUIRE(cols % 32 == 0, FT_ERR_SHAPE, "quantize: cols=%lld not a multiple of 32", (long long)cols);
+  REQUIRE(ld >= cols, FT_ERR_SHAPE, "quantize: ld=%lld < cols=%lld", (long long)ld, (long long)cols);
+  REQUIRE((ld * (int64_t)elem_size(x_dt)) % 16 == 0, FT_ERR_ALIGN,
+          "quantize: row stride of %lld bytes not a multiple of 16", (long long)(ld * elem_size(x_dt)));
+  REQUIRE(rows < (int64_t)65535 * 32, FT_ERR_UNSUPPORTED, "quantize: rows=%lld too large", (long long)rows);
+  if (rows == 0 || cols == 0) return ok();
+  REQUIRE(x != nullptr, FT_ERR_NULL, "quantize: NULL x");
+  REQUIRE(aligned16(x), FT_ERR_ALIGN, "quantize: x not 16-byte aligned");
+  TRY(check_mx4(out, rows, cols, "quantize: out"));
+  TRY(hip_check(ft::launch_quantize(x, x_dt == FT_BF16, rows, cols, ld, out->codes, out->scales,
+                                    static_cast<hipStream_t>(stream)),
+                "quantize launch"));
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------- linear helpers
+ft_status check_linear(const ft_linear* L, const char* who) {
+  REQUIRE(L != nullptr, FT_ERR_NULL, "%s: NULL ft_linear", who);
+  REQUIRE(L->n > 0 && L->k > 0 && L->n % 32 == 0 && L->k % 32 == 0, FT_ERR_SHAPE,
+          "%s: n=%lld, k=%lld must be positive multiples of 32", who, (long long)L->n, (long long)L->k);
+  REQUIRE(L->rank >= 0 && L->stab_rank >= 0 && L->rank % 16 == 0 && L->stab_rank % 16 == 0,
+          FT_ERR_SHAPE, "%s: rank=%lld, stab_rank=%lld must be multiples of 16", who,
+          (long long)L->rank, (long long)L->stab_rank);
+  const int64_t rt = L->rank + L->stab_rank;
+  REQUIRE(rt % 32 == 0, FT_ERR_SHAPE, "%s: rank + stab_rank = %lld must be a multiple of 32", who, (long long)rt);
+  REQUIRE(rt <= 128, FT_ERR_UNSUPPORTED, "%s: rank + stab_rank = %lld > 128", who, (long long)rt);
+  TRY(check_mx4(&L->r, L->n, L->k, "linear: Q(R)"));
+  if (L->rank > 0) {
+    REQUIRE(L->lora_a && L->lora_b, FT_ERR_NULL, "%s: NULL LoRA factor", who);
+    REQUIRE(aligned16(L->lora_a) && aligned16(L->lora_b), FT_ERR_ALIGN, "%s: LoRA factor misaligned", who);
+  }
+  if (L->stab_rank > 0) {
+    REQUIRE(L->stab_down && L->stab_up, FT_ERR_NULL, "%s: NULL stabilizer factor", who);
+    REQUIRE(aligned16(L->stab_down) && aligned16(L->stab_up), FT_ERR_ALIGN, "%s: stabilizer factor misaligned", who);
+  }
+  return FT_OK;
+}
+
+ft_status check_tensor(const void* p, const char* who, const char* name) {
+  REQUIRE(p != nullptr, FT_ERR_NULL, "%s: NULL %s", who, name);
+  REQUIRE(aligned16(p), FT_ERR_ALIGN, "%s: %s not 16-byte aligned", who, name);
+  return FT_OK;
+}
+
+struct FwdLayout {
+  uint8_t* xq_codes;
+  uint8_t* xq_scales;
+  size_t bytes;
+};
+
+FwdLayout fwd_layout(void* ws, int64_t m, const ft_linear* L, bool need_xq) {
+  Carver c(ws);
+  FwdLayout f{};
+  if (need_xq) {
+    f.xq_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, L->k));
+    f.xq_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, L->k));
+  }
+  f.bytes = c.used;
+  return f;
+}
+
+struct BwdLayout {
+  ft::bf16_t* Ut;
+  ft::bf16_t* Dt;
+  uint8_t* gq_codes;
+  uint8_t* gq_scales;
+  ft::bf16_t* GB;
+  float* partials;
+  uint32_t* counters;
+  int splits, tiles;
+  size_t bytes;
+};
+
+BwdLayout bwd_layout(void* ws, int64_t m, const ft_linear* L, bool need_gq) {
+  Carver c(ws);
+  BwdLayout b{};
+  const int64_t rt = L->rank + L->stab_rank;
+  const int64_t rp = (L->rank + 31) / 32 * 32;
+  b.Ut = c.take<ft::bf16_t>((size_t)rt * L->n * 2);
+  b.Dt = c.take<ft::bf16_t>((size_t)rt * L->k * 2);
+  if (need_gq) {
+    b.gq_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, L->n));
+    b.gq_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, L->n));
+  }
+  b.GB = c.take<ft::bf16_t>((size_t)m * rt * 2);
+  b.tiles = ft::lora_grad_tiles(L->k, L->n);
+  b.splits = L->rank > 0 ? ft::lora_grad_splits(m, L->k, L->n) : 1;
+  b.partials = c.take<float>(b.splits > 1 ? (size_t)b.splits * rp * (L->k + L->n) * 4 : 0);
+  b.counters = c.take<uint32_t>((size_t)b.tiles * 4);
+  b.bytes = c.used;
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fourtune_linear_workspace_bytes(int64_t m, const ft_linear* L) {
+  if (L == nullptr || m < 0) return 0;
+  const size_t f = fwd_layout(nullptr, m, L, true).bytes;
+  const size_t b = bwd_layout(nullptr, m, L, true).bytes;
+  return f > b ? f : b;
+}
+
+ft_status fourtune_linear_fwd(const ft_linear* L, const void* x, ft_dtype x_dt, int64_t m, void* y,
+                              ft_dtype y_dt, void* xl_saved, ft_mx4* xq_out, void* ws,
+                              size_t ws_bytes, void* stream) {
+  const char* who = "linear_fwd";
+  TRY(check_linear(L, who));
+  REQUIRE(dtype_ok(x_dt) && dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m == 0) return ok();
+  const int64_t rt = L->rank + L->stab_rank;
+  TRY(check_tensor(x, who, "x"));
+  TRY(check_tensor(y, who, "y"));
+  if (rt > 0) TRY(check_tensor(xl_saved, who, "xl_saved"));
+  if (xq_out) TRY(check_mx4(xq_out, m, L->k, "linear_fwd: xq_out"));
+  const FwdLayout lay = fwd_layout(ws, m, L, xq_out == nullptr);
+  REQUIRE(lay.bytes == 0 || (ws != nullptr && ws_bytes >= lay.bytes), FT_ERR_WORKSPACE,
+          "%s: workspace of %zu bytes, %zu needed", who, ws_bytes, lay.bytes);
+  if (lay.bytes) REQUIRE(aligned16(ws), FT_ERR_ALIGN, "%s: workspace misaligned", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* xq_codes = xq_out ? xq_out->codes : lay.xq_codes;
+  uint8_t* xq_scales = xq_out ? xq_out->scales : lay.xq_scales;
+
+  ft::QuantDownArgs qd{};
+  qd.x = x; qd.M = m; qd.K = L->k; qd.ldx = L->k;
+  qd.codes = xq_codes; qd.scales = xq_scales;
+  qd.d0 = static_cast<const ft::bf16_t*>(L->lora_a);
+  qd.d1 = static_cast<const ft::bf16_t*>(L->stab_down);
+  qd.r0 = (int)L->rank; qd.rt = (int)rt;
+  qd.low = static_cast<ft::bf16_t*>(xl_saved);
+  TRY(hip_check(ft::launch_quant_down(qd, x_dt == FT_BF16, st), "linear_fwd quant_down"));
+
+  ft::GemmArgs g{};
+  g.a_codes = xq_codes; g.a_scales = xq_scales;
+  g.b_codes = L->r.codes; g.b_scales = L->r.scales; g.b_pitch = L->k / 2;
+  g.M = m; g.N = L->n; g.Kred = L->k;
+  g.low = static_cast<const ft::bf16_t*>(xl_saved); g.rt = (int)rt;
+  g.up0 = static_cast<const ft::bf16_t*>(L->lora_b); g.up0_ld = L->rank;
+  g.up1 = static_cast<const ft::bf16_t*>(L->stab_up); g.up1_ld = L->stab_rank;
+  g.up_split = (int)L->rank;
+  g.out = y; g.ldo = L->n;
+  TRY(hip_check(ft::launch_gemm_mx4(g, false, y_dt == FT_BF16, st), "linear_fwd gemm"));
+  return ok();
+}
+
+ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt, const void* x,
+                              ft_dtype x_dt, const void* xl_saved, int64_t m, void* dx,
+                              ft_dtype dx_dt, float* d_lora_a, float* d_lora_b, ft_mx4* gq_out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "linear_bwd";
+  TRY(check_linear(L, who));
+  REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m == 0) return ok();
+  const int64_t rt = L->rank + L->stab_rank;
+  TRY(check_tensor(dy, who, "dy"));
+  TRY(check_tensor(dx, who, "dx"));
+  if (L->rank > 0) {
+    TRY(check_tensor(x, who, "x"));
+    TRY(check_tensor(xl_saved, who, "xl_saved"));
+    TRY(check_tensor(d_lora_a, who, "d_lora_a"));
+    TRY(check_tensor(d_lora_b, who, "d_lora_b"));
+  }
+  if (gq_out) TRY(check_mx4(gq_out, m, L->n, "linear_bwd: gq_out"));
+  const BwdLayout lay = bwd_layout(ws, m, L, gq_out == nullptr);
+  REQUIRE(ws != nullptr && ws_bytes >= lay.bytes, FT_ERR_WORKSPACE,
+          "%s: workspace of %zu bytes, %zu needed", who, ws_bytes, lay.bytes);
+  REQUIRE(aligned16(ws), FT_ERR_ALIGN, "%s: workspace misaligned", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* gq_codes = gq_out ? gq_out->codes : lay.gq_codes;
+  uint8_t* gq_scales = gq_out ? gq_out->scales : lay.gq_scales;
+
+  ft::PrepArgs pa{};
+  pa.A = static_cast<const ft::bf16_t*>(L->lora_a);
+  pa.L1 = static_cast<const ft::bf16_t*>(L->stab_down);
+  pa.B = static_cast<const ft::bf16_t*>(L->lora_b);
+  pa.L2 = static_cast<const ft::bf16_t*>(L->stab_up);
+  pa.N = L->n; pa.K = L->k; pa.r = (int)L->rank; pa.s = (int)L->stab_rank;
+  pa.Ut = lay.Ut; pa.Dt = lay.Dt; pa.counters = lay.counters; pa.ncounters = lay.tiles;
+  TRY(hip_check(ft::launch_prep_bwd(pa, st), "linear_bwd prep"));
+
+  ft::QuantDownArgs qd{};
+  qd.x = dy; qd.M = m; qd.K = L->n; qd.ldx = L->n;
+  qd.codes = gq_codes; qd.scales = gq_scales;
+  qd.d0 = lay.Ut; qd.d1 = nullptr; qd.r0 = (int)rt; qd.rt = (int)rt;
+  qd.low = lay.GB;
+  TRY(hip_check(ft::launch_quant_down(qd, dy_dt == FT_BF16, st), "linear_bwd quant_down"));
+
+  ft::GemmArgs g{};
+  g.a_codes = gq_codes; g.a_scales = gq_scales;
+  g.b_codes = L->r.codes; g.b_scales = L->r.scales; g.b_pitch = L->k / 2;
+  g.M = m; g.N = L->k; g.Kred = L->n;
+  g.low = lay.GB; g.rt = (int)rt;
+  g.up0 = lay.Dt; g.up0_ld = rt; g.up1 = nullptr; g.up1_ld = 0; g.up_split = (int)rt;
+  g.out = dx; g.ldo = L->k;
+  TRY(hip_check(ft::launch_gemm_mx4(g, true, dx_dt == FT_BF16, st), "linear_bwd gemm"));
+
+  if (L->rank > 0) {
+    ft::LoraGradArgs lg{};
+    lg.M = m; lg.r = (int)L->rank;
+    lg.gb = lay.GB; lg.ld_gb = rt; lg.x = x; lg.x_bf16 = x_dt == FT_BF16; lg.K = L->k; lg.dA = d_lora_a;
+    lg.xl = static_cast<const ft::bf16_t*>(xl_saved); lg.ld_xl = rt; lg.g = dy;
+    lg.g_bf16 = dy_dt == FT_BF16; lg.N = L->n; lg.dB = d_lora_b;
+    lg.partials = lay.partials; lg.counters = lay.counters; lg.splits = lay.splits;
+    TRY(hip_check(ft::launch_lora_grad(lg, st), "linear_bwd lora_grad"));
+  }
+  return ok();
+}
+
+size_t fourtune_mlp_workspace_bytes(int64_t, const ft_linear*, const ft_linear*) { return 0; }
+
+ft_status fourtune_mlp_fwd(const ft_linear*, const ft_linear*, const void*, ft_dtype, int64_t,
+                           void*, ft_dtype, void*, void*, void*, float*, void*, size_t, void*) {
+  return fail(FT_ERR_UNSUPPORTED, "mlp_fwd: not built yet");
+}
+
+ft_status fourtune_mlp_bwd(const ft_linear*, const ft_linear*, const void*, ft_dtype, const void*,
+                           ft_dtype, const void*, const void*, const void*, int64_t, void*,
+                           ft_dtype, float*, float*, float*, float*, float*, void*, size_t,
+                           void*) {
+  return fail(FT_ERR_UNSUPPORTED, "mlp_bwd: not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Argument blocks and launchers of the GEMM-shaped kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace ft {
+
+// 4-bit backbone GEMM with the low-rank up-projection accumulated in its epilogue.
+//   forward : out[M x N] = deq A[M x Kred] * deq R[N x Kred]^T + low[M x rt] * up[N x rt]^T
+//   backward: out[M x N] = deq A[M x Kred] * deq R[Kred x N]   + low[M x rt] * up[N x rt]^T
+// A and R are MXFP4 (codes + 32x32-block E8M0 scales). `up` row q is the rt values
+// up0[q*up0_ld + 0 .. up_split) followed by up1[q*up1_ld + 0 .. rt-up_split).
+struct GemmArgs {
+  const uint8_t* a_codes;   // [M x Kred/2]
+  const uint8_t* a_scales;  // [ceil(M/32) x Kred/32]
+  const uint8_t* b_codes;   // Q(R) codes, b_pitch bytes per row
+  const uint8_t* b_scales;  // Q(R) scales, row-major over R's blocks
+  int64_t b_pitch;
+  int64_t M, N, Kred;
+  const bf16_t* low;        // [M x rt]
+  int rt;
+  const bf16_t* up0;
+  int64_t up0_ld;
+  const bf16_t* up1;
+  int64_t up1_ld;
+  int up_split;
+  void* out;                // [M x N] fp32 or bf16, row stride ldo
+  int64_t ldo;
+};
+
+hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipStream_t stream);
+
+// Fused quantize + down-projection over the rows of x [M x K] (row stride ldx):
+// Q(x) -> codes/scales, low[M x rt] = bf16( bf16(x) * D^T ), D row j = d0 row j (j < r0)
+// or d1 row j - r0, each row K-contiguous with row stride K.
+struct QuantDownArgs {
+  const void* x;
+  int64_t M, K, ldx;
+  uint8_t* codes;
+  uint8_t* scales;
+  const bf16_t* d0;
+  const bf16_t* d1;
+  int r0;
+  int rt;
+  bf16_t* low;
+};
+
+hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t stream);
+
+// Backward set-up: Ut[rt x N] = [B | L2]^T, Dt[K x rt] = [A; L1]^T, and zeroed counters.
+struct PrepArgs {
+  const bf16_t* A;   // [r x K]
+  const bf16_t* L1;  // [s x K]
+  const bf16_t* B;   // [N x r]
+  const bf16_t* L2;  // [N x s]
+  int64_t N, K;
+  int r, s;
+  bf16_t* Ut;
+  bf16_t* Dt;
+  uint32_t* counters;
+  int ncounters;
+};
+
+hipError_t launch_prep_bwd(const PrepArgs& a, hipStream_t stream);
+
+// LoRA parameter gradients, reductions over the M rows (FourTune §3.2: parameter updates
+// only for the adapter):
+//   dA[r x K] = GB[:, :r]^T * bf16(X)      dB[N x r] = bf16(G)^T * XL[:, :r]
+// Split over M; each split writes fp32 partials and the last split to finish a tile
+// sums all splits in a fixed order (deterministic).
+struct LoraGradArgs {
+  int64_t M;
+  int r;
+  // dA job
+  const bf16_t* gb;      // [M x rt], first r columns used
+  int64_t ld_gb;
+  const void* x;         // [M x K] fp32/bf16
+  bool x_bf16;
+  int64_t K;
+  float* dA;             // [r x K]
+  // dB job
+  const bf16_t* xl;      // [M x rt], first r columns used
+  int64_t ld_xl;
+  const void* g;         // [M x N] fp32/bf16
+  bool g_bf16;
+  int64_t N;
+  float* dB;             // [N x r]
+  // scratch
+  float* partials;       // [splits x r_pad x (K + N)]
+  uint32_t* counters;    // one per output tile, zero on entry, left zero on exit
+  int splits;
+};
+
+hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream);
+int lora_grad_splits(int64_t M, int64_t K, int64_t N);
+int lora_grad_tiles(int64_t K, int64_t N);
+
+}  // namespace ft

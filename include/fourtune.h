@@ -1,0 +1,174 @@
+/*
+ * fourtune.h -- C ABI of the W4A4G4 quantized linear layer on MI355X (gfx950).
+ *
+ * Method: "FourTune: Towards Fully 4-Bit Efficient Post-Training for Diffusion
+ * Models". Weights, activations and gradients are quantized to 4 bits and the
+ * backbone matrix products run in 4 bits (§3, opening paragraph). A linear layer has
+ * three branches (§3.1): a frozen 4-bit backbone on the residual R = W - L2 L1, a
+ * frozen full-precision low-rank stabilizer (L1, L2) and a trainable LoRA adapter
+ * (A, B). Quantization is block-wise with block-local scales so that the backward
+ * can read the same 4-bit weight transposed (§3.2). Quantization is fused with the
+ * down-projections, and the 4-bit GEMM with the up-projections (§3.3 "LoRA Fusion");
+ * in an MLP the FC1 GEMM is fused with GELU and the quantization of FC2's input
+ * (§3.3 "MLP Fusion").
+ *
+ * Conventions for every entry point
+ *   - Row-major storage everywhere; nn.Linear layout: W is [out x in], Y = X W^T.
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library never
+ *     allocates, frees or synchronizes, keeps no pointer after returning, and holds no
+ *     mutable global state. Work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     null stream) and completes asynchronously.
+ *   - Arguments are validated before anything is launched. On a bad argument the call
+ *     returns an FT_ERR_* code, launches nothing and records a message readable with
+ *     fourtune_last_error() (thread-local). A launch failure returns FT_ERR_HIP.
+ *     Faults inside kernels surface at the caller's next synchronization.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Required alignment: 16 bytes for every tensor pointer and for the workspace.
+ *   - Results are deterministic: the same inputs give bitwise-identical outputs.
+ *
+ * MXFP4 tensor format (ft_mx4)
+ *   A [rows x cols] tensor is cut into 32x32 blocks (the last block row may be
+ *   partial; cols must be a multiple of 32). Each element is an E2M1 code: bit 3 the
+ *   sign, bits 0..2 the index into {0, 0.5, 1, 1.5, 2, 3, 4, 6}. Two codes per byte,
+ *   the even column in the low nibble: codes is [rows x cols/2] bytes. Each block has
+ *   one E8M0 scale byte e, the value being 2^(e-127): scales is
+ *   [ceil(rows/32) x cols/32] bytes, row-major over blocks. A block's exponent is
+ *   E = clamp(floor(log2(amax)) - 2, -127, 127) (E = -127 for an all-zero block),
+ *   elements are rounded to nearest on the E2M1 grid, ties to the even code,
+ *   saturating at 6, the sign kept for values that round to zero. A block holding
+ *   a NaN or infinity gets scale byte 0xFF and zero codes.
+ */
+#ifndef FOURTUNE_H
+#define FOURTUNE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FT_OK = 0,
+  FT_ERR_NULL = 1,         /* a required pointer is NULL                           */
+  FT_ERR_SHAPE = 2,        /* a size is negative, inconsistent or not a multiple   */
+  FT_ERR_DTYPE = 3,        /* unknown dtype                                        */
+  FT_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned                     */
+  FT_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required           */
+  FT_ERR_UNSUPPORTED = 6,  /* valid request this build does not handle             */
+  FT_ERR_HIP = 7           /* the HIP runtime reported an error                    */
+} ft_status;
+
+typedef enum { FT_F32 = 0, FT_BF16 = 1 } ft_dtype;
+
+/* One MXFP4 tensor (see the format above). */
+typedef struct {
+  uint8_t *codes;   /* [rows x cols/2] bytes                      */
+  uint8_t *scales;  /* [ceil(rows/32) x cols/32] E8M0 bytes       */
+  int64_t rows;
+  int64_t cols;     /* multiple of 32                             */
+} ft_mx4;
+
+/* One W4A4G4 linear: Y = Q(X) Q(R)^T + X^ L1^T L2^T + X^ A^T B^T (FourTune §3.1).
+ * n = out features, k = in features (multiples of 32). rank = r (LoRA), stab_rank = s;
+ * each a multiple of 16, r + s a multiple of 32; either may be 0 (branch absent). */
+typedef struct {
+  ft_mx4 r;               /* Q(R), rows = n, cols = k (frozen; from fourtune_quantize) */
+  const void *lora_a;     /* A  [rank x k]      bf16, trainable down-projection     */
+  const void *lora_b;     /* B  [n x rank]      bf16, trainable up-projection       */
+  const void *stab_down;  /* L1 [stab_rank x k] bf16, frozen                        */
+  const void *stab_up;    /* L2 [n x stab_rank] bf16, frozen                        */
+  int64_t n, k, rank, stab_rank;
+} ft_linear;
+
+/* Sizes of the two arrays of an MXFP4 tensor. */
+size_t ft_mx4_codes_bytes(int64_t rows, int64_t cols);
+size_t ft_mx4_scales_bytes(int64_t rows, int64_t cols);
+
+/* fourtune_quantize -- 32x32-block MXFP4 quantization of a [rows x cols] tensor.
+ * Source: FourTune §2.3 (Round(W/s) with a group scale; MXFP4) and §3.2 (block-wise
+ * quantization with block-local scales). Used once on each frozen residual R.
+ *   x      [rows x cols] fp32 or bf16 (x_dt), row stride ld >= cols elements
+ *          (ld * element size must keep rows 16-byte aligned).
+ *   out    codes/scales buffers of the sizes above; out->rows/cols must equal
+ *          rows/cols.
+ * rows >= 0 (0 is a no-op), cols a multiple of 32. */
+ft_status fourtune_quantize(const void *x, ft_dtype x_dt, int64_t rows, int64_t cols,
+                            int64_t ld, ft_mx4 *out, void *stream);
+
+/* Workspace bytes needed by fourtune_linear_fwd and fourtune_linear_bwd for m rows. */
+size_t fourtune_linear_workspace_bytes(int64_t m, const ft_linear *L);
+
+/* fourtune_linear_fwd -- forward of one W4A4G4 linear (FourTune §3.1, §3.3 "LoRA
+ * Fusion"). One pass over X writes Q(X) and XL = bf16(X^ [A;L1]^T) (X^ = bf16(X));
+ * then the 4-bit GEMM Q(X) Q(R)^T runs with the up-projection XL [B|L2]^T accumulated
+ * into the same fp32 accumulators before the single store of Y.
+ *   x        [m x k] fp32 or bf16 (x_dt), contiguous.
+ *   y        [m x n] fp32 or bf16 (y_dt), overwritten.
+ *   xl_saved [m x (rank + stab_rank)] bf16, overwritten; pass it to the backward.
+ *   xq_out   optional (may be NULL): receives Q(X) ([m x k] MXFP4) instead of the
+ *            workspace holding it.
+ *   ws       workspace of fourtune_linear_workspace_bytes(m, L) bytes. */
+ft_status fourtune_linear_fwd(const ft_linear *L, const void *x, ft_dtype x_dt, int64_t m,
+                              void *y, ft_dtype y_dt, void *xl_saved, ft_mx4 *xq_out,
+                              void *ws, size_t ws_bytes, void *stream);
+
+/* fourtune_linear_bwd -- backward of one W4A4G4 linear (FourTune §3.2). The incoming
+ * gradient G = dY is quantized in the same 32x32 blocks, in the same pass as
+ * GB = bf16(G^ [B|L2]) (G^ = bf16(G)); dX = Q(G) Q(R) + GB [A;L1] is a 4-bit GEMM that
+ * reads the forward's Q(R) codes and scales transposed, with no requantization. Only
+ * the adapter gets parameter gradients: dA = GB[:, :r]^T X^, dB = G^^T XL[:, :r].
+ *   dy        [m x n] fp32 or bf16 (dy_dt).
+ *   x         [m x k] the forward's input (x_dt).
+ *   xl_saved  [m x (r+s)] bf16 from fourtune_linear_fwd.
+ *   dx        [m x k] fp32 or bf16 (dx_dt), overwritten.
+ *   d_lora_a  [rank x k] fp32, overwritten (may be NULL only when rank == 0).
+ *   d_lora_b  [n x rank] fp32, overwritten (may be NULL only when rank == 0).
+ *   gq_out    optional (may be NULL): receives Q(dY) ([m x n] MXFP4).
+ *   ws        workspace of fourtune_linear_workspace_bytes(m, L) bytes. */
+ft_status fourtune_linear_bwd(const ft_linear *L, const void *dy, ft_dtype dy_dt,
+                              const void *x, ft_dtype x_dt, const void *xl_saved, int64_t m,
+                              void *dx, ft_dtype dx_dt, float *d_lora_a, float *d_lora_b,
+                              ft_mx4 *gq_out, void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes needed by fourtune_mlp_fwd and fourtune_mlp_bwd for m rows. */
+size_t fourtune_mlp_workspace_bytes(int64_t m, const ft_linear *fc1, const ft_linear *fc2);
+
+/* fourtune_mlp_fwd -- FC1 -> GELU (tanh form) -> FC2 (FourTune §3.3 "MLP Fusion").
+ * fc1: d -> f, fc2: f -> d (fc1->n == fc2->k, fc2->n == fc1->k). The FC1 GEMM's
+ * epilogue stores P^ = bf16(FC1 output) (kept for the backward), computes
+ * H = GELU(P^) in fp32 and writes FC2's 4-bit operand Q(H) and partial sums of
+ * bf16(H) [A2;L1_2]^T directly; H itself is never written to memory.
+ *   x         [m x d] fp32 or bf16 (x_dt)
+ *   y         [m x d] fp32 or bf16 (y_dt), overwritten
+ *   xl1_saved [m x rt1] bf16, pre_saved [m x f] bf16, hl2_saved [m x rt2] bf16:
+ *             overwritten; pass them to the backward.
+ *   h_debug   optional [m x f] fp32: receives H (for checks), may be NULL. */
+ft_status fourtune_mlp_fwd(const ft_linear *fc1, const ft_linear *fc2, const void *x,
+                           ft_dtype x_dt, int64_t m, void *y, ft_dtype y_dt, void *xl1_saved,
+                           void *pre_saved, void *hl2_saved, float *h_debug, void *ws,
+                           size_t ws_bytes, void *stream);
+
+/* fourtune_mlp_bwd -- backward of the MLP pair. FC2's dX GEMM epilogue forms
+ * dP = dH * GELU'(P^) and writes FC1's 4-bit gradient operand Q(dP) and its
+ * down-projection partials directly; FC1's backward then runs as in
+ * fourtune_linear_bwd with G = dP.
+ *   dy [m x d] (dy_dt); x, xl1_saved, pre_saved, hl2_saved from the forward;
+ *   dx [m x d] (dx_dt); d_a1 [r1 x d], d_b1 [f x r1], d_a2 [r2 x f], d_b2 [d x r2] fp32;
+ *   dp_debug optional [m x f] fp32: receives dP, may be NULL. */
+ft_status fourtune_mlp_bwd(const ft_linear *fc1, const ft_linear *fc2, const void *dy,
+                           ft_dtype dy_dt, const void *x, ft_dtype x_dt, const void *xl1_saved,
+                           const void *pre_saved, const void *hl2_saved, int64_t m, void *dx,
+                           ft_dtype dx_dt, float *d_a1, float *d_b1, float *d_a2, float *d_b2,
+                           float *dp_debug, void *ws, size_t ws_bytes, void *stream);
+
+/* Static text of a status code. */
+const char *fourtune_status_string(ft_status s);
+/* Detail of the last failing call on this thread ("" if none). */
+const char *fourtune_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOURTUNE_H */

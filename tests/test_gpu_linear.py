@@ -1,0 +1,129 @@
+"""GPU parity of fourtune_linear_fwd / fourtune_linear_bwd against the oracle.
+
+Bar: Q(X), Q(dY) codes and scales bit-exact; Y, dX, dA, dB (fp32 outputs) within a
+relative Frobenius error of 1e-3 of the fp64 oracle; bf16 outputs against the oracle
+rounded to bf16 within the same bar. The oracle computes everything from the same
+seeded inputs; nothing it uses comes from the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_lora_fp4_amd import abi
+from oracle import layer, mx4
+from synth import workloads as wl
+from tests.gpu_util import dev, host, host_u8, log, oracle_packed, rel_fro
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+def _gpu_linear(d):
+    R = dev(d["R"], "fp32")
+    L = abi.make_linear(R, dev(d["A"]), dev(d["B"]), dev(d["L1"]), dev(d["L2"]))
+    return L
+
+
+def _oracle_linear(d):
+    return layer.Linear(R=d["R"].astype(np.float64), A=d["A"].astype(np.float64),
+                        B=d["B"].astype(np.float64), L1=d["L1"].astype(np.float64),
+                        L2=d["L2"].astype(np.float64))
+
+
+def _run(d, out_dtype=torch.float32):
+    """Forward + backward on the GPU; returns host arrays."""
+    m, n, k = d["X"].shape[0], d["R"].shape[0], d["R"].shape[1]
+    L = _gpu_linear(d)
+    x = dev(d["X"], d["x_dtype"])
+    dy = dev(d["dY"], d["dy_dtype"])
+    xq = abi.Mx4.empty(m, k)
+    gq = abi.Mx4.empty(m, n)
+    ws = abi.workspace(abi.fourtune_linear_workspace_bytes(m, L))
+    y, xl = abi.linear_forward(L, x, y_dtype=out_dtype, ws=ws, xq_out=xq)
+    dx, da, db = abi.linear_backward(L, dy, x, xl, dx_dtype=out_dtype, ws=ws, gq_out=gq)
+    torch.cuda.synchronize()
+    return dict(Y=host(y), XL=host(xl), dX=host(dx), dA=host(da), dB=host(db),
+                xq=(host_u8(xq.codes), host_u8(xq.scales)), gq=(host_u8(gq.codes), host_u8(gq.scales)))
+
+
+def _check_full(d, got, out_bf16=False):
+    lin = _oracle_linear(d)
+    X = d["X"].astype(np.float64)
+    G = d["dY"].astype(np.float64)
+    Y, XL = layer.linear_forward(X, lin)
+    dX, dA, dB, _ = layer.linear_backward(G, X, XL, lin)
+    wc, ws_ = oracle_packed(X)
+    assert np.array_equal(got["xq"][1], ws_) and np.array_equal(got["xq"][0], wc), "Q(X)"
+    gc, gs = oracle_packed(G)
+    assert np.array_equal(got["gq"][1], gs) and np.array_equal(got["gq"][0], gc), "Q(dY)"
+    rnd = mx4.bf16_round if out_bf16 else (lambda a: a)
+    errs = dict(XL=rel_fro(got["XL"], XL), Y=rel_fro(got["Y"], rnd(Y)), dX=rel_fro(got["dX"], rnd(dX)),
+                dA=rel_fro(got["dA"], dA) if dA.size else 0.0,
+                dB=rel_fro(got["dB"], dB) if dB.size else 0.0)
+    log(f"  rel errors {errs}")
+    for k_, e in errs.items():
+        assert e <= TOL, (k_, e)
+    return errs
+
+
+CASES = [
+    # m, n, k, r, s, x_dtype
+    (64, 256, 256, 16, 16, "bf16"),
+    (300, 544, 384, 32, 32, "bf16"),     # ragged M (partial block, partial tile), N tail
+    (257, 512, 416, 64, 32, "bf16"),     # K % 128 != 0 (scale bytes one by one)
+    (200, 320, 288, 0, 32, "bf16"),      # no LoRA
+    (200, 320, 288, 32, 0, "fp32"),      # no stabilizer, fp32 input
+    (96, 256, 512, 0, 0, "bf16"),        # plain 4-bit GEMM
+    (520, 768, 640, 64, 64, "fp32"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,r,s,xdt", CASES)
+def test_small_cases(m, n, k, r, s, xdt):
+    log(f"linear m={m} n={n} k={k} r={r} s={s} x={xdt}")
+    d = wl.random_linear(m, n, k, r, s, seed=m + n + k, x_dtype=xdt, dy_dtype=xdt)
+    _check_full(d, _run(d))
+
+
+def test_bf16_outputs():
+    log("linear bf16 outputs")
+    d = wl.random_linear(300, 544, 384, 32, 32, seed=9)
+    _check_full(d, _run(d, out_dtype=torch.bfloat16), out_bf16=True)
+
+
+def test_c1_tiny_layer():
+    log("linear c1")
+    d = wl.linear_case("c1")
+    _check_full(d, _run(d))
+
+
+def test_c2_attention_projection():
+    log("linear c2 (full size, full oracle)")
+    d = wl.linear_case("c2")
+    _check_full(d, _run(d))
+
+
+def test_deterministic():
+    d = wl.random_linear(300, 544, 384, 32, 32, seed=5)
+    a, b = _run(d), _run(d)
+    for key in ("Y", "XL", "dX", "dA", "dB"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_workspace_and_argument_errors():
+    d = wl.random_linear(64, 256, 256, 16, 16, seed=3)
+    L = _gpu_linear(d)
+    x = dev(d["X"])
+    y = torch.empty((64, 256), dtype=torch.float32, device="cuda")
+    xl = torch.empty((64, 32), dtype=torch.bfloat16, device="cuda")
+    small = abi.workspace(64)
+    with pytest.raises(abi.FourTuneError) as e:
+        abi.fourtune_linear_fwd(L, x, y, xl, small)
+    assert e.value.name == "FT_ERR_WORKSPACE"
+    ws = abi.workspace(abi.fourtune_linear_workspace_bytes(64, L))
+    with pytest.raises(abi.FourTuneError) as e:
+        abi.fourtune_linear_fwd(L, x, y, None, ws)
+    assert e.value.name == "FT_ERR_NULL"
+    with pytest.raises(abi.FourTuneError) as e:
+        abi.fourtune_linear_fwd(L, x[:, 1:], y, xl, ws)  # misaligned
+    assert e.value.name == "FT_ERR_ALIGN"
