@@ -1,0 +1,230 @@
+"""Benchmark of the W4A4G4 quantized linear (FourTune) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2|c3|...] [--no-cpu-baseline]
+
+One step = the whole hot path once over one batch: the layer's forward (fused
+quantize + down-projection, 4-bit GEMM + up-projection) and backward (fused
+quantize + down-projection of dY, transposed 4-bit GEMM + up-projection, LoRA
+gradients). Inputs are seeded synthetic tensors of the named workload, resident in
+HBM before timing; several independent input/weight sets are rotated so that the
+256 MB Infinity Cache cannot hold a step's operands from one step to the next.
+
+Prints one JSON line. `value` is backbone TFLOP/s of the whole step, 4*M*N*K per
+linear (the 4-bit GEMM flops of forward and backward) divided by the step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MXFP4_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2")
+    ap.add_argument("--sets", type=int, default=4, help="rotated input/weight sets")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------- GPU side
+def build_sets(case, nsets, torch, abi):
+    """Device copies of one linear's operands; set i gets its own buffers."""
+    dt = {"fp32": torch.float32, "bf16": torch.bfloat16}
+    m, k = case["X"].shape
+    n = case["R"].shape[0]
+    sets = []
+    for i in range(nsets):
+        def d(a, dtype):
+            return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt[dtype])
+        L = abi.make_linear(d(case["R"], "fp32"), d(case["A"], "bf16"), d(case["B"], "bf16"),
+                            d(case["L1"], "bf16"), d(case["L2"], "bf16"))
+        rt = L.rank + L.stab_rank
+        s = dict(L=L, x=d(case["X"], case["x_dtype"]), dy=d(case["dY"], case["dy_dtype"]),
+                 y=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+                 dx=torch.empty((m, k), dtype=torch.bfloat16, device="cuda"),
+                 xl=torch.empty((m, rt), dtype=torch.bfloat16, device="cuda"),
+                 da=torch.empty((L.rank, k), dtype=torch.float32, device="cuda"),
+                 db=torch.empty((n, L.rank), dtype=torch.float32, device="cuda"),
+                 ws=abi.workspace(abi.fourtune_linear_workspace_bytes(m, L)),
+                 xq=abi.Mx4.empty(m, k), gq=abi.Mx4.empty(m, n),
+                 gb=(torch.randn((m, rt), device="cuda") * 1e-3).to(torch.bfloat16))
+        sets.append(s)
+    return sets
+
+
+def step(abi, s):
+    abi.fourtune_linear_fwd(s["L"], s["x"], s["y"], s["xl"], s["ws"])
+    abi.fourtune_linear_bwd(s["L"], s["dy"], s["x"], s["xl"], s["dx"], s["da"], s["db"], s["ws"])
+
+
+def time_region(torch, fn, iters):
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(iters):
+        fn(i)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1000.0  # seconds
+
+
+def time_each(torch, fn, iters):
+    """Average duration of fn(i) bracketed by events on the current stream."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        evs[i][0].record()
+        fn(i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1000.0
+
+
+# --------------------------------------------------------------------------- CPU side
+def cpu_baseline(case, seconds):
+    """The oracle as it stands, fwd+bwd on a row sample of the same layer."""
+    from oracle import layer, mx4
+
+    lin = layer.Linear(R=case["R"].astype(np.float64), A=case["A"].astype(np.float64),
+                       B=case["B"].astype(np.float64), L1=case["L1"].astype(np.float64),
+                       L2=case["L2"].astype(np.float64))
+    Rq = mx4.fake_quant(lin.R)  # frozen weight: quantized once, outside the timing
+    rows = 512
+    X = case["X"][:rows].astype(np.float64)
+    G = case["dY"][:rows].astype(np.float64)
+    n, k = lin.R.shape
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        Y, XL = layer.linear_forward(X, lin, Rq=Rq)
+        layer.linear_backward(G, X, XL, lin, Rq=Rq)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    flops = 4.0 * rows * n * k * reps
+    return dict(value=flops / el / 1e12, unit="TFLOP/s", cores=len(os.sched_getaffinity(0)),
+                kind="oracle",
+                sample=f"fwd+bwd of the same linear on the first {rows} of {case['X'].shape[0]} "
+                       f"token rows, {reps} repetitions in {el:.1f} s (numpy fp64, BLAS threads = cores)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the hot path runs on a single MI355X; sharding is a design note only).",
+              file=sys.stderr)
+        return 2
+    import torch
+    from bit_quantized_lora_fp4_amd import abi
+    from synth import workloads as wl
+
+    abi.lib()  # fails loudly when the library is not built
+    spec = wl.WORKLOADS[args.workload]
+    lin_spec = spec.layers[0]
+    if not isinstance(lin_spec, wl.LinearSpec):
+        raise SystemExit(f"workload {args.workload} has no single linear; use c1 or c2")
+    log(f"[bench] generating {args.workload} inputs")
+    case = wl.linear_case(args.workload)
+    m, k = case["X"].shape
+    n = case["R"].shape[0]
+    r, s = lin_spec.r, lin_spec.s
+    sets = build_sets(case, args.sets, torch, abi)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.sets} sets resident; warmup {args.warmup}")
+
+    for st in sets:  # fill each set's Q(X) and Q(dY) for the GEMM-only timings
+        abi.fourtune_linear_fwd(st["L"], st["x"], st["y"], st["xl"], st["ws"], xq_out=st["xq"])
+        abi.fourtune_linear_bwd(st["L"], st["dy"], st["x"], st["xl"], st["dx"], st["da"], st["db"],
+                                st["ws"], gq_out=st["gq"])
+    for i in range(args.warmup):
+        step(abi, sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps
+    t = time_region(torch, lambda i: step(abi, sets[i % len(sets)]), args.steps)
+    ms_per_step = 1000.0 * t / args.steps
+    flops_step = 4.0 * m * n * k
+    value = flops_step / (t / args.steps) / 1e12
+    log(f"[bench] step {ms_per_step:.4f} ms -> {value:.1f} TFLOP/s")
+
+    # ---- per-kernel: the two 4-bit GEMMs alone, and the standalone quantizer
+    def S(i):
+        return sets[i % len(sets)]
+
+    t_gf = time_each(torch, lambda i: abi.fourtune_gemm_fwd(S(i)["L"], S(i)["xq"], S(i)["xl"], S(i)["y"]),
+                     args.steps)
+    t_gb = time_each(torch, lambda i: abi.fourtune_gemm_bwd(S(i)["L"], S(i)["gq"], S(i)["gb"], S(i)["dx"]),
+                     args.steps)
+    t_fwd = time_each(torch, lambda i: abi.fourtune_linear_fwd(S(i)["L"], S(i)["x"], S(i)["y"], S(i)["xl"],
+                                                              S(i)["ws"]), args.steps)
+    t_bwd = time_each(torch, lambda i: abi.fourtune_linear_bwd(S(i)["L"], S(i)["dy"], S(i)["x"], S(i)["xl"],
+                                                              S(i)["dx"], S(i)["da"], S(i)["db"], S(i)["ws"]),
+                      args.steps)
+    t_q = time_each(torch, lambda i: abi.fourtune_quantize(S(i)["x"], S(i)["xq"]), args.steps)
+    gemm_flops = 2.0 * m * n * k
+    tf_gf, tf_gb = gemm_flops / t_gf / 1e12, gemm_flops / t_gb / 1e12
+    xbytes = case["X"].dtype.itemsize if case["x_dtype"] == "fp32" else 2
+    q_bytes = m * k * xbytes + m * k / 2 + ((m + 31) // 32) * (k // 32)
+    q_gbps = q_bytes / t_q / 1e9
+    dominant = ("gemm_fwd", t_gf, tf_gf) if t_gf >= t_gb else ("gemm_bwd", t_gb, tf_gb)
+    log(f"[bench] gemm_fwd {t_gf*1e6:.1f} us ({tf_gf:.0f} TF/s), gemm_bwd {t_gb*1e6:.1f} us "
+        f"({tf_gb:.0f} TF/s), linear_fwd {t_fwd*1e6:.1f} us, linear_bwd {t_bwd*1e6:.1f} us, quantize X {t_q*1e6:.1f} us ({q_gbps:.0f} GB/s)")
+
+    out = {
+        "metric": "W4A4G4 linear fwd+bwd TFLOPS (4-bit backbone flops / whole step time)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {spec.title}, W4A4G4 linear fwd+bwd",
+                   "m": m, "k": k, "n": n, "lora_rank": r, "stab_rank": s,
+                   "x_dtype": case["x_dtype"], "out_dtype": "bf16", "input_sets": args.sets},
+        "frac_of_mxfp4_peak": round(value / PEAK_MXFP4_TFLOPS, 4),
+        "roofline": {"kernel": dominant[0], "bound": "mfma", "achieved": round(dominant[2], 1),
+                     "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dominant[2] / PEAK_MXFP4_TFLOPS, 4), "traffic": None},
+        "kernels_us": {"gemm_fwd": round(t_gf * 1e6, 2), "gemm_bwd": round(t_gb * 1e6, 2),
+                       "linear_fwd": round(t_fwd * 1e6, 2),
+                       "linear_bwd": round(t_bwd * 1e6, 2), "quantize_x": round(t_q * 1e6, 2)},
+        "gemm_tflops": {"fwd": round(tf_gf, 1), "bwd": round(tf_gb, 1),
+                        "fwd_bwd": round(2 * gemm_flops / (t_gf + t_gb) / 1e12, 1)},
+        "quantize_gbps": round(q_gbps, 1),
+        "quantize_frac_of_hbm": round(q_gbps / PEAK_HBM_GBPS, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

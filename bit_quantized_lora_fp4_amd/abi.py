@@ -58,6 +58,10 @@ _SIGS = {
     "fourtune_linear_bwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), c_vp, ctypes.c_int, c_vp,
                                            ctypes.c_int, c_vp, c_i64, c_vp, ctypes.c_int, c_vp,
                                            c_vp, ctypes.POINTER(FtMx4), c_vp, c_sz, c_vp]),
+    "fourtune_gemm_fwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtMx4), c_vp,
+                                         c_i64, c_vp, ctypes.c_int, c_vp]),
+    "fourtune_gemm_bwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtMx4), c_vp,
+                                         c_i64, c_vp, ctypes.c_int, c_vp]),
     "fourtune_mlp_workspace_bytes": (c_sz, [c_i64, ctypes.POINTER(FtLinear),
                                             ctypes.POINTER(FtLinear)]),
     "fourtune_mlp_fwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear), c_vp,
@@ -213,6 +217,20 @@ def fourtune_linear_bwd(L: Linear, dy: torch.Tensor, x: torch.Tensor, xl_saved: 
                                      ctypes.byref(gq) if gq is not None else None,
                                      _ptr(ws), ws.numel() if ws is not None else 0,
                                      _stream(stream)))
+
+
+def fourtune_gemm_fwd(L: Linear, xq: Mx4, xl: Optional[torch.Tensor], y: torch.Tensor,
+                      stream=None):
+    s, q = L.struct(), xq.struct()
+    _check(lib().fourtune_gemm_fwd(ctypes.byref(s), ctypes.byref(q), _ptr(xl), xq.rows, _ptr(y),
+                                   _dt(y), _stream(stream)))
+
+
+def fourtune_gemm_bwd(L: Linear, gq: Mx4, gb: Optional[torch.Tensor], dx: torch.Tensor,
+                      stream=None):
+    s, q = L.struct(), gq.struct()
+    _check(lib().fourtune_gemm_bwd(ctypes.byref(s), ctypes.byref(q), _ptr(gb), gq.rows, _ptr(dx),
+                                   _dt(dx), _stream(stream)))
 
 
 def fourtune_mlp_workspace_bytes(m: int, fc1: Linear, fc2: Linear) -> int:

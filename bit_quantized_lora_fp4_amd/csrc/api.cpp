@@ -139,6 +139,9 @@ ft_status check_linear(const ft_linear* L, const char* who) {
   const int64_t rt = L->rank + L->stab_rank;
   REQUIRE(rt % 32 == 0, FT_ERR_SHAPE, "%s: rank + stab_rank = %lld must be a multiple of 32", who, (long long)rt);
   REQUIRE(rt <= 128, FT_ERR_UNSUPPORTED, "%s: rank + stab_rank = %lld > 128", who, (long long)rt);
+  REQUIRE(L->n <= ft::GEMM_MAX_KRED && L->k <= ft::GEMM_MAX_KRED, FT_ERR_UNSUPPORTED,
+          "%s: n=%lld, k=%lld; the 4-bit GEMMs reduce over at most %lld elements", who,
+          (long long)L->n, (long long)L->k, (long long)ft::GEMM_MAX_KRED);
   TRY(check_mx4(&L->r, L->n, L->k, "linear: Q(R)"));
   if (L->rank > 0) {
     REQUIRE(L->lora_a && L->lora_b, FT_ERR_NULL, "%s: NULL LoRA factor", who);
@@ -176,7 +179,6 @@ FwdLayout fwd_layout(void* ws, int64_t m, const ft_linear* L, bool need_xq) {
 
 struct BwdLayout {
   ft::bf16_t* Ut;
-  ft::bf16_t* Dt;
   uint8_t* gq_codes;
   uint8_t* gq_scales;
   ft::bf16_t* GB;
@@ -192,7 +194,6 @@ BwdLayout bwd_layout(void* ws, int64_t m, const ft_linear* L, bool need_gq) {
   const int64_t rt = L->rank + L->stab_rank;
   const int64_t rp = (L->rank + 31) / 32 * 32;
   b.Ut = c.take<ft::bf16_t>((size_t)rt * L->n * 2);
-  b.Dt = c.take<ft::bf16_t>((size_t)rt * L->k * 2);
   if (need_gq) {
     b.gq_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, L->n));
     b.gq_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, L->n));
@@ -204,6 +205,34 @@ BwdLayout bwd_layout(void* ws, int64_t m, const ft_linear* L, bool need_gq) {
   b.counters = c.take<uint32_t>((size_t)b.tiles * 4);
   b.bytes = c.used;
   return b;
+}
+
+ft_status run_gemm_fwd(const ft_linear* L, const uint8_t* xq_codes, const uint8_t* xq_scales,
+                       const void* xl, int64_t m, void* y, ft_dtype y_dt, hipStream_t st) {
+  ft::GemmArgs g{};
+  g.a_codes = xq_codes; g.a_scales = xq_scales;
+  g.b_codes = L->r.codes; g.b_scales = L->r.scales; g.b_pitch = L->k / 2;
+  g.M = m; g.N = L->n; g.Kred = L->k;
+  g.low = static_cast<const ft::bf16_t*>(xl); g.rt = (int)(L->rank + L->stab_rank);
+  g.up0 = static_cast<const ft::bf16_t*>(L->lora_b); g.up0_ld = L->rank;
+  g.up1 = static_cast<const ft::bf16_t*>(L->stab_up); g.up1_ld = L->stab_rank;
+  g.up_split = (int)L->rank;
+  g.out = y; g.ldo = L->n;
+  return hip_check(ft::launch_gemm_mx4(g, false, y_dt == FT_BF16, st), "gemm_fwd");
+}
+
+ft_status run_gemm_bwd(const ft_linear* L, const uint8_t* gq_codes, const uint8_t* gq_scales,
+                       const void* gb, int64_t m, void* dx, ft_dtype dx_dt, hipStream_t st) {
+  ft::GemmArgs g{};
+  g.a_codes = gq_codes; g.a_scales = gq_scales;
+  g.b_codes = L->r.codes; g.b_scales = L->r.scales; g.b_pitch = L->k / 2;
+  g.M = m; g.N = L->k; g.Kred = L->n;
+  g.low = static_cast<const ft::bf16_t*>(gb); g.rt = (int)(L->rank + L->stab_rank);
+  g.up0 = static_cast<const ft::bf16_t*>(L->lora_a); g.up0_ld = L->k;
+  g.up1 = static_cast<const ft::bf16_t*>(L->stab_down); g.up1_ld = L->k;
+  g.up_split = (int)L->rank;
+  g.out = dx; g.ldo = L->k;
+  return hip_check(ft::launch_gemm_mx4(g, true, dx_dt == FT_BF16, st), "gemm_bwd");
 }
 
 }  // namespace
@@ -246,17 +275,7 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const void* x, ft_dtype x_dt, 
   qd.r0 = (int)L->rank; qd.rt = (int)rt;
   qd.low = static_cast<ft::bf16_t*>(xl_saved);
   TRY(hip_check(ft::launch_quant_down(qd, x_dt == FT_BF16, st), "linear_fwd quant_down"));
-
-  ft::GemmArgs g{};
-  g.a_codes = xq_codes; g.a_scales = xq_scales;
-  g.b_codes = L->r.codes; g.b_scales = L->r.scales; g.b_pitch = L->k / 2;
-  g.M = m; g.N = L->n; g.Kred = L->k;
-  g.low = static_cast<const ft::bf16_t*>(xl_saved); g.rt = (int)rt;
-  g.up0 = static_cast<const ft::bf16_t*>(L->lora_b); g.up0_ld = L->rank;
-  g.up1 = static_cast<const ft::bf16_t*>(L->stab_up); g.up1_ld = L->stab_rank;
-  g.up_split = (int)L->rank;
-  g.out = y; g.ldo = L->n;
-  TRY(hip_check(ft::launch_gemm_mx4(g, false, y_dt == FT_BF16, st), "linear_fwd gemm"));
+  TRY(run_gemm_fwd(L, xq_codes, xq_scales, xl_saved, m, y, y_dt, st));
   return ok();
 }
 
@@ -288,12 +307,10 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
   uint8_t* gq_scales = gq_out ? gq_out->scales : lay.gq_scales;
 
   ft::PrepArgs pa{};
-  pa.A = static_cast<const ft::bf16_t*>(L->lora_a);
-  pa.L1 = static_cast<const ft::bf16_t*>(L->stab_down);
   pa.B = static_cast<const ft::bf16_t*>(L->lora_b);
   pa.L2 = static_cast<const ft::bf16_t*>(L->stab_up);
-  pa.N = L->n; pa.K = L->k; pa.r = (int)L->rank; pa.s = (int)L->stab_rank;
-  pa.Ut = lay.Ut; pa.Dt = lay.Dt; pa.counters = lay.counters; pa.ncounters = lay.tiles;
+  pa.N = L->n; pa.r = (int)L->rank; pa.s = (int)L->stab_rank;
+  pa.Ut = lay.Ut; pa.counters = lay.counters; pa.ncounters = lay.tiles;
   TRY(hip_check(ft::launch_prep_bwd(pa, st), "linear_bwd prep"));
 
   ft::QuantDownArgs qd{};
@@ -303,14 +320,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
   qd.low = lay.GB;
   TRY(hip_check(ft::launch_quant_down(qd, dy_dt == FT_BF16, st), "linear_bwd quant_down"));
 
-  ft::GemmArgs g{};
-  g.a_codes = gq_codes; g.a_scales = gq_scales;
-  g.b_codes = L->r.codes; g.b_scales = L->r.scales; g.b_pitch = L->k / 2;
-  g.M = m; g.N = L->k; g.Kred = L->n;
-  g.low = lay.GB; g.rt = (int)rt;
-  g.up0 = lay.Dt; g.up0_ld = rt; g.up1 = nullptr; g.up1_ld = 0; g.up_split = (int)rt;
-  g.out = dx; g.ldo = L->k;
-  TRY(hip_check(ft::launch_gemm_mx4(g, true, dx_dt == FT_BF16, st), "linear_bwd gemm"));
+  TRY(run_gemm_bwd(L, gq_codes, gq_scales, lay.GB, m, dx, dx_dt, st));
 
   if (L->rank > 0) {
     ft::LoraGradArgs lg{};
@@ -321,6 +331,34 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
     lg.partials = lay.partials; lg.counters = lay.counters; lg.splits = lay.splits;
     TRY(hip_check(ft::launch_lora_grad(lg, st), "linear_bwd lora_grad"));
   }
+  return ok();
+}
+
+ft_status fourtune_gemm_fwd(const ft_linear* L, const ft_mx4* xq, const void* xl, int64_t m,
+                            void* y, ft_dtype y_dt, void* stream) {
+  const char* who = "gemm_fwd";
+  TRY(check_linear(L, who));
+  REQUIRE(dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m == 0) return ok();
+  TRY(check_mx4(xq, m, L->k, "gemm_fwd: xq"));
+  if (L->rank + L->stab_rank > 0) TRY(check_tensor(xl, who, "xl"));
+  TRY(check_tensor(y, who, "y"));
+  TRY(run_gemm_fwd(L, xq->codes, xq->scales, xl, m, y, y_dt, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+ft_status fourtune_gemm_bwd(const ft_linear* L, const ft_mx4* gq, const void* gb, int64_t m,
+                            void* dx, ft_dtype dx_dt, void* stream) {
+  const char* who = "gemm_bwd";
+  TRY(check_linear(L, who));
+  REQUIRE(dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m == 0) return ok();
+  TRY(check_mx4(gq, m, L->n, "gemm_bwd: gq"));
+  if (L->rank + L->stab_rank > 0) TRY(check_tensor(gb, who, "gb"));
+  TRY(check_tensor(dx, who, "dx"));
+  TRY(run_gemm_bwd(L, gq->codes, gq->scales, gb, m, dx, dx_dt, static_cast<hipStream_t>(stream)));
   return ok();
 }
 

@@ -83,6 +83,58 @@ __device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
   return (a > b ? a : b) << 16;
 }
 
+// ---------------------------------------------------------------- LDS transposed reads
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each 16-lane group, source lane s supplies the address of
+// 4 consecutive 16-bit elements; viewing the group's 64 elements as 4 rows of 16 (row q
+// = source lanes 4q..4q+3), output lane i receives column i of those 4 rows.
+// lds_tr16_pair reads, from a row-major bf16 tile (row pitch `pitch` bytes), the bf16
+// MFMA operand "8 consecutive rows m0 + 8*(l/32) .. +8 of column c0 + l%32" for every
+// lane l, as two such reads.
+__device__ __forceinline__ v4i lds_tr16_pair(const lds_char* base, int pitch, int m0, int c0, int lane) {
+  // 8 consecutive m (m0 + 8*(l>>5) .. +8) of column c0 + (l & 31), via two tr_b16 reads
+  const int g = lane >> 4, s = lane & 15;
+  const int col = c0 + 16 * (g & 1) + 4 * (s & 3);
+  const int m = m0 + 8 * (g >> 1) + (s >> 2);
+  const lds_char* p0 = base + m * pitch + col * 2;
+  v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
+  v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0 + 4 * pitch));
+  v4i r;
+  r.x = (int)(((uint32_t)(uint16_t)lo.x) | ((uint32_t)(uint16_t)lo.y << 16));
+  r.y = (int)(((uint32_t)(uint16_t)lo.z) | ((uint32_t)(uint16_t)lo.w << 16));
+  r.z = (int)(((uint32_t)(uint16_t)hi.x) | ((uint32_t)(uint16_t)hi.y << 16));
+  r.w = (int)(((uint32_t)(uint16_t)hi.z) | ((uint32_t)(uint16_t)hi.w << 16));
+  return r;
+}
+
+// ---------------------------------------------------------------- buffer loads
+// Raw buffer resources: loads beyond num_records bytes return zero with no branch, so
+// ragged tiles need no predicated code. An offset of BUF_OOB is always out of range.
+typedef __amdgpu_buffer_rsrc_t bufres;
+constexpr uint32_t BUF_OOB = 0xFFFFFF00u;
+constexpr int BUF_FLAGS = 0x00020000;  // raw, untyped 32-bit data (gfx9 dword3)
+
+__device__ __forceinline__ bufres make_buf(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes >= 0xFFFFFF00ull ? 0xFFFFFF00u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, BUF_FLAGS);
+}
+__device__ __forceinline__ v4i buf_load16(bufres r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(bufres r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load1(bufres r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+// 16 bytes per lane straight into LDS: lane l's data lands at lds + 16*l.
+__device__ __forceinline__ void buf_load16_lds(bufres r, lds_char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           (int)off, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 

@@ -9,10 +9,13 @@
 namespace ft {
 
 // 4-bit backbone GEMM with the low-rank up-projection accumulated in its epilogue.
-//   forward : out[M x N] = deq A[M x Kred] * deq R[N x Kred]^T + low[M x rt] * up[N x rt]^T
-//   backward: out[M x N] = deq A[M x Kred] * deq R[Kred x N]   + low[M x rt] * up[N x rt]^T
-// A and R are MXFP4 (codes + 32x32-block E8M0 scales). `up` row q is the rt values
-// up0[q*up0_ld + 0 .. up_split) followed by up1[q*up1_ld + 0 .. rt-up_split).
+//   forward : out[M x N] = deq A[M x Kred] * deq R[N x Kred]^T + low[M x rt] * U[N x rt]^T
+//             U row q = up0[q*up0_ld + 0 .. up_split) ++ up1[q*up1_ld + 0 .. rt-up_split)
+//             ([B | L2]: up0 = B, up1 = L2)
+//   backward: out[M x N] = deq A[M x Kred] * deq R[Kred x N]   + low[M x rt] * D[rt x N]
+//             D row j = up0 row j (j < up_split) or up1 row j - up_split, row strides
+//             up0_ld / up1_ld ([A; L1]: up0 = A, up1 = L1)
+// A and R are MXFP4 (codes + 32x32-block E8M0 scales).
 struct GemmArgs {
   const uint8_t* a_codes;   // [M x Kred/2]
   const uint8_t* a_scales;  // [ceil(M/32) x Kred/32]
@@ -32,6 +35,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipStream_t stream);
+// Longest reduction the GEMM supports (its block scales are staged in LDS once).
+constexpr int64_t GEMM_MAX_KRED = 16384;
 
 // Fused quantize + down-projection over the rows of x [M x K] (row stride ldx):
 // Q(x) -> codes/scales, low[M x rt] = bf16( bf16(x) * D^T ), D row j = d0 row j (j < r0)
@@ -50,16 +55,13 @@ struct QuantDownArgs {
 
 hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t stream);
 
-// Backward set-up: Ut[rt x N] = [B | L2]^T, Dt[K x rt] = [A; L1]^T, and zeroed counters.
+// Backward set-up: Ut[rt x N] = [B | L2]^T and zeroed counters.
 struct PrepArgs {
-  const bf16_t* A;   // [r x K]
-  const bf16_t* L1;  // [s x K]
   const bf16_t* B;   // [N x r]
   const bf16_t* L2;  // [N x s]
-  int64_t N, K;
+  int64_t N;
   int r, s;
   bf16_t* Ut;
-  bf16_t* Dt;
   uint32_t* counters;
   int ncounters;
 };

@@ -6,29 +6,34 @@
 //   forward  (TRANS_B = false): Y  = deq Q(X) deq Q(R)^T + XL [B|L2]^T     (§3.1)
 //   backward (TRANS_B = true ): dX = deq Q(G) deq Q(R)   + GB [A;L1]       (§3.2)
 //
-// Operand A is always an MXFP4 tensor [M x Kred] read along its rows. Operand B is the
-// frozen Q(R) [N x K]: the forward reads its rows (reduction over K); the backward
-// reduces over N, i.e. reads Q(R) down its columns. Because the 32x32 block scales are
-// local to a block, the backward uses the very same codes and scale bytes: code tiles
-// are staged row-major in LDS and read transposed with ds_read_b64_tr_b4 (a 16x16
-// nibble transpose across 16 lanes), and each lane picks the scale byte of the block
-// its 32 reduction elements fall in (§3.2: a 4-bit block and its scale are fetched
-// together in either orientation, with no dequantize/requantize).
+// The activation operand is an MXFP4 tensor [M x Kred] read along its rows. Q(R) is the
+// frozen [N x K] weight: the forward reduces over its rows' K; the backward reduces
+// over N, i.e. reads Q(R) down its columns. Because the 32x32 block scales are local to
+// a block, the backward uses the very same codes and scale bytes: code tiles are staged
+// row-major in LDS and read transposed with ds_read_b64_tr_b4 (a 16x16 nibble transpose
+// across 16 lanes), and each lane picks the scale byte of the block its 32 reduction
+// elements fall in (§3.2: a 4-bit block and its scale are fetched together in either
+// orientation, with no dequantize/requantize).
 //
-// Tiling. A workgroup of 4 waves computes a 256 x 256 output tile; each wave a
+// Tiling. A workgroup of 4 waves computes a 256 x 256 output tile, each wave a
 // 128 x 128 quarter as 4 x 4 tiles of V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP4 x FP4,
-// E8M0 scale per lane = per 32 reduction elements). The reduction advances 128
-// elements per step; each step's A and B code tiles (16 KB each) are double-buffered
-// in LDS, the next step's global loads being in flight while the current step's 32
-// MFMAs per wave run. LDS rows are XOR-swizzled in 16-byte units so that both the
-// fragment reads and the staging writes are free of bank conflicts.
+// one E8M0 scale per lane = per 32 reduction elements). The reduction advances 128
+// elements per step. Each step's two code tiles (16 KB each) are brought into one of
+// four LDS stages by direct-to-LDS buffer loads issued three steps ahead, so the
+// memory latency of a step hides behind three steps of MFMAs. The block scales of the
+// workgroup's rows and columns for the whole reduction are staged into LDS once, before
+// the main loop. LDS rows are XOR-swizzled in 16-byte units so fragment reads hit
+// distinct banks.
 //
-// MFMA operand layout (32x32x64, FP4): lane l holds row l%32 of its operand and the
-// 32 reduction elements (l/32)*32 .. +32 of the 64-step, two per byte, even element
-// in the low nibble; its scale operand byte (selected by op_sel) scales those 32.
-// Accumulator register r of lane l is element (8*(r/4) + 4*(l/32) + r%4, l%32).
-// The bf16 MFMA 32x32x16 uses the same accumulator layout, 8 bf16 per lane at
-// reduction offset (l/32)*8.
+// Operand order. The MFMA's first operand is the Q(R) side (output columns), the second
+// the activation side (output rows): a lane's accumulator registers 4g..4g+3 then hold
+// four consecutive output columns of one output row, so results leave in 8- or 16-byte
+// stores. MFMA layout (32x32x64, FP4): lane l holds row l%32 of an operand and the 32
+// reduction elements (l/32)*32 .. +32 of the 64-step, two per byte, even element in
+// the low nibble; the scale operand byte chosen by op_sel scales those 32. Accumulator
+// register r of lane l is element (8*(r/4) + 4*(l/32) + r%4, l%32) of the 32x32 tile
+// (first-operand index, second-operand index). The bf16 MFMA 32x32x16 has the same
+// accumulator layout, 8 bf16 per lane at reduction offset (l/32)*8.
 #include "common.h"
 #include "gemm.h"
 
@@ -36,13 +41,17 @@ namespace ft {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;  // output tile, reduction step (elements)
-constexpr int WAVES = 4;
-constexpr int TI = 4, TJ = 4;                 // 32x32 MFMA tiles per wave (rows, cols)
-constexpr int A_TILE_BYTES = BM * BK / 2;     // 16 KB
-constexpr int B_TILE_BYTES = BN * BK / 2;     // 16 KB
+constexpr int BM = 256, BN = 256, BK = 128;    // output tile (rows, cols), reduction step
+constexpr int TI = 4, TJ = 4;                  // 32x32 MFMA tiles per wave: R side, act side
+constexpr int TILE_BYTES = 256 * BK / 2;       // 16 KB of codes per operand tile per step
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // activation tile + R tile
+constexpr int STAGES = 4;
+constexpr int SEGS = TILE_BYTES / 1024 / 4;    // 1 KB load segments per wave per tile (4)
+constexpr int SCALE_BYTES = 8192;              // LDS for the two operands' block scales
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES + SCALE_BYTES;
+constexpr int MAX_NKB = SCALE_BYTES / 2 / 8;   // 8 block rows per operand: Kred <= 16384
+constexpr int SW = 8 * MAX_NKB / 4 / 256;      // scale words staged per thread per operand (4)
 
-typedef __attribute__((address_space(3))) char lds_char;
 typedef int v2i __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4i lds_read_b128(const lds_char* p) {
@@ -51,60 +60,62 @@ __device__ __forceinline__ v4i lds_read_b128(const lds_char* p) {
 __device__ __forceinline__ void lds_write_b128(lds_char* p, v4i v) {
   *reinterpret_cast<__attribute__((address_space(3))) v4i*>(p) = v;
 }
-__device__ __forceinline__ v2i lds_read_tr4(const lds_char* p) {
-  return __builtin_amdgcn_ds_read_tr4_b64_v2i32(
-      (__attribute__((address_space(3))) v2i*)(p));
-}
 
-// A / forward-B tiles: 256 rows x 64 bytes, 16-byte unit c stored at unit c ^ ((row>>2)&3).
-__device__ __forceinline__ int swz64(int row, int c16) {
-  return row * 64 + ((c16 ^ ((row >> 2) & 3)) << 4);
-}
-// backward-B tile: 128 rows (reduction) x 128 bytes (256 output columns),
-// 16-byte unit c stored at unit c ^ ((row>>1)&7).
-__device__ __forceinline__ int swz128(int row, int c16) {
-  return row * 128 + ((c16 ^ ((row >> 1) & 7)) << 4);
-}
+// Activation / forward-R tiles have 64-byte rows (four 16-byte units); unit c of row
+// r is stored at unit c ^ swz4(r). swz4 is distinct over the four rows of either
+// parity among 8 consecutive rows and over rows r, r+4, r+8, r+12, so 16-byte reads of
+// one logical unit by consecutive rows meet distinct banks whether LDS serves 8 or 16
+// lanes per cycle.
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int off64(int row, int c16) { return row * 64 + ((c16 ^ swz4(row)) << 4); }
+// Backward-R tiles have 128-byte rows (eight units); swz8 is distinct over each parity
+// class of 16 consecutive rows, as the 16-lane transposed reads need.
+__device__ __forceinline__ int swz8(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
+__device__ __forceinline__ int off128(int row, int c16) { return row * 128 + ((c16 ^ swz8(row)) << 4); }
 
-struct Frag {  // global -> LDS staging registers of one thread for one operand tile
-  v4i v[4];
-};
-
-__device__ __forceinline__ v4i ldg_b128(const uint8_t* p, bool ok) {
-  if (!ok) return v4i{0, 0, 0, 0};
-  return *reinterpret_cast<const v4i*>(p);
-}
-
-__device__ __forceinline__ uint32_t ldg_u32(const uint8_t* p, bool ok) {
-  return ok ? *reinterpret_cast<const uint32_t*>(p) : 0u;
-}
-__device__ __forceinline__ uint32_t ldg_u8(const uint8_t* p, bool ok) { return ok ? (uint32_t)*p : 0u; }
-
-// 4 consecutive scale bytes of row `rb` starting at block column `kb` (zero past the end).
-__device__ __forceinline__ uint32_t load_scale4(const uint8_t* s, int64_t rb, int64_t nrb,
-                                                int64_t kb, int64_t nkb, bool vec_ok) {
-  if (rb >= nrb) return 0u;
-  const uint8_t* p = s + rb * nkb + kb;
-  if (vec_ok) return *reinterpret_cast<const uint32_t*>(p);
-  uint32_t w = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (kb + q < nkb) w |= (uint32_t)p[q] << (8 * q);
-  return w;
-}
-
-__device__ __forceinline__ v16f mfma_fp4(v4i a, v4i b, v16f c, uint32_t sa, uint32_t sb, int s) {
-  v8i a8 = {a.x, a.y, a.z, a.w, 0, 0, 0, 0};
-  v8i b8 = {b.x, b.y, b.z, b.w, 0, 0, 0, 0};
-  if (s == 0)
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 0, (int)sa, 0, (int)sb);
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, 2, (int)sa, 2, (int)sb);
+// first operand (R side) and its scale word with op_sel SA; second (activation) with SB
+template <int SA, int SB>
+__device__ __forceinline__ v16f mfma_fp4(v4i r, v4i x, v16f c, uint32_t sr, uint32_t sx) {
+  v8i a8 = {r.x, r.y, r.z, r.w, 0, 0, 0, 0};
+  v8i b8 = {x.x, x.y, x.z, x.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, SA, (int)sr, SB, (int)sx);
 }
 
 __device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+
+// Wait until at most N vector-memory operations of this wave are outstanding, then
+// meet the other waves. The memory clobber keeps the compiler from moving LDS accesses
+// across it; unlike __syncthreads() it does not drain loads that may stay in flight.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  static_assert(N == 0 || N == 16, "vmcnt immediate");
+  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Four transposed 16x16-nibble reads (two output-column fragments) and the wait for
+// them in one block: the LDS-bound loads still in flight write other stages, and
+// issuing the reads here keeps the compiler from draining those loads first.
+__device__ __forceinline__ void tr4_x4(const lds_char* p0, const lds_char* p1, const lds_char* p2,
+                                       const lds_char* p3, v4i& f0, v4i& f1) {
+  v2i a, b, c, d;
+  asm volatile(
+      "ds_read_b64_tr_b4 %0, %4\n\t"
+      "ds_read_b64_tr_b4 %1, %5\n\t"
+      "ds_read_b64_tr_b4 %2, %6\n\t"
+      "ds_read_b64_tr_b4 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+      : "v"((uint32_t)(uintptr_t)p0), "v"((uint32_t)(uintptr_t)p1), "v"((uint32_t)(uintptr_t)p2),
+        "v"((uint32_t)(uintptr_t)p3)
+      : "memory");
+  f0 = v4i{a.x, a.y, b.x, b.y};
+  f1 = v4i{c.x, c.y, d.x, d.y};
+}
+
 
 // Workgroup -> output tile. Workgroups are dealt round-robin to the 8 XCDs; renumber
 // so each XCD gets a contiguous run of tiles, then walk tiles in bands of GROUP_M
@@ -123,67 +134,151 @@ __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_m, int tiles
 
 template <bool TRANS_B, bool OUT_BF16>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
-  extern __shared__ __align__(16) char smem_raw[];
+  __shared__ __align__(16) char smem_raw[LDS_BYTES];
   lds_char* smem = (lds_char*)(smem_raw);
-  lds_char* sA[2] = {smem, smem + A_TILE_BYTES};
-  lds_char* sB[2] = {smem + 2 * A_TILE_BYTES, smem + 2 * A_TILE_BYTES + B_TILE_BYTES};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // wave's half of the tile rows / columns
+  const int half = lane >> 5;               // which 32-element half of a 64-step this lane holds
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t Kred = g.Kred;
   const int KT = (int)((Kred + BK - 1) / BK);
-  const int64_t a_pitch = Kred >> 1;                        // bytes per A row
-  const int64_t nkb_a = Kred >> 5;                          // scale blocks per A row
-  const int64_t nrb_a = (g.M + 31) >> 5;
-  const bool a_vec = (nkb_a & 3) == 0;
 
-  // ---------------------------------------------------------------- staging helpers
-  auto load_a = [&](int kt, Frag& f) {
+  const int64_t a_pitch = Kred >> 1;                    // bytes per activation row
+  const int64_t nkb = Kred >> 5;                        // scale blocks per reduction row
+  const int64_t nrb_a = (g.M + 31) >> 5;
+  const int64_t r_rows = TRANS_B ? Kred : g.N;          // rows of Q(R)
+  const int64_t nkb_r = TRANS_B ? (g.N >> 5) : nkb;     // scale bytes per R block row
+  const bool vec_scales = (nkb & 7) == 0;
+
+  const bufres ra = make_buf(g.a_codes, (uint64_t)g.M * a_pitch);
+  const bufres rsa = make_buf(g.a_scales, (uint64_t)nrb_a * nkb);
+  const bufres rr = make_buf(g.b_codes, (uint64_t)r_rows * g.b_pitch);
+  const bufres rsr = make_buf(g.b_scales, (uint64_t)((r_rows + 31) >> 5) * nkb_r);
+
+  // ---- per-lane DMA sources: segment q (1 KB) of a tile; lane l fills the 16-byte LDS
+  // slot 16*l of the segment.
+  //   activation / forward-R tile (64-byte rows): rows 16q + l/4, slot unit l%4
+  //   backward-R tile (128-byte rows, reduction rows x 256 output columns):
+  //     rows 8q + l/8, slot unit l%8
+  uint32_t a_base[SEGS], r_base[SEGS];
+  bool a_ok[SEGS], r_ok[SEGS];
+  int a_k[SEGS], r_k[SEGS];  // reduction offset within the step (elements)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 2, c16 = c & 3;
-      const int64_t gr = m0 + row, gk = (int64_t)kt * BK + c16 * 32;
-      f.v[i] = ldg_b128(g.a_codes + gr * a_pitch + (gk >> 1), gr < g.M && gk < Kred);
+  for (int i = 0; i < SEGS; ++i) {
+    const int q = wave * SEGS + i;
+    {
+      const int row = 16 * q + (lane >> 2), c16 = (lane & 3) ^ swz4(row);
+      a_k[i] = c16 * 32;
+      a_ok[i] = m0 + row < g.M;
+      a_base[i] = (uint32_t)((m0 + row) * a_pitch + c16 * 16);
     }
-  };
-  auto store_a = [&](lds_char* dst, const Frag& f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, row = c >> 2, c16 = c & 3;
-      lds_write_b128(dst + swz64(row, c16), f.v[i]);
-    }
-  };
-  auto load_b = [&](int kt, Frag& f) {
     if constexpr (!TRANS_B) {
-      // B rows are R rows n0.. (reduction over K, K-contiguous)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, row = c >> 2, c16 = c & 3;
-        const int64_t gr = n0 + row, gk = (int64_t)kt * BK + c16 * 32;
-        f.v[i] = ldg_b128(g.b_codes + gr * g.b_pitch + (gk >> 1), gr < g.N && gk < Kred);
-      }
+      const int row = 16 * q + (lane >> 2), c16 = (lane & 3) ^ swz4(row);
+      r_k[i] = c16 * 32;
+      r_ok[i] = n0 + row < g.N;
+      r_base[i] = (uint32_t)((n0 + row) * g.b_pitch + c16 * 16);
     } else {
-      // R rows kt*128 .. +128 (reduction index), 256 output columns n0.. (128 bytes)
+      const int row = 8 * q + (lane >> 3), c16 = (lane & 7) ^ swz8(row);
+      r_k[i] = row;
+      r_ok[i] = n0 + c16 * 32 < g.N;
+      r_base[i] = (uint32_t)(row * g.b_pitch + (n0 >> 1) + c16 * 16);
+    }
+  }
+  lds_char* stages = smem;
+  auto issue_stage = [&](int kt) {
+    lds_char* st = stages + (kt % STAGES) * STAGE_BYTES;
+    const bool live = kt < KT;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, row = c >> 3, c16 = c & 7;
-        const int64_t gr = (int64_t)kt * BK + row, gc = n0 + c16 * 32;
-        f.v[i] = ldg_b128(g.b_codes + gr * g.b_pitch + (gc >> 1), gr < Kred && gc < g.N);
-      }
+    for (int i = 0; i < SEGS; ++i) {
+      const int q = wave * SEGS + i;
+      const bool ka = live && a_ok[i] && (int64_t)kt * BK + a_k[i] < Kred;
+      buf_load16_lds(ra, st + q * 1024, ka ? a_base[i] + (uint32_t)kt * (BK / 2) : BUF_OOB);
+      const bool kr = live && r_ok[i] && (int64_t)kt * BK + r_k[i] < Kred;
+      uint32_t ro;
+      if constexpr (!TRANS_B) ro = r_base[i] + (uint32_t)kt * (BK / 2);
+      else ro = r_base[i] + (uint32_t)((int64_t)kt * BK * g.b_pitch);
+      buf_load16_lds(rr, st + TILE_BYTES + q * 1024, kr ? ro : BUF_OOB);
     }
   };
-  auto store_b = [&](lds_char* dst, const Frag& f) {
+
+  // ---- block scales for the whole reduction, staged once:
+  //   sSA[j][kb]: activation row block j (0..7) of the tile, reduction block kb
+  //   sSR[i][kb]: R side, output block i (0..7) of the tile (the backward stores the
+  //               transposed scale matrix here, so both directions read alike)
+  // Rows are padded to a multiple of 4 bytes (zeros) for 32-bit reads. The loads are
+  // issued before the first stages' and written to LDS after them, so their latency
+  // overlaps.
+  const int sp = (int)((nkb + 3) & ~3);
+  lds_char* sSA = smem + STAGES * STAGE_BYTES;
+  lds_char* sSR = sSA + SCALE_BYTES / 2;
+  const int wpr = sp / 4;  // words per staged row
+  uint32_t sa_w[SW], sr_w[SW], st_lo[2], st_hi[2];
+  auto word = [&](bufres res, int64_t row, bool row_ok, int64_t pitch, int kw) -> uint32_t {
+    // bytes 4kw .. 4kw+3 of a scale row, zero past the row end
+    const int64_t o = row * pitch + 4 * kw;
+    if ((pitch & 3) == 0) return buf_load4(res, (row_ok && 4 * kw < pitch) ? (uint32_t)o : BUF_OOB);
+    uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      if constexpr (!TRANS_B)
-        lds_write_b128(dst + swz64(c >> 2, c & 3), f.v[i]);
-      else
-        lds_write_b128(dst + swz128(c >> 3, c & 7), f.v[i]);
+    for (int q = 0; q < 4; ++q)
+      w |= buf_load1(res, (row_ok && 4 * kw + q < pitch) ? (uint32_t)(o + q) : BUF_OOB) << (8 * q);
+    return w;
+  };
+#pragma unroll
+  for (int u = 0; u < SW; ++u) {
+    const int e = tid + 256 * u, blk = e / max(wpr, 1), kw = e % max(wpr, 1);
+    const bool live = e < 8 * wpr;
+    const int64_t arb = (m0 >> 5) + blk;
+    sa_w[u] = word(rsa, arb, live && arb < nrb_a, nkb, kw);
+    if constexpr (!TRANS_B) {
+      const int64_t rrb = (n0 >> 5) + blk;
+      sr_w[u] = word(rsr, rrb, live && rrb < ((g.N + 31) >> 5), nkb, kw);
+    }
+  }
+  if constexpr (TRANS_B) {
+    // scale row kb (reduction block) holds output blocks cb0 .. cb0+7 in 8 bytes
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kb = tid + 256 * u;
+      const bool live = kb < nkb;
+      const int64_t o = (int64_t)kb * nkb_r + (n0 >> 5);
+      if ((nkb_r & 3) == 0) {
+        st_lo[u] = buf_load4(rsr, live ? (uint32_t)o : BUF_OOB);
+        st_hi[u] = buf_load4(rsr, live ? (uint32_t)(o + 4) : BUF_OOB);
+      } else {
+        st_lo[u] = st_hi[u] = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t b = buf_load1(rsr, (live && (n0 >> 5) + q < nkb_r) ? (uint32_t)(o + q) : BUF_OOB);
+          if (q < 4) st_lo[u] |= b << (8 * q);
+          else st_hi[u] |= b << (8 * (q - 4));
+        }
+      }
+    }
+  }
+  auto write_scales = [&]() {
+#pragma unroll
+    for (int u = 0; u < SW; ++u) {
+      const int e = tid + 256 * u, blk = e / max(wpr, 1), kw = e % max(wpr, 1);
+      if (e < 8 * wpr) {
+        *(__attribute__((address_space(3))) uint32_t*)(sSA + blk * sp + 4 * kw) = sa_w[u];
+        if constexpr (!TRANS_B) *(__attribute__((address_space(3))) uint32_t*)(sSR + blk * sp + 4 * kw) = sr_w[u];
+      }
+    }
+    if constexpr (TRANS_B) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int kb = tid + 256 * u;
+        if (kb < sp) {  // rows kb in [nkb, sp) are the zero padding
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            sSR[q * sp + kb] = (char)(((q < 4 ? st_lo[u] : st_hi[u]) >> (8 * (q & 3))) & 0xFFu);
+        }
+      }
     }
   };
 
@@ -193,146 +288,240 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
 
-  Frag fa, fb;
-  load_a(0, fa);
-  load_b(0, fb);
-  store_a(sA[0], fa);
-  store_b(sB[0], fb);
-  __syncthreads();
-
-  const int half = lane >> 5;  // which 32-element half of the 64-step this lane holds
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) {
-      load_a(kt + 1, fa);
-      load_b(kt + 1, fb);
-    }
-    // scale bytes of this step: A row-block of each row tile, 4 reduction blocks
-    uint32_t sa[TI], sb[TJ];
+  // ---- one reduction step of MFMAs. A 32-bit scale read gives the step's 4 reduction
+  // blocks; shifted by this lane's half, substep s's byte sits at position 2s (op_sel).
+  auto compute = [&](int kt) {
+    const lds_char* st = stages + (kt % STAGES) * STAGE_BYTES;
+    const lds_char* sX = st;
+    const lds_char* sR = st + TILE_BYTES;
+    uint32_t xs[TJ], rs[TI];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int64_t rb = (m0 + wm * 128 + 32 * i) >> 5;
-      sa[i] = load_scale4(g.a_scales, rb, nrb_a, (int64_t)kt * 4, nkb_a, a_vec) >> (8 * half);
-    }
-    if constexpr (!TRANS_B) {
-      const int64_t nkb_b = Kred >> 5, nrb_b = (g.N + 31) >> 5;
+    for (int j = 0; j < TJ; ++j)
+      xs[j] = *(const __attribute__((address_space(3))) uint32_t*)(sSA + (wm * 4 + j) * sp + kt * 4) >> (8 * half);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int64_t rb = (n0 + wn * 128 + 32 * j) >> 5;
-        sb[j] = load_scale4(g.b_scales, rb, nrb_b, (int64_t)kt * 4, nkb_b, (nkb_b & 3) == 0) >> (8 * half);
-      }
-    } else {
-      // reduction blocks kt*4 + {half, 2 + half}; output block column of tile j
-      const int64_t nkb_b = g.N >> 5, nrb_b = (Kred + 31) >> 5;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int64_t cb = (n0 + wn * 128 + 32 * j) >> 5;
-        const int64_t rb0 = (int64_t)kt * 4 + half, rb1 = rb0 + 2;
-        const bool cok = cb < nkb_b;
-        sb[j] = ldg_u8(g.b_scales + rb0 * nkb_b + cb, cok && rb0 < nrb_b) |
-                (ldg_u8(g.b_scales + rb1 * nkb_b + cb, cok && rb1 < nrb_b) << 16);
-      }
-    }
+    for (int i = 0; i < TI; ++i)
+      rs[i] = *(const __attribute__((address_space(3))) uint32_t*)(sSR + (wn * 4 + i) * sp + kt * 4) >> (8 * half);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      v4i af[TI], bf[TJ];
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        const int row = wm * 128 + 32 * i + (lane & 31);
-        af[i] = lds_read_b128(sA[cur] + swz64(row, 2 * s + half));
-      }
+      v4i xf[TJ], rf[TI];
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        if constexpr (!TRANS_B) {
-          const int row = wn * 128 + 32 * j + (lane & 31);
-          bf[j] = lds_read_b128(sB[cur] + swz64(row, 2 * s + half));
-        } else {
-          // column kc of the tile; rows 64s + 32*half + 16h + (lane&15) of the group
-          const int grp = lane >> 4;
-          const int kc = wn * 128 + 32 * j + 16 * (grp & 1);
-          const int rbase = 64 * s + 32 * (grp >> 1) + (lane & 15);
-          const int unit = kc >> 5, sub8 = ((kc >> 4) & 1) << 3;
-          v2i h0 = lds_read_tr4(sB[cur] + swz128(rbase, unit) + sub8);
-          v2i h1 = lds_read_tr4(sB[cur] + swz128(rbase + 16, unit) + sub8);
-          bf[j] = v4i{h0.x, h0.y, h1.x, h1.y};
+        const int row = wm * 128 + 32 * j + (lane & 31);
+        xf[j] = lds_read_b128(sX + off64(row, 2 * s + half));
+      }
+      if constexpr (!TRANS_B) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const int row = wn * 128 + 32 * i + (lane & 31);
+          rf[i] = lds_read_b128(sR + off64(row, 2 * s + half));
         }
+      } else {
+        // output column c = wn*128 + 32i + (lane&31); reduction rows
+        // 64s + 32*half + 16h + (lane&15): two 16x16 nibble transposes per fragment
+        const int grp = lane >> 4;
+        const int rbase = 64 * s + 32 * (grp >> 1) + (lane & 15);
+        const lds_char* p[TI][2];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const int c = wn * 128 + 32 * i + 16 * (grp & 1);
+          const int unit = c >> 5, sub8 = ((c >> 4) & 1) << 3;
+          p[i][0] = sR + off128(rbase, unit) + sub8;
+          p[i][1] = sR + off128(rbase + 16, unit) + sub8;
+        }
+        tr4_x4(p[0][0], p[0][1], p[1][0], p[1][1], rf[0], rf[1]);
+        tr4_x4(p[2][0], p[2][1], p[3][0], p[3][1], rf[2], rf[3]);
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_fp4(af[i], bf[j], acc[i][j], sa[i], sb[j], s);
+        for (int j = 0; j < TJ; ++j) {
+          if (s == 0) acc[i][j] = mfma_fp4<0, 0>(rf[i], xf[j], acc[i][j], rs[i], xs[j]);
+          else acc[i][j] = mfma_fp4<2, 2>(rf[i], xf[j], acc[i][j], rs[i], xs[j]);
+        }
     }
-    if (kt + 1 < KT) {
-      store_a(sA[cur ^ 1], fa);
-      store_b(sB[cur ^ 1], fb);
-    }
-    __syncthreads();
+  };
+
+  // ---------------------------------------------------------------- main loop
+  // Branch-free: past the last step the loads go to out-of-range offsets (zeros into a
+  // stage nobody reads), so every step waits with the same count: the two most recent
+  // steps' 2 x 8 loads may stay in flight.
+  issue_stage(0);
+  issue_stage(1);
+  issue_stage(2);
+  write_scales();
+  vm_barrier<16>();  // step 0 landed; the scale bytes are in LDS
+  for (int kt = 0; kt < KT; ++kt) {
+    issue_stage(kt + 3);
+    compute(kt);
+    // keep this step's MFMAs ahead of the wait: they run while later stages land
+    __builtin_amdgcn_sched_barrier(0);
+    vm_barrier<16>();
   }
+  vm_barrier<0>();  // the last (out-of-range) stage loads write LDS too
 
   // ---------------------------------------------------------------- up-projection
-  // acc += low[rows, 0:rt] * up[cols, 0:rt]^T on bf16 MFMA 32x32x16. `low` is XL (fwd)
-  // or GB (bwd), [M x rt] bf16. `up` row q holds rt values: the first up_split from
-  // up0 (row stride up0_ld), the rest from up1 (row stride up1_ld).
+  // acc += up * low^T on bf16 MFMA 32x32x16 (first operand the output-column side),
+  // `low` = XL (forward) or GB (backward), [M x rt] bf16.
   const int rt = g.rt;
-  for (int t = 0; t < rt; t += 16) {
-    const int j0 = t + 8 * half;
-    v4i la[TI], ub[TJ];
+  const bufres rl = make_buf(g.low, (uint64_t)g.M * rt * 2);
+  if constexpr (!TRANS_B) {
+    // forward: up = [B | L2], row q (output column) = rt values read straight from
+    // memory: the first up_split from up0 (row stride up0_ld), the rest from up1.
+    const bufres ru0 = make_buf(g.up0, (uint64_t)g.N * g.up0_ld * 2);
+    const bufres ru1 = make_buf(g.up1, (uint64_t)g.N * g.up1_ld * 2);
+    for (int t0 = 0; t0 < rt; t0 += 64) {  // up to four 16-steps' operands in flight
+      v4i la[4][TJ], ub[4][TI];
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const int64_t row = m0 + wm * 128 + 32 * i + (lane & 31);
-      la[i] = row < g.M ? *reinterpret_cast<const v4i*>(g.low + row * rt + j0) : v4i{0, 0, 0, 0};
+      for (int u = 0; u < 4; ++u) {
+        const int t = t0 + 16 * u, j0 = t + 8 * half;
+        const bool live = t < rt;
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int64_t row = m0 + wm * 128 + 32 * j + (lane & 31);
+          la[u][j] = buf_load16(rl, live ? (uint32_t)((row * rt + j0) * 2) : BUF_OOB);
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const int64_t q = n0 + wn * 128 + 32 * i + (lane & 31);
+          ub[u][i] = (live && t < g.up_split) ? buf_load16(ru0, (uint32_t)((q * g.up0_ld + j0) * 2))
+                                              : buf_load16(ru1, live ? (uint32_t)((q * g.up1_ld + j0 - g.up_split) * 2) : BUF_OOB);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t0 + 16 * u >= rt) break;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(ub[u][i], la[u][j], acc[i][j]);
+      }
     }
+  } else {
+    // backward: up = [A; L1] [rt x N] (row j = up0 row j for j < up_split, else up1 row
+    // j - up_split; row strides up*_ld). The MFMA wants 8 consecutive j per output
+    // column, so 32-row slabs of the tile's 256 columns are staged in LDS (free after
+    // the main loop) and read transposed with ds_read_b64_tr_b16.
+    constexpr int DP = BN * 2 + 32;  // slab row pitch (bytes), padded against bank conflicts
+    const bufres ru0 = make_buf(g.up0, (uint64_t)g.up_split * g.up0_ld * 2);
+    const bufres ru1 = make_buf(g.up1, (uint64_t)(rt - g.up_split) * g.up1_ld * 2);
+    for (int jc = 0; jc < rt; jc += 32) {
+      v4i la[2][TJ];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int64_t q = n0 + wn * 128 + 32 * j + (lane & 31);
-      const bf16_t* p = j0 < g.up_split ? g.up0 + q * g.up0_ld + j0
-                                        : g.up1 + q * g.up1_ld + (j0 - g.up_split);
-      ub[j] = q < g.N ? *reinterpret_cast<const v4i*>(p) : v4i{0, 0, 0, 0};
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int64_t row = m0 + wm * 128 + 32 * j + (lane & 31);
+          la[u][j] = buf_load16(rl, (uint32_t)((row * rt + jc + 16 * u + 8 * half) * 2));
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i, row = c >> 5, c16 = c & 31;
+        const int j = jc + row;
+        const int64_t col = n0 + 8 * c16;
+        const bool ok = col < g.N;
+        const v4i v = j < g.up_split
+                          ? buf_load16(ru0, ok ? (uint32_t)(((int64_t)j * g.up0_ld + col) * 2) : BUF_OOB)
+                          : buf_load16(ru1, ok ? (uint32_t)(((int64_t)(j - g.up_split) * g.up1_ld + col) * 2) : BUF_OOB);
+        lds_write_b128(smem + row * DP + c16 * 16, v);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        v4i ub[TI];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) ub[i] = lds_tr16_pair(smem, DP, 16 * u, wn * 128 + 32 * i, lane);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(ub[i], la[u][j], acc[i][j]);
+      }
+      __syncthreads();
     }
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(la[i], ub[j], acc[i][j]);
   }
 
   // ---------------------------------------------------------------- store
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
+  // Each wave stages its 128 x 128 result in LDS (the stages are free now), then 16
+  // consecutive lanes write 256 contiguous bytes of one output row per instruction.
+  // acc[i][j]: lane holds output row 32j + l%32 of the wave tile and, in registers
+  // 4g..4g+3, columns 32i + 8g + 4*half .. +4.
+  __syncthreads();
+  lds_char* wbuf = smem + wave * 34816;  // 128 rows x 272 bytes (256 + 16 padding)
+  constexpr int OP = 272;
+  const int64_t orow0 = m0 + wm * 128, ocol0 = n0 + wn * 128;
+  if constexpr (OUT_BF16) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const int64_t col = n0 + wn * 128 + 32 * j + (lane & 31);
-      if (col >= g.N) continue;
+      const int r = 32 * j + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row < g.M) {
-          if constexpr (OUT_BF16)
-            reinterpret_cast<bf16_t*>(g.out)[row * g.ldo + col] = (bf16_t)f32_to_bf16_bits(acc[i][j][r]);
-          else
-            reinterpret_cast<float*>(g.out)[row * g.ldo + col] = acc[i][j][r];
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const v16f& a = acc[i][j];
+          const v2i v = {(int)pack_bf16x2(a[4 * gq], a[4 * gq + 1]),
+                         (int)pack_bf16x2(a[4 * gq + 2], a[4 * gq + 3])};
+          *(__attribute__((address_space(3))) v2i*)(wbuf + r * OP + (32 * i + 8 * gq + 4 * half) * 2) = v;
         }
-      }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
+#pragma unroll 4
+    for (int k = 0; k < 32; ++k) {  // 4 rows x 256 bytes per instruction
+      const int r = 4 * k + (lane >> 4), c = (lane & 15) * 8;
+      const v4i v = lds_read_b128(wbuf + r * OP + c * 2);
+      const int64_t row = orow0 + r, col = ocol0 + c;
+      if (row < g.M && col < g.N)
+        *reinterpret_cast<v4i*>(reinterpret_cast<bf16_t*>(g.out) + row * g.ldo + col) = v;
+    }
+  } else {
+    // fp32: two passes of 64 rows (64 x 512 bytes per wave)
+    constexpr int OPF = 528;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * p + jj;
+        const int r = 32 * jj + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const v16f& a = acc[i][j];
+            *(__attribute__((address_space(3))) v4f*)(wbuf + r * OPF + (32 * i + 8 * gq + 4 * half) * 4) =
+                v4f{a[4 * gq], a[4 * gq + 1], a[4 * gq + 2], a[4 * gq + 3]};
+          }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll 4
+      for (int k = 0; k < 32; ++k) {  // 2 rows x 512 bytes per instruction
+        const int r = 2 * k + (lane >> 5), c = (lane & 31) * 4;
+        const v4i v = lds_read_b128(wbuf + r * OPF + c * 4);
+        const int64_t row = orow0 + 64 * p + r, col = ocol0 + c;
+        if (row < g.M && col < g.N)
+          *reinterpret_cast<v4i*>(reinterpret_cast<float*>(g.out) + row * g.ldo + col) = v;
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  }
 }
 
 }  // namespace
 
-constexpr size_t GEMM_LDS = 2 * (A_TILE_BYTES + B_TILE_BYTES);
+static_assert(GEMM_MAX_KRED == MAX_NKB * 32, "scale staging bound");
 
 hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipStream_t stream) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
+  if (g.Kred > GEMM_MAX_KRED) return hipErrorInvalidValue;
   const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
   dim3 grid(tiles), block(256);
   if (!trans_b) {
     if (out_bf16)
-      hipLaunchKernelGGL((k_gemm_mx4<false, true>), grid, block, GEMM_LDS, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<false, true>), grid, block, 0, stream, g);
     else
-      hipLaunchKernelGGL((k_gemm_mx4<false, false>), grid, block, GEMM_LDS, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<false, false>), grid, block, 0, stream, g);
   } else {
     if (out_bf16)
-      hipLaunchKernelGGL((k_gemm_mx4<true, true>), grid, block, GEMM_LDS, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<true, true>), grid, block, 0, stream, g);
     else
-      hipLaunchKernelGGL((k_gemm_mx4<true, false>), grid, block, GEMM_LDS, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<true, false>), grid, block, 0, stream, g);
   }
   return hipGetLastError();
 }

@@ -1,8 +1,8 @@
 // Low-rank side of the backward pass (FourTune §3.2: gradients propagate through all
 // three branches; parameter updates are computed for the adapter only).
 //
-// k_prep_bwd   : [B | L2]^T and [A; L1]^T in workspace (the operand layouts the
-//                bf16 MFMAs read), and zeroed tile counters for k_lora_grad.
+// k_prep_bwd   : [B | L2]^T in workspace (the operand layout the G-side
+//                down-projection reads), and zeroed tile counters for k_lora_grad.
 // k_lora_grad  : dA = GB[:, :r]^T bf16(X) and dB = bf16(G)^T XL[:, :r], reductions over
 //                the M rows on bf16 MFMA. Both operands are m-major in memory, so
 //                64-row slabs are staged in LDS and read transposed with
@@ -14,47 +14,32 @@ namespace ft {
 
 namespace {
 
-typedef __attribute__((address_space(3))) char lds_char;
-typedef short v4s __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ prep (transposes)
 constexpr int TT = 64;  // transpose tile
 
-// Element (row, col) of the virtual source matrices:
-//   job 0: U [N x rt], U(n, j) = j < r ? B[n, j] : L2[n, j - r]      -> Ut [rt x N]
-//   job 1: D [rt x K], D(j, k) = j < r ? A[j, k] : L1[j - r, k]      -> Dt [K x rt]
+// U [N x rt], U(n, j) = j < r ? B[n, j] : L2[n, j - r]  ->  Ut [rt x N]
 __global__ __launch_bounds__(256) void k_prep_bwd(const PrepArgs a) {
   __shared__ bf16_t tile[TT][TT + 2];
   const int rt = a.r + a.s;
-  const int64_t tilesU = ((a.N + TT - 1) / TT) * ((rt + TT - 1) / TT);
-  const int64_t tilesD = ((int64_t)(rt + TT - 1) / TT) * ((a.K + TT - 1) / TT);
+  const int64_t ntc = (rt + TT - 1) / TT;
+  const int64_t tiles = ((a.N + TT - 1) / TT) * ntc;
   const int64_t b = blockIdx.x;
   if (b == 0)
     for (int i = threadIdx.x; i < a.ncounters; i += 256) a.counters[i] = 0u;
-  if (b >= tilesU + tilesD) return;
-  const bool jobU = b < tilesU;
-  const int64_t tb = jobU ? b : b - tilesU;
-  const int64_t src_rows = jobU ? a.N : rt, src_cols = jobU ? rt : a.K;
-  const int64_t ntc = (src_cols + TT - 1) / TT;
-  const int64_t r0 = (tb / ntc) * TT, c0 = (tb % ntc) * TT;
+  if (b >= tiles) return;
+  const int64_t r0 = (b / ntc) * TT, c0 = (b % ntc) * TT;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   for (int i = ty; i < TT; i += 4) {
-    const int64_t row = r0 + i, col = c0 + tx;
+    const int64_t n = r0 + i, j = c0 + tx;
     bf16_t v = 0;
-    if (row < src_rows && col < src_cols) {
-      if (jobU)
-        v = col < a.r ? a.B[row * a.r + col] : a.L2[row * a.s + (col - a.r)];
-      else
-        v = row < a.r ? a.A[row * a.K + col] : a.L1[(row - a.r) * a.K + col];
-    }
+    if (n < a.N && j < rt) v = j < a.r ? a.B[n * a.r + j] : a.L2[n * a.s + (j - a.r)];
     tile[i][tx] = v;
   }
   __syncthreads();
-  // destination [src_cols x src_rows]
-  bf16_t* dst = jobU ? a.Ut : a.Dt;
   for (int i = ty; i < TT; i += 4) {
-    const int64_t drow = c0 + i, dcol = r0 + tx;
-    if (drow < src_cols && dcol < src_rows) dst[drow * src_rows + dcol] = tile[tx][i];
+    const int64_t j = c0 + i, n = r0 + tx;
+    if (j < rt && n < a.N) a.Ut[j * a.N + n] = tile[tx][i];
   }
 }
 
@@ -63,22 +48,6 @@ __global__ __launch_bounds__(256) void k_prep_bwd(const PrepArgs a) {
 // per (tile, M-split). 4 waves, each 64 big columns (2 MFMA column tiles).
 constexpr int LG_BT = 256, LG_MS = 64;  // big-tile width, rows per LDS slab
 constexpr int BIG_PITCH = LG_BT * 2 + 32;
-
-__device__ __forceinline__ v4i lds_tr16_pair(const lds_char* base, int pitch, int m0, int c0, int lane) {
-  // 8 consecutive m (m0 + 8*(l>>5) .. +8) of column c0 + (l & 31), via two tr_b16 reads
-  const int g = lane >> 4, s = lane & 15;
-  const int col = c0 + 16 * (g & 1) + 4 * (s & 3);
-  const int m = m0 + 8 * (g >> 1) + (s >> 2);
-  const lds_char* p0 = base + m * pitch + col * 2;
-  v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p0);
-  v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p0 + 4 * pitch));
-  v4i r;
-  r.x = (int)(((uint32_t)(uint16_t)lo.x) | ((uint32_t)(uint16_t)lo.y << 16));
-  r.y = (int)(((uint32_t)(uint16_t)lo.z) | ((uint32_t)(uint16_t)lo.w << 16));
-  r.z = (int)(((uint32_t)(uint16_t)hi.x) | ((uint32_t)(uint16_t)hi.y << 16));
-  r.w = (int)(((uint32_t)(uint16_t)hi.z) | ((uint32_t)(uint16_t)hi.w << 16));
-  return r;
-}
 
 // 8 consecutive elements of a bf16 or fp32 row as 8 bf16 (RNE for fp32).
 __device__ __forceinline__ uint4 load8_bf16(const void* base, bool is_bf16, int64_t off, bool ok) {
@@ -204,9 +173,8 @@ __global__ __launch_bounds__(256) void k_lora_grad(const LoraGradArgs a) {
 
 hipError_t launch_prep_bwd(const PrepArgs& a, hipStream_t stream) {
   const int rt = a.r + a.s;
-  const int64_t tilesU = ((a.N + TT - 1) / TT) * ((rt + TT - 1) / TT);
-  const int64_t tilesD = ((int64_t)(rt + TT - 1) / TT) * ((a.K + TT - 1) / TT);
-  const int64_t blocks = rt > 0 ? tilesU + tilesD : 1;
+  const int64_t tiles = ((a.N + TT - 1) / TT) * ((rt + TT - 1) / TT);
+  const int64_t blocks = tiles > 0 ? tiles : 1;
   hipLaunchKernelGGL(k_prep_bwd, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

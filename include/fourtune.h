@@ -131,6 +131,23 @@ ft_status fourtune_linear_bwd(const ft_linear *L, const void *dy, ft_dtype dy_dt
                               void *dx, ft_dtype dx_dt, float *d_lora_a, float *d_lora_b,
                               ft_mx4 *gq_out, void *ws, size_t ws_bytes, void *stream);
 
+/* fourtune_gemm_fwd -- the forward's second kernel on its own: given Q(X) and XL
+ * (e.g. produced by a previous fused epilogue), Y = Q(X) Q(R)^T + XL [B|L2]^T, the
+ * up-projection accumulated with the 4-bit product before the single store of Y
+ * (FourTune §3.3 "LoRA Fusion").
+ *   xq  Q(X), [m x k] MXFP4.   xl  [m x (rank + stab_rank)] bf16.
+ *   y   [m x n] fp32 or bf16 (y_dt), overwritten. No workspace. */
+ft_status fourtune_gemm_fwd(const ft_linear *L, const ft_mx4 *xq, const void *xl, int64_t m,
+                            void *y, ft_dtype y_dt, void *stream);
+
+/* fourtune_gemm_bwd -- the backward's 4-bit GEMM on its own: given Q(dY) and GB,
+ * dX = Q(dY) Q(R) + GB [A;L1], reading Q(R)'s codes and block scales transposed
+ * (FourTune §3.2).
+ *   gq  Q(dY), [m x n] MXFP4.  gb  [m x (rank + stab_rank)] bf16.
+ *   dx  [m x k] fp32 or bf16 (dx_dt), overwritten. No workspace. */
+ft_status fourtune_gemm_bwd(const ft_linear *L, const ft_mx4 *gq, const void *gb, int64_t m,
+                            void *dx, ft_dtype dx_dt, void *stream);
+
 /* Workspace bytes needed by fourtune_mlp_fwd and fourtune_mlp_bwd for m rows. */
 size_t fourtune_mlp_workspace_bytes(int64_t m, const ft_linear *fc1, const ft_linear *fc2);
 
