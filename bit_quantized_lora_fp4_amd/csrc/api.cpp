@@ -139,6 +139,8 @@ ft_status check_linear(const ft_linear* L, const char* who) {
   const int64_t rt = L->rank + L->stab_rank;
   REQUIRE(rt % 32 == 0, FT_ERR_SHAPE, "%s: rank + stab_rank = %lld must be a multiple of 32", who, (long long)rt);
   REQUIRE(rt <= 128, FT_ERR_UNSUPPORTED, "%s: rank + stab_rank = %lld > 128", who, (long long)rt);
+  REQUIRE(ft::quant_down_tiles((int)L->rank, (int)rt) <= ft::QD_MAX_TILES, FT_ERR_UNSUPPORTED,
+          "%s: ceil(rank/32) + ceil(stab_rank/32) > %d", who, ft::QD_MAX_TILES);
   REQUIRE(L->n <= ft::GEMM_MAX_KRED && L->k <= ft::GEMM_MAX_KRED, FT_ERR_UNSUPPORTED,
           "%s: n=%lld, k=%lld; the 4-bit GEMMs reduce over at most %lld elements", who,
           (long long)L->n, (long long)L->k, (long long)ft::GEMM_MAX_KRED);
@@ -160,51 +162,59 @@ ft_status check_tensor(const void* p, const char* who, const char* name) {
   return FT_OK;
 }
 
+// Workspace: the call's scratch (Q(X) or Q(dY) when the caller does not take them,
+// GB, fp32 partial sums of the split reductions). Nothing in it outlives a call.
 struct FwdLayout {
   uint8_t* xq_codes;
   uint8_t* xq_scales;
+  float* partials;
   size_t bytes;
 };
 
 FwdLayout fwd_layout(void* ws, int64_t m, const ft_linear* L, bool need_xq) {
   Carver c(ws);
   FwdLayout f{};
+  const int rt = (int)(L->rank + L->stab_rank);
   if (need_xq) {
     f.xq_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, L->k));
     f.xq_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, L->k));
   }
+  f.partials = c.take<float>(ft::quant_down_partial_bytes(m, L->k, (int)L->rank, rt));
   f.bytes = c.used;
   return f;
 }
 
 struct BwdLayout {
-  ft::bf16_t* Ut;
   uint8_t* gq_codes;
   uint8_t* gq_scales;
   ft::bf16_t* GB;
-  float* partials;
-  uint32_t* counters;
-  int splits, tiles;
+  float* partials;  // quant_down's, then lora_grad's (the kernels run in turn)
   size_t bytes;
 };
 
 BwdLayout bwd_layout(void* ws, int64_t m, const ft_linear* L, bool need_gq) {
   Carver c(ws);
   BwdLayout b{};
-  const int64_t rt = L->rank + L->stab_rank;
-  const int64_t rp = (L->rank + 31) / 32 * 32;
-  b.Ut = c.take<ft::bf16_t>((size_t)rt * L->n * 2);
+  const int rt = (int)(L->rank + L->stab_rank);
   if (need_gq) {
     b.gq_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, L->n));
     b.gq_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, L->n));
   }
   b.GB = c.take<ft::bf16_t>((size_t)m * rt * 2);
-  b.tiles = ft::lora_grad_tiles(L->k, L->n);
-  b.splits = L->rank > 0 ? ft::lora_grad_splits(m, L->k, L->n) : 1;
-  b.partials = c.take<float>(b.splits > 1 ? (size_t)b.splits * rp * (L->k + L->n) * 4 : 0);
-  b.counters = c.take<uint32_t>((size_t)b.tiles * 4);
+  const size_t pq = ft::quant_down_partial_bytes(m, L->n, (int)L->rank, rt);
+  const size_t pl = ft::lora_grad_partial_bytes(m, L->k, L->n, (int)L->rank);
+  b.partials = c.take<float>(pq > pl ? pq : pl);
   b.bytes = c.used;
   return b;
+}
+
+// Buffer-resource addressing is 32-bit: every activation-sized tensor stays below 4 GiB.
+ft_status check_m(int64_t m, const ft_linear* L, const char* who) {
+  const int64_t widest = L->n > L->k ? L->n : L->k;
+  // 64 rows of margin: offsets of rows just past m must not wrap around
+  REQUIRE(m + 64 <= (int64_t)(0xFFFFFF00ull / 4 / (uint64_t)widest), FT_ERR_UNSUPPORTED,
+          "%s: m=%lld rows of %lld fp32 elements exceed 4 GiB", who, (long long)m, (long long)widest);
+  return FT_OK;
 }
 
 ft_status run_gemm_fwd(const ft_linear* L, const uint8_t* xq_codes, const uint8_t* xq_scales,
@@ -254,6 +264,7 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const void* x, ft_dtype x_dt, 
   REQUIRE(dtype_ok(x_dt) && dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
   REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
   if (m == 0) return ok();
+  TRY(check_m(m, L, who));
   const int64_t rt = L->rank + L->stab_rank;
   TRY(check_tensor(x, who, "x"));
   TRY(check_tensor(y, who, "y"));
@@ -272,8 +283,9 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const void* x, ft_dtype x_dt, 
   qd.codes = xq_codes; qd.scales = xq_scales;
   qd.d0 = static_cast<const ft::bf16_t*>(L->lora_a);
   qd.d1 = static_cast<const ft::bf16_t*>(L->stab_down);
-  qd.r0 = (int)L->rank; qd.rt = (int)rt;
+  qd.r0 = (int)L->rank; qd.rt = (int)rt; qd.u_cols = false;
   qd.low = static_cast<ft::bf16_t*>(xl_saved);
+  qd.partials = lay.partials;
   TRY(hip_check(ft::launch_quant_down(qd, x_dt == FT_BF16, st), "linear_fwd quant_down"));
   TRY(run_gemm_fwd(L, xq_codes, xq_scales, xl_saved, m, y, y_dt, st));
   return ok();
@@ -288,6 +300,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
   REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
   REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
   if (m == 0) return ok();
+  TRY(check_m(m, L, who));
   const int64_t rt = L->rank + L->stab_rank;
   TRY(check_tensor(dy, who, "dy"));
   TRY(check_tensor(dx, who, "dx"));
@@ -306,18 +319,14 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
   uint8_t* gq_codes = gq_out ? gq_out->codes : lay.gq_codes;
   uint8_t* gq_scales = gq_out ? gq_out->scales : lay.gq_scales;
 
-  ft::PrepArgs pa{};
-  pa.B = static_cast<const ft::bf16_t*>(L->lora_b);
-  pa.L2 = static_cast<const ft::bf16_t*>(L->stab_up);
-  pa.N = L->n; pa.r = (int)L->rank; pa.s = (int)L->stab_rank;
-  pa.Ut = lay.Ut; pa.counters = lay.counters; pa.ncounters = lay.tiles;
-  TRY(hip_check(ft::launch_prep_bwd(pa, st), "linear_bwd prep"));
-
   ft::QuantDownArgs qd{};
   qd.x = dy; qd.M = m; qd.K = L->n; qd.ldx = L->n;
   qd.codes = gq_codes; qd.scales = gq_scales;
-  qd.d0 = lay.Ut; qd.d1 = nullptr; qd.r0 = (int)rt; qd.rt = (int)rt;
+  qd.d0 = static_cast<const ft::bf16_t*>(L->lora_b);
+  qd.d1 = static_cast<const ft::bf16_t*>(L->stab_up);
+  qd.r0 = (int)L->rank; qd.rt = (int)rt; qd.u_cols = true;
   qd.low = lay.GB;
+  qd.partials = lay.partials;
   TRY(hip_check(ft::launch_quant_down(qd, dy_dt == FT_BF16, st), "linear_bwd quant_down"));
 
   TRY(run_gemm_bwd(L, gq_codes, gq_scales, lay.GB, m, dx, dx_dt, st));
@@ -328,7 +337,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
     lg.gb = lay.GB; lg.ld_gb = rt; lg.x = x; lg.x_bf16 = x_dt == FT_BF16; lg.K = L->k; lg.dA = d_lora_a;
     lg.xl = static_cast<const ft::bf16_t*>(xl_saved); lg.ld_xl = rt; lg.g = dy;
     lg.g_bf16 = dy_dt == FT_BF16; lg.N = L->n; lg.dB = d_lora_b;
-    lg.partials = lay.partials; lg.counters = lay.counters; lg.splits = lay.splits;
+    lg.partials = lay.partials;
     TRY(hip_check(ft::launch_lora_grad(lg, st), "linear_bwd lora_grad"));
   }
   return ok();
@@ -341,6 +350,7 @@ ft_status fourtune_gemm_fwd(const ft_linear* L, const ft_mx4* xq, const void* xl
   REQUIRE(dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
   REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
   if (m == 0) return ok();
+  TRY(check_m(m, L, who));
   TRY(check_mx4(xq, m, L->k, "gemm_fwd: xq"));
   if (L->rank + L->stab_rank > 0) TRY(check_tensor(xl, who, "xl"));
   TRY(check_tensor(y, who, "y"));
@@ -355,6 +365,7 @@ ft_status fourtune_gemm_bwd(const ft_linear* L, const ft_mx4* gq, const void* gb
   REQUIRE(dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
   REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
   if (m == 0) return ok();
+  TRY(check_m(m, L, who));
   TRY(check_mx4(gq, m, L->n, "gemm_bwd: gq"));
   if (L->rank + L->stab_rank > 0) TRY(check_tensor(gb, who, "gb"));
   TRY(check_tensor(dx, who, "dx"));

@@ -8,6 +8,7 @@
 namespace ft {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -129,6 +130,19 @@ __device__ __forceinline__ uint32_t buf_load4(bufres r, uint32_t off) {
 __device__ __forceinline__ uint32_t buf_load1(bufres r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buf_store4(bufres r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store1(bufres r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, r, (int)off, 0, 0);
+}
+// `ok ? off : BUF_OOB`, kept opaque so that the optimizer does not turn the select
+// into control flow around the load that consumes it.
+__device__ __forceinline__ uint32_t sel_off(bool ok, uint32_t off) {
+  uint32_t v = ok ? off : BUF_OOB;
+  asm("" : "+v"(v));
+  return v;
+}
 // 16 bytes per lane straight into LDS: lane l's data lands at lds + 16*l.
 __device__ __forceinline__ void buf_load16_lds(bufres r, lds_char* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
@@ -141,6 +155,25 @@ __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b 
 template <int MASK>
 __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v) {
   return (uint32_t)__shfl_xor((int)v, MASK, 64);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Maximum over the 64 lanes, all in VALU: DPP butterflies inside each 16-lane row,
+// then v_permlane16_swap / v_permlane32_swap, each of which leaves a lane holding its
+// own value and that of lane ^16 (^32) in its two results.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = umax(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+  v = umax(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+  v = umax(v, dpp<0x141>(v));  // row_half_mirror: the other quad of the 8
+  v = umax(v, dpp<0x140>(v));  // row_mirror: the other half of the row
+  const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = umax(p[0], p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return umax(q[0], q[1]);
 }
 
 }  // namespace ft

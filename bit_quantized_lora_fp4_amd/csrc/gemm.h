@@ -39,8 +39,14 @@ hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipSt
 constexpr int64_t GEMM_MAX_KRED = 16384;
 
 // Fused quantize + down-projection over the rows of x [M x K] (row stride ldx):
-// Q(x) -> codes/scales, low[M x rt] = bf16( bf16(x) * D^T ), D row j = d0 row j (j < r0)
-// or d1 row j - r0, each row K-contiguous with row stride K.
+// Q(x) -> codes/scales, low[M x rt] = bf16( bf16(x) * D^T ).
+//   u_cols = false: D row j = d0 row j (j < r0) or d1 row j - r0, each K-contiguous
+//                   with row stride K ([A; L1] in the forward).
+//   u_cols = true : D^T row n = d0[n*r0 .. +r0] ++ d1[n*(rt-r0) .. +(rt-r0)]
+//                   ([B | L2] in the backward, read as stored).
+// The K range is split S = quant_down_splits(M, K, rt) ways; with S > 1 the launch
+// needs quant_down_partial_bytes(M, K, r0, rt) bytes of fp32 partials, which a second
+// kernel sums in a fixed order.
 struct QuantDownArgs {
   const void* x;
   int64_t M, K, ldx;
@@ -50,29 +56,24 @@ struct QuantDownArgs {
   const bf16_t* d1;
   int r0;
   int rt;
+  bool u_cols;
   bf16_t* low;
+  float* partials;
 };
 
 hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t stream);
-
-// Backward set-up: Ut[rt x N] = [B | L2]^T and zeroed counters.
-struct PrepArgs {
-  const bf16_t* B;   // [N x r]
-  const bf16_t* L2;  // [N x s]
-  int64_t N;
-  int r, s;
-  bf16_t* Ut;
-  uint32_t* counters;
-  int ncounters;
-};
-
-hipError_t launch_prep_bwd(const PrepArgs& a, hipStream_t stream);
+// The low-rank side is handled in ceil(r0/32) + ceil((rt-r0)/32) padded 32-wide tiles.
+int quant_down_tiles(int r0, int rt);
+constexpr int QD_MAX_TILES = 4;
+int quant_down_splits(int64_t M, int64_t K, int rt);
+size_t quant_down_partial_bytes(int64_t M, int64_t K, int r0, int rt);
 
 // LoRA parameter gradients, reductions over the M rows (FourTune §3.2: parameter updates
 // only for the adapter):
 //   dA[r x K] = GB[:, :r]^T * bf16(X)      dB[N x r] = bf16(G)^T * XL[:, :r]
-// Split over M; each split writes fp32 partials and the last split to finish a tile
-// sums all splits in a fixed order (deterministic).
+// Split over M; each split writes fp32 partials and a second kernel sums them in a
+// fixed order (deterministic).
+// X and G must each be smaller than 4 GiB (32-bit buffer offsets).
 struct LoraGradArgs {
   int64_t M;
   int r;
@@ -91,13 +92,15 @@ struct LoraGradArgs {
   int64_t N;
   float* dB;             // [N x r]
   // scratch
-  float* partials;       // [splits x r_pad x (K + N)]
-  uint32_t* counters;    // one per output tile, zero on entry, left zero on exit
-  int splits;
+  float* partials;       // lora_grad_partial_bytes(M, K, N, r) bytes
+  // set by the launcher
+  int tile_offset;
+  int ntiles;
 };
 
 hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream);
 int lora_grad_splits(int64_t M, int64_t K, int64_t N);
 int lora_grad_tiles(int64_t K, int64_t N);
+size_t lora_grad_partial_bytes(int64_t M, int64_t K, int64_t N, int r);
 
 }  // namespace ft

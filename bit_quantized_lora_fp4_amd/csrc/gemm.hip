@@ -52,7 +52,6 @@ constexpr int LDS_BYTES = STAGES * STAGE_BYTES + SCALE_BYTES;
 constexpr int MAX_NKB = SCALE_BYTES / 2 / 8;   // 8 block rows per operand: Kred <= 16384
 constexpr int SW = 8 * MAX_NKB / 4 / 256;      // scale words staged per thread per operand (4)
 
-typedef int v2i __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ v4i lds_read_b128(const lds_char* p) {
   return *reinterpret_cast<const __attribute__((address_space(3))) v4i*>(p);

@@ -1,12 +1,21 @@
-// Low-rank side of the backward pass (FourTune §3.2: gradients propagate through all
-// three branches; parameter updates are computed for the adapter only).
+// LoRA parameter gradients (FourTune §3.2: gradients flow through all three branches,
+// only the adapter is updated):
 //
-// k_prep_bwd   : [B | L2]^T in workspace (the operand layout the G-side
-//                down-projection reads), and zeroed tile counters for k_lora_grad.
-// k_lora_grad  : dA = GB[:, :r]^T bf16(X) and dB = bf16(G)^T XL[:, :r], reductions over
-//                the M rows on bf16 MFMA. Both operands are m-major in memory, so
-//                64-row slabs are staged in LDS and read transposed with
-//                ds_read_b64_tr_b16. HBM-bound: it re-reads X and G once.
+//   dA [r x K] = GB[:, :r]^T bf16(X)          dB [N x r] = bf16(G)^T XL[:, :r]
+//
+// Both are reductions over the M token rows of a narrow "small" operand (GB or XL,
+// bf16 [M x rt]) against a wide "big" one (X or G, bf16 or fp32). HBM-bound: X and G
+// are read once more, everything else is small; the flops run on bf16 MFMA.
+//
+// Work split. The output is cut into tiles of RP (r rounded up to 32) x 64 big
+// columns; the dA tiles come first, then the dB tiles. A workgroup owns one tile and
+// one of S contiguous 32-aligned row ranges; its 4 waves take the range's 32-row slabs
+// in turn (w, w+4, ...), each with the next slab's loads in flight. Both operands are
+// row-major in m, but the MFMA reduces over m inside a lane, so a wave writes its slab
+// into a private LDS area and reads it back transposed (ds_read_b64_tr_b16). At the
+// end the four waves' sums meet in LDS in wave order; with S > 1 the range sums go to
+// an fp32 partial buffer and a second kernel adds the S partials in range order. The
+// result is independent of timing.
 #include "common.h"
 #include "gemm.h"
 
@@ -14,103 +23,116 @@ namespace ft {
 
 namespace {
 
+constexpr int LG_WAVES = 4;
+constexpr int LG_Q = 64;       // big columns per tile
+constexpr int LG_SLAB = 32;    // rows per wave slab
+constexpr int BIG_PITCH = LG_Q * 2 + 16;
 
-// ------------------------------------------------------------------ prep (transposes)
-constexpr int TT = 64;  // transpose tile
+template <bool BIG_BF16, int PT>
+struct Slab {
+  static constexpr int RP = 32 * PT;
+  static constexpr int NB = BIG_BF16 ? 4 : 8;  // 16-byte big loads per lane
+  static constexpr int NS = RP / 16;           // 16-byte small loads per lane
+  v4i big[NB];
+  v4i small[NS];
 
-// U [N x rt], U(n, j) = j < r ? B[n, j] : L2[n, j - r]  ->  Ut [rt x N]
-__global__ __launch_bounds__(256) void k_prep_bwd(const PrepArgs a) {
-  __shared__ bf16_t tile[TT][TT + 2];
-  const int rt = a.r + a.s;
-  const int64_t ntc = (rt + TT - 1) / TT;
-  const int64_t tiles = ((a.N + TT - 1) / TT) * ntc;
-  const int64_t b = blockIdx.x;
-  if (b == 0)
-    for (int i = threadIdx.x; i < a.ncounters; i += 256) a.counters[i] = 0u;
-  if (b >= tiles) return;
-  const int64_t r0 = (b / ntc) * TT, c0 = (b % ntc) * TT;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < TT; i += 4) {
-    const int64_t n = r0 + i, j = c0 + tx;
-    bf16_t v = 0;
-    if (n < a.N && j < rt) v = j < a.r ? a.B[n * a.r + j] : a.L2[n * a.s + (j - a.r)];
-    tile[i][tx] = v;
+  // big: unit e = i*64 + lane -> row e/8, 8 columns at 8*(e%8)
+  // small: unit e = i*64 + lane -> row e/(RP/8), 8 columns at 8*(e%(RP/8))
+  __device__ void load(bufres rb, bufres rs, int64_t m0, int64_t q0, int64_t nbig, int64_t ld_big,
+                       int64_t ld_small, int r, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = i * 64 + lane, row = e >> 3;
+      const int64_t q = q0 + 8 * (e & 7);
+      const int64_t m = m0 + row;
+      const bool ok = q < nbig;
+      if constexpr (BIG_BF16) {
+        big[i] = buf_load16(rb, sel_off(ok, (uint32_t)((m * ld_big + q) * 2)));
+      } else {
+        const uint32_t off = sel_off(ok, (uint32_t)((m * ld_big + q) * 4));
+        big[2 * i] = buf_load16(rb, off);
+        big[2 * i + 1] = buf_load16(rb, off + 16);  // OOB + 16 is still OOB
+      }
+    }
+    constexpr int UPR = RP / 8;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int e = i * 64 + lane, row = e / UPR, p = 8 * (e % UPR);
+      const int64_t m = m0 + row;
+      small[i] = buf_load16(rs, sel_off(p < r, (uint32_t)((m * ld_small + p) * 2)));
+    }
   }
-  __syncthreads();
-  for (int i = ty; i < TT; i += 4) {
-    const int64_t j = c0 + i, n = r0 + tx;
-    if (j < rt && n < a.N) a.Ut[j * a.N + n] = tile[tx][i];
+
+  __device__ void stage(lds_char* sbig, lds_char* ssmall, int small_pitch, int lane) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = i * 64 + lane;
+      v4i v;
+      if constexpr (BIG_BF16) {
+        v = big[i];
+      } else {
+        const v4f a = __builtin_bit_cast(v4f, big[2 * i]), b = __builtin_bit_cast(v4f, big[2 * i + 1]);
+        v = v4i{(int)pack_bf16x2(a.x, a.y), (int)pack_bf16x2(a.z, a.w), (int)pack_bf16x2(b.x, b.y),
+                (int)pack_bf16x2(b.z, b.w)};
+      }
+      *(__attribute__((address_space(3))) v4i*)(sbig + (e >> 3) * BIG_PITCH + (e & 7) * 16) = v;
+    }
+    constexpr int UPR = RP / 8;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int e = i * 64 + lane;
+      *(__attribute__((address_space(3))) v4i*)(ssmall + (e / UPR) * small_pitch + (e % UPR) * 16) = small[i];
+    }
   }
-}
+};
 
-// ------------------------------------------------------------------ LoRA gradients
-// Output tile: RP (= r rounded up to 32) small rows x 256 big columns, one workgroup
-// per (tile, M-split). 4 waves, each 64 big columns (2 MFMA column tiles).
-constexpr int LG_BT = 256, LG_MS = 64;  // big-tile width, rows per LDS slab
-constexpr int BIG_PITCH = LG_BT * 2 + 32;
-
-// 8 consecutive elements of a bf16 or fp32 row as 8 bf16 (RNE for fp32).
-__device__ __forceinline__ uint4 load8_bf16(const void* base, bool is_bf16, int64_t off, bool ok) {
-  if (!ok) return make_uint4(0, 0, 0, 0);
-  if (is_bf16) return *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(base) + off);
-  const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-  const float4 a = p[0], b = p[1];
-  return make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y),
-                    pack_bf16x2(b.z, b.w));
-}
-
-template <int PT>  // small-side 32-row tiles (RP = 32 * PT)
+template <bool BIG_BF16, int PT>
 __global__ __launch_bounds__(256) void k_lora_grad(const LoraGradArgs a) {
   constexpr int RP = 32 * PT;
-  constexpr int SMALL_PITCH = RP * 2 + 32;
-  __shared__ __align__(16) char s_big[LG_MS * BIG_PITCH];
-  __shared__ __align__(16) char s_small[LG_MS * SMALL_PITCH];
-  __shared__ uint32_t s_last;
-  lds_char* big = (lds_char*)(s_big);
-  lds_char* small = (lds_char*)(s_small);
+  constexpr int SMALL_PITCH = RP * 2 + 16;
+  constexpr int STAGE = LG_SLAB * BIG_PITCH + LG_SLAB * SMALL_PITCH;  // per wave
+  constexpr int RED = LG_WAVES * RP * LG_Q * 4;
+  constexpr int SMEM = LG_WAVES * STAGE > RED ? LG_WAVES * STAGE : RED;
+  __shared__ __align__(16) char smem_raw[SMEM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tilesA = (int)((a.K + LG_BT - 1) / LG_BT);
-  const int tile = blockIdx.x / a.splits, split = blockIdx.x % a.splits;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = gridDim.y, split = blockIdx.y;
+  const int tilesA = (int)((a.K + LG_Q - 1) / LG_Q);
+  const int tile = blockIdx.x + a.tile_offset;
   const bool jobA = tile < tilesA;
-  // dA: small = GB (first r cols), big = X. dB^T: small = XL (first r cols), big = G.
   const bf16_t* sm = jobA ? a.gb : a.xl;
   const int64_t ld_sm = jobA ? a.ld_gb : a.ld_xl;
   const void* bg = jobA ? a.x : a.g;
-  const bool bg_bf16 = jobA ? a.x_bf16 : a.g_bf16;
   const int64_t nbig = jobA ? a.K : a.N;
-  const int64_t q0 = (int64_t)(jobA ? tile : tile - tilesA) * LG_BT;
-  const int64_t per = ((a.M + a.splits - 1) / a.splits + LG_MS - 1) / LG_MS * LG_MS;
+  const int64_t q0 = (int64_t)(jobA ? tile : tile - tilesA) * LG_Q;
+  const int64_t per = ((a.M + S - 1) / S + LG_SLAB - 1) / LG_SLAB * LG_SLAB;
   const int64_t mb = split * per, me = min(a.M, mb + per);
+
+  const bufres rb = make_buf(bg, (uint64_t)a.M * nbig * (BIG_BF16 ? 2 : 4));
+  const bufres rs = make_buf(sm, (uint64_t)a.M * ld_sm * 2);
+  lds_char* sbig = (lds_char*)smem_raw + wave * STAGE;
+  lds_char* ssmall = sbig + LG_SLAB * BIG_PITCH;
 
   v16f acc[PT][2];
 #pragma unroll
   for (int p = 0; p < PT; ++p) acc[p][0] = acc[p][1] = v16f{};
 
-  for (int64_t m0 = mb; m0 < me; m0 += LG_MS) {
-    // stage big slab [64 x 256] and small slab [64 x RP] as bf16
+  // Two register sets in turn: one slab's loads are in flight while the other is
+  // staged and multiplied. A slab past the range loads nothing (its row start is M,
+  // beyond the buffers).
+  auto load = [&](Slab<BIG_BF16, PT>& sl, int64_t m0) {
+    sl.load(rb, rs, m0 < me ? m0 : a.M, q0, nbig, nbig, ld_sm, a.r, lane);
+  };
+  auto work = [&](const Slab<BIG_BF16, PT>& sl) {
+    sl.stage(sbig, ssmall, SMALL_PITCH, lane);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + 256 * i, row = c >> 5, c8 = c & 31;
-      const int64_t gm = m0 + row, gq = q0 + 8 * c8;
-      const uint4 v = load8_bf16(bg, bg_bf16, gm * nbig + gq, gm < me && gq < nbig);
-      *(__attribute__((address_space(3))) v4i*)(big + row * BIG_PITCH + c8 * 16) = __builtin_bit_cast(v4i, v);
-    }
-    for (int c = tid; c < LG_MS * (RP / 8); c += 256) {
-      const int row = c / (RP / 8), c8 = c % (RP / 8);
-      const int64_t gm = m0 + row;
-      const bool ok = gm < me && 8 * c8 < a.r;
-      const uint4 v = ok ? *reinterpret_cast<const uint4*>(sm + gm * ld_sm + 8 * c8) : make_uint4(0, 0, 0, 0);
-      *(__attribute__((address_space(3))) v4i*)(small + row * SMALL_PITCH + c8 * 16) = __builtin_bit_cast(v4i, v);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ms = 0; ms < LG_MS; ms += 16) {
+    for (int ms = 0; ms < LG_SLAB; ms += 16) {
       v4i sa[PT], bb[2];
 #pragma unroll
-      for (int p = 0; p < PT; ++p) sa[p] = lds_tr16_pair(small, SMALL_PITCH, ms, 32 * p, lane);
+      for (int p = 0; p < PT; ++p) sa[p] = lds_tr16_pair(ssmall, SMALL_PITCH, ms, 32 * p, lane);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) bb[q] = lds_tr16_pair(big, BIG_PITCH, ms, wave * 64 + 32 * q, lane);
+      for (int q = 0; q < 2; ++q) bb[q] = lds_tr16_pair(sbig, BIG_PITCH, ms, 32 * q, lane);
 #pragma unroll
       for (int p = 0; p < PT; ++p)
 #pragma unroll
@@ -118,28 +140,31 @@ __global__ __launch_bounds__(256) void k_lora_grad(const LoraGradArgs a) {
           acc[p][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sa[p]),
                                                              __builtin_bit_cast(bf16x8, bb[q]), acc[p][q], 0, 0, 0);
     }
-    __syncthreads();
-  }
-
-  // ---- partials [splits][RP][K + N]: dA tiles at column q, dB^T tiles at column K + q
-  const int64_t ptot = a.K + a.N;
-  const int64_t pcol0 = (jobA ? 0 : a.K) + q0;
-  auto out_final = [&](int p, int64_t q, float v) {
-    if (p >= a.r || q >= nbig) return;
-    if (jobA) a.dA[(int64_t)p * a.K + q] = v;
-    else a.dB[q * a.r + p] = v;
   };
-  if (a.splits == 1) {
-#pragma unroll
-    for (int p = 0; p < PT; ++p)
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          out_final(32 * p + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), q0 + wave * 64 + 32 * q + (lane & 31), acc[p][q][r]);
-    return;
+  // Two slabs per trip, each in its own register set; the second may lie past the
+  // range (it then loads zeros), which keeps the trip branch-free. Scheduling barriers
+  // keep each half's arithmetic after the loads of the other half are issued.
+  constexpr int STEP = LG_WAVES * LG_SLAB;
+  Slab<BIG_BF16, PT> s0, s1;
+  int64_t m0 = mb + (int64_t)wave * LG_SLAB;
+  load(s0, m0);
+  for (; m0 < me; m0 += 2 * STEP) {
+    load(s1, m0 + STEP);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    work(s0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(s0, m0 + 2 * STEP);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    work(s1);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  float* part = a.partials + (int64_t)split * RP * ptot;
+  // Rows past M were read as zero (buffer bounds), so the ragged last slab needs no mask.
+
+  // ---- wave sums into LDS, [wave][p][q] fp32
+  __syncthreads();
+  float* red = (float*)smem_raw;
 #pragma unroll
   for (int p = 0; p < PT; ++p)
 #pragma unroll
@@ -147,62 +172,140 @@ __global__ __launch_bounds__(256) void k_lora_grad(const LoraGradArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int pr = 32 * p + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t qc = wave * 64 + 32 * q + (lane & 31);
-        if (q0 + qc < nbig) part[(int64_t)pr * ptot + pcol0 + qc] = acc[p][q][r];
+        red[(wave * RP + pr) * LG_Q + 32 * q + (lane & 31)] = acc[p][q][r];
       }
-  __threadfence();
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[tile], 1u) == (uint32_t)(a.splits - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // last split of this tile: fixed-order sum over splits
-  const int width = (int)min((int64_t)LG_BT, nbig - q0);
-  for (int e = tid; e < a.r * LG_BT; e += 256) {
-    const int p = e / LG_BT, qc = e % LG_BT;
-    if (qc >= width) continue;
-    float s = 0.f;
-    for (int sp = 0; sp < a.splits; ++sp)
-      s += __builtin_nontemporal_load(a.partials + (int64_t)sp * RP * ptot + (int64_t)p * ptot + pcol0 + qc);
-    out_final(p, q0 + qc, s);
+
+  // Tile element order matches the output's: dA rows p with q contiguous (index p*64+q),
+  // dB rows q with p contiguous (index q*RP+p). Thread t handles 4 consecutive indices.
+  const int width = (int)min((int64_t)LG_Q, nbig - q0);
+  auto elem = [&](int idx, int& p, int& q) {
+    if (jobA) { p = idx / LG_Q; q = idx % LG_Q; }
+    else { q = idx / RP; p = idx % RP; }
+  };
+  auto store_final = [&](int idx, v4f v) {
+    int p, q;
+    elem(idx, p, q);
+    if (p >= a.r || q >= width) return;
+    if (jobA) {
+      *reinterpret_cast<v4f*>(a.dA + (int64_t)p * a.K + q0 + q) = v;
+    } else {
+      *reinterpret_cast<v4f*>(a.dB + (q0 + q) * a.r + p) = v;
+    }
+  };
+  constexpr int NE = RP * LG_Q;
+  v4f sums[NE / 1024 > 0 ? NE / 1024 : 1];
+#pragma unroll
+  for (int i = 0; i < NE / 1024; ++i) {
+    const int idx = 4 * (tid + 256 * i);
+    int p, q;
+    elem(idx, p, q);
+    v4f s = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < LG_WAVES; ++w) {
+      if (jobA) {
+        s += *reinterpret_cast<const v4f*>(red + (w * RP + p) * LG_Q + q);
+      } else {
+        s.x += red[(w * RP + p + 0) * LG_Q + q];
+        s.y += red[(w * RP + p + 1) * LG_Q + q];
+        s.z += red[(w * RP + p + 2) * LG_Q + q];
+        s.w += red[(w * RP + p + 3) * LG_Q + q];
+      }
+    }
+    sums[i] = s;
   }
-  if (tid == 0) a.counters[tile] = 0u;
+  if (S == 1) {
+#pragma unroll
+    for (int i = 0; i < NE / 1024; ++i) store_final(4 * (tid + 256 * i), sums[i]);
+    return;
+  }
+  v4f* part = reinterpret_cast<v4f*>(a.partials);
+#pragma unroll
+  for (int i = 0; i < NE / 1024; ++i) part[((int64_t)split * a.ntiles + tile) * (NE / 4) + tid + 256 * i] = sums[i];
+}
+
+// Sum of the S row-range partials of every tile, in range order (same element order
+// as k_lora_grad's tiles), written to dA / dB.
+__global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs a, int S, int rp) {
+  const int ne4 = rp * LG_Q / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.ntiles * ne4) return;
+  const int tile = (int)(i / ne4), idx = 4 * (int)(i % ne4);
+  const int tilesA = (int)((a.K + LG_Q - 1) / LG_Q);
+  const bool jobA = tile < tilesA;
+  const int64_t q0 = (int64_t)(jobA ? tile : tile - tilesA) * LG_Q;
+  const int64_t nbig = jobA ? a.K : a.N;
+  int p, q;
+  if (jobA) { p = idx / LG_Q; q = idx % LG_Q; }
+  else { q = idx / rp; p = idx % rp; }
+  if (p >= a.r || q0 + q >= nbig) return;
+  const v4f* pv = reinterpret_cast<const v4f*>(a.partials);
+  const int64_t stride = (int64_t)a.ntiles * ne4;
+  v4f s = pv[i];
+  for (int sp = 1; sp < S; ++sp) s += pv[sp * stride + i];
+  if (jobA) *reinterpret_cast<v4f*>(a.dA + (int64_t)p * a.K + q0 + q) = s;
+  else *reinterpret_cast<v4f*>(a.dB + (q0 + q) * a.r + p) = s;
+}
+
+template <bool BIG_BF16>
+hipError_t launch_t(const LoraGradArgs& a, dim3 grid, hipStream_t stream) {
+  switch ((a.r + 31) / 32) {
+    case 1: hipLaunchKernelGGL((k_lora_grad<BIG_BF16, 1>), grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_lora_grad<BIG_BF16, 2>), grid, dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((k_lora_grad<BIG_BF16, 3>), grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_lora_grad<BIG_BF16, 4>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prep_bwd(const PrepArgs& a, hipStream_t stream) {
-  const int rt = a.r + a.s;
-  const int64_t tiles = ((a.N + TT - 1) / TT) * ((rt + TT - 1) / TT);
-  const int64_t blocks = tiles > 0 ? tiles : 1;
-  hipLaunchKernelGGL(k_prep_bwd, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
 int lora_grad_tiles(int64_t K, int64_t N) {
-  return (int)((K + LG_BT - 1) / LG_BT + (N + LG_BT - 1) / LG_BT);
+  return (int)((K + LG_Q - 1) / LG_Q + (N + LG_Q - 1) / LG_Q);
 }
 
 int lora_grad_splits(int64_t M, int64_t K, int64_t N) {
   const int tiles = lora_grad_tiles(K, N);
-  int64_t s = 512 / tiles;
-  s = s < 1 ? 1 : s;
-  const int64_t maxs = (M + 255) / 256;  // at least 256 rows per split
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t maxs = M / (2 * LG_WAVES * LG_SLAB);  // at least two slabs per wave
   if (s > maxs) s = maxs;
+  if (s > 64) s = 64;
   return (int)(s < 1 ? 1 : s);
+}
+
+size_t lora_grad_partial_bytes(int64_t M, int64_t K, int64_t N, int r) {
+  const int S = lora_grad_splits(M, K, N);
+  if (S <= 1 || r == 0) return 0;
+  const int64_t rp = (r + 31) / 32 * 32;
+  return (size_t)S * lora_grad_tiles(K, N) * rp * LG_Q * 4;
 }
 
 hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream) {
   if (a.r == 0 || a.M == 0) return hipSuccess;
-  const int tiles = lora_grad_tiles(a.K, a.N);
-  dim3 grid((unsigned)(tiles * a.splits)), block(256);
-  switch ((a.r + 31) / 32) {
-    case 1: hipLaunchKernelGGL(k_lora_grad<1>, grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(k_lora_grad<2>, grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(k_lora_grad<3>, grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(k_lora_grad<4>, grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+  const int S = lora_grad_splits(a.M, a.K, a.N);
+  if (S > 1 && a.partials == nullptr) return hipErrorInvalidValue;
+  const int tilesA = (int)((a.K + LG_Q - 1) / LG_Q), tiles = lora_grad_tiles(a.K, a.N);
+  LoraGradArgs b = a;
+  b.ntiles = tiles;
+  hipError_t e;
+  if (a.x_bf16 == a.g_bf16) {  // one launch for both jobs
+    b.tile_offset = 0;
+    e = a.x_bf16 ? launch_t<true>(b, dim3((unsigned)tiles, (unsigned)S), stream)
+                 : launch_t<false>(b, dim3((unsigned)tiles, (unsigned)S), stream);
+  } else {  // X and G differ in dtype: the dA tiles and the dB tiles are two launches
+    b.tile_offset = 0;
+    e = a.x_bf16 ? launch_t<true>(b, dim3((unsigned)tilesA, (unsigned)S), stream)
+                 : launch_t<false>(b, dim3((unsigned)tilesA, (unsigned)S), stream);
+    if (e != hipSuccess) return e;
+    b.tile_offset = tilesA;
+    e = a.g_bf16 ? launch_t<true>(b, dim3((unsigned)(tiles - tilesA), (unsigned)S), stream)
+                 : launch_t<false>(b, dim3((unsigned)(tiles - tilesA), (unsigned)S), stream);
   }
+  if (e != hipSuccess || S == 1) return e;
+  const int rp = (a.r + 31) / 32 * 32;
+  const int64_t items = (int64_t)tiles * rp * LG_Q / 4;
+  hipLaunchKernelGGL(k_lora_reduce, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, b, S, rp);
   return hipGetLastError();
 }
 

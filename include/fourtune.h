@@ -71,7 +71,10 @@ typedef struct {
 
 /* One W4A4G4 linear: Y = Q(X) Q(R)^T + X^ L1^T L2^T + X^ A^T B^T (FourTune §3.1).
  * n = out features, k = in features (multiples of 32). rank = r (LoRA), stab_rank = s;
- * each a multiple of 16, r + s a multiple of 32; either may be 0 (branch absent). */
+ * each a multiple of 16, r + s a multiple of 32; either may be 0 (branch absent).
+ * Limits of this build (FT_ERR_UNSUPPORTED beyond them): n, k <= 16384;
+ * r + s <= 128 and ceil(r/32) + ceil(s/32) <= 4; (m + 64) * max(n, k) * 4 bytes
+ * below 4 GiB (32-bit buffer addressing). */
 typedef struct {
   ft_mx4 r;               /* Q(R), rows = n, cols = k (frozen; from fourtune_quantize) */
   const void *lora_a;     /* A  [rank x k]      bf16, trainable down-projection     */
@@ -96,7 +99,10 @@ size_t ft_mx4_scales_bytes(int64_t rows, int64_t cols);
 ft_status fourtune_quantize(const void *x, ft_dtype x_dt, int64_t rows, int64_t cols,
                             int64_t ld, ft_mx4 *out, void *stream);
 
-/* Workspace bytes needed by fourtune_linear_fwd and fourtune_linear_bwd for m rows. */
+/* Workspace bytes needed by fourtune_linear_fwd and fourtune_linear_bwd for m rows.
+ * The workspace is device scratch owned by the caller (16-byte aligned, contents
+ * irrelevant, overwritten by every call; nothing in it outlives a call). Two calls
+ * that overlap in time (different streams) must not share one. */
 size_t fourtune_linear_workspace_bytes(int64_t m, const ft_linear *L);
 
 /* fourtune_linear_fwd -- forward of one W4A4G4 linear (FourTune §3.1, §3.3 "LoRA
