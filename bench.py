@@ -1,20 +1,26 @@
 """Benchmark of the W4A4G4 quantized linear (FourTune) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload c2|c3|...] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+    python bench.py --calibrate-copy     (a plain 512 MiB device copy, for counter scaling)
 
 One step = the whole hot path once over one batch: the layer's forward (fused
-quantize + down-projection, 4-bit GEMM + up-projection) and backward (fused
-quantize + down-projection of dY, transposed 4-bit GEMM + up-projection, LoRA
-gradients). Inputs are seeded synthetic tensors of the named workload, resident in
-HBM before timing; several independent input/weight sets are rotated so that the
-256 MB Infinity Cache cannot hold a step's operands from one step to the next.
+quantize + down-projection, 4-bit GEMM + up-projection) and backward (fused quantize +
+down-projection of dY, transposed 4-bit GEMM + up-projection, LoRA gradients), every
+kernel of `fourtune_linear_fwd` and `fourtune_linear_bwd`. Inputs are seeded synthetic
+tensors of the named workload, resident in HBM before timing; several independent
+input/weight sets are rotated so that the 256 MB Infinity Cache cannot carry a step's
+operands over from the step before.
 
-Prints one JSON line. `value` is backbone TFLOP/s of the whole step, 4*M*N*K per
-linear (the 4-bit GEMM flops of forward and backward) divided by the step time.
+Prints one JSON line. `value` is 4*M*N*K (the 4-bit GEMM flops of forward and
+backward) divided by the whole step's time. `roofline` is the dominant kernel (the
+forward 4-bit GEMM) against the dense MXFP4 peak, its duration taken with HIP events
+on the stream it is launched on; `traffic` comes from the rocprofv3 counter summary
+in profiles/ when that summary was taken on the current kernel source, else null.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +33,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_MXFP4_TFLOPS = 10100.0   # MI355X dense MXFP4 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fwd_c2_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "bit_quantized_lora_fp4_amd", "csrc", "gemm.hip")
 
 
 def parse():
@@ -38,11 +46,17 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="rotated input/weight sets")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true")
     return ap.parse_args()
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 # --------------------------------------------------------------------------- GPU side
@@ -77,6 +91,7 @@ def step(abi, s):
 
 
 def time_region(torch, fn, iters):
+    """Seconds for `iters` calls, bracketed by a synchronize on both sides."""
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -84,11 +99,12 @@ def time_region(torch, fn, iters):
         fn(i)
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1000.0  # seconds
+    return start.elapsed_time(end) / 1000.0
 
 
 def time_each(torch, fn, iters):
-    """Average duration of fn(i) bracketed by events on the current stream."""
+    """Mean duration of fn(i), each bracketed by events on the current stream (the one
+    the library launches on)."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(iters)]
     torch.cuda.synchronize()
@@ -98,6 +114,30 @@ def time_each(torch, fn, iters):
         evs[i][1].record()
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1000.0
+
+
+def traffic_for(m, n, k):
+    """Counter-measured HBM bytes per forward-GEMM launch, if taken on this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_src_sha256_16") != source_hash(GEMM_SRC) or t.get("shape") != [m, n, k]:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    nbytes = 512 << 20
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes_read": nbytes, "bytes_written": nbytes, "launches": 5}))
+    return 0
 
 
 # --------------------------------------------------------------------------- CPU side
@@ -121,20 +161,28 @@ def cpu_baseline(case, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    threads = None
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or None
+    except Exception:  # noqa: BLE001 - report what is known
+        pass
     flops = 4.0 * rows * n * k * reps
-    return dict(value=flops / el / 1e12, unit="TFLOP/s", cores=len(os.sched_getaffinity(0)),
-                kind="oracle",
+    return dict(value=round(flops / el / 1e12, 5), unit="TFLOP/s",
+                cores=threads or len(os.sched_getaffinity(0)), kind="oracle",
                 sample=f"fwd+bwd of the same linear on the first {rows} of {case['X'].shape[0]} "
-                       f"token rows, {reps} repetitions in {el:.1f} s (numpy fp64, BLAS threads = cores)")
+                       f"token rows, {reps} repetitions in {el:.1f} s (numpy fp64)")
 
 
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the hot path runs on a single MI355X; sharding is a design note only).",
+              "(the hot path runs on a single MI355X; how it would shard is a design note).",
               file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        return calibrate_copy()
     import torch
     from bit_quantized_lora_fp4_amd import abi
     from synth import workloads as wl
@@ -164,32 +212,29 @@ def main():
     # ---- timed region: K whole steps
     t = time_region(torch, lambda i: step(abi, sets[i % len(sets)]), args.steps)
     ms_per_step = 1000.0 * t / args.steps
-    flops_step = 4.0 * m * n * k
-    value = flops_step / (t / args.steps) / 1e12
+    value = 4.0 * m * n * k / (t / args.steps) / 1e12
     log(f"[bench] step {ms_per_step:.4f} ms -> {value:.1f} TFLOP/s")
 
-    # ---- per-kernel: the two 4-bit GEMMs alone, and the standalone quantizer
+    # ---- per-kernel: the two 4-bit GEMMs alone, the layer halves, the quantizer
     def S(i):
         return sets[i % len(sets)]
 
-    t_gf = time_each(torch, lambda i: abi.fourtune_gemm_fwd(S(i)["L"], S(i)["xq"], S(i)["xl"], S(i)["y"]),
-                     args.steps)
-    t_gb = time_each(torch, lambda i: abi.fourtune_gemm_bwd(S(i)["L"], S(i)["gq"], S(i)["gb"], S(i)["dx"]),
-                     args.steps)
+    it = max(args.steps, 10)
+    t_gf = time_each(torch, lambda i: abi.fourtune_gemm_fwd(S(i)["L"], S(i)["xq"], S(i)["xl"], S(i)["y"]), it)
+    t_gb = time_each(torch, lambda i: abi.fourtune_gemm_bwd(S(i)["L"], S(i)["gq"], S(i)["gb"], S(i)["dx"]), it)
     t_fwd = time_each(torch, lambda i: abi.fourtune_linear_fwd(S(i)["L"], S(i)["x"], S(i)["y"], S(i)["xl"],
-                                                              S(i)["ws"]), args.steps)
+                                                              S(i)["ws"]), it)
     t_bwd = time_each(torch, lambda i: abi.fourtune_linear_bwd(S(i)["L"], S(i)["dy"], S(i)["x"], S(i)["xl"],
-                                                              S(i)["dx"], S(i)["da"], S(i)["db"], S(i)["ws"]),
-                      args.steps)
-    t_q = time_each(torch, lambda i: abi.fourtune_quantize(S(i)["x"], S(i)["xq"]), args.steps)
+                                                              S(i)["dx"], S(i)["da"], S(i)["db"], S(i)["ws"]), it)
+    t_q = time_each(torch, lambda i: abi.fourtune_quantize(S(i)["x"], S(i)["xq"]), it)
     gemm_flops = 2.0 * m * n * k
     tf_gf, tf_gb = gemm_flops / t_gf / 1e12, gemm_flops / t_gb / 1e12
-    xbytes = case["X"].dtype.itemsize if case["x_dtype"] == "fp32" else 2
+    xbytes = 4 if case["x_dtype"] == "fp32" else 2
     q_bytes = m * k * xbytes + m * k / 2 + ((m + 31) // 32) * (k // 32)
     q_gbps = q_bytes / t_q / 1e9
-    dominant = ("gemm_fwd", t_gf, tf_gf) if t_gf >= t_gb else ("gemm_bwd", t_gb, tf_gb)
     log(f"[bench] gemm_fwd {t_gf*1e6:.1f} us ({tf_gf:.0f} TF/s), gemm_bwd {t_gb*1e6:.1f} us "
-        f"({tf_gb:.0f} TF/s), linear_fwd {t_fwd*1e6:.1f} us, linear_bwd {t_bwd*1e6:.1f} us, quantize X {t_q*1e6:.1f} us ({q_gbps:.0f} GB/s)")
+        f"({tf_gb:.0f} TF/s), linear_fwd {t_fwd*1e6:.1f} us, linear_bwd {t_bwd*1e6:.1f} us, "
+        f"quantize X {t_q*1e6:.1f} us ({q_gbps:.0f} GB/s)")
 
     out = {
         "metric": "W4A4G4 linear fwd+bwd TFLOPS (4-bit backbone flops / whole step time)",
@@ -207,15 +252,16 @@ def main():
         "config": {"workload": f"{args.workload}: {spec.title}, W4A4G4 linear fwd+bwd",
                    "m": m, "k": k, "n": n, "lora_rank": r, "stab_rank": s,
                    "x_dtype": case["x_dtype"], "out_dtype": "bf16", "input_sets": args.sets},
-        "frac_of_mxfp4_peak": round(value / PEAK_MXFP4_TFLOPS, 4),
-        "roofline": {"kernel": dominant[0], "bound": "mfma", "achieved": round(dominant[2], 1),
-                     "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dominant[2] / PEAK_MXFP4_TFLOPS, 4), "traffic": None},
+        "roofline": {"kernel": "k_gemm_mx4 forward (4-bit GEMM + up-projection)", "bound": "mfma",
+                     "achieved": round(tf_gf, 1), "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf_gf / PEAK_MXFP4_TFLOPS, 4),
+                     "traffic": traffic_for(m, n, k)},
         "kernels_us": {"gemm_fwd": round(t_gf * 1e6, 2), "gemm_bwd": round(t_gb * 1e6, 2),
-                       "linear_fwd": round(t_fwd * 1e6, 2),
-                       "linear_bwd": round(t_bwd * 1e6, 2), "quantize_x": round(t_q * 1e6, 2)},
+                       "linear_fwd": round(t_fwd * 1e6, 2), "linear_bwd": round(t_bwd * 1e6, 2),
+                       "quantize_x": round(t_q * 1e6, 2)},
         "gemm_tflops": {"fwd": round(tf_gf, 1), "bwd": round(tf_gb, 1),
-                        "fwd_bwd": round(2 * gemm_flops / (t_gf + t_gb) / 1e12, 1)},
+                        "fwd_bwd": round(2 * gemm_flops / (t_gf + t_gb) / 1e12, 1),
+                        "frac_of_mxfp4_peak": round(2 * gemm_flops / (t_gf + t_gb) / 1e12 / PEAK_MXFP4_TFLOPS, 4)},
         "quantize_gbps": round(q_gbps, 1),
         "quantize_frac_of_hbm": round(q_gbps / PEAK_HBM_GBPS, 4),
     }
