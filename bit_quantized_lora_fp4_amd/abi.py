@@ -66,11 +66,11 @@ _SIGS = {
                                             ctypes.POINTER(FtLinear)]),
     "fourtune_mlp_fwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear), c_vp,
                                         ctypes.c_int, c_i64, c_vp, ctypes.c_int, c_vp, c_vp, c_vp,
-                                        c_vp, c_vp, c_sz, c_vp]),
+                                        ctypes.POINTER(FtMx4), c_vp, c_sz, c_vp]),
     "fourtune_mlp_bwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear), c_vp,
                                         ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_i64,
-                                        c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                        c_sz, c_vp]),
+                                        c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_vp,
+                                        ctypes.POINTER(FtMx4), c_vp, c_sz, c_vp]),
     "fourtune_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fourtune_last_error": (ctypes.c_char_p, []),
 }
@@ -240,24 +240,26 @@ def fourtune_mlp_workspace_bytes(m: int, fc1: Linear, fc2: Linear) -> int:
 
 def fourtune_mlp_fwd(fc1: Linear, fc2: Linear, x: torch.Tensor, y: torch.Tensor,
                      xl1_saved: torch.Tensor, pre_saved: torch.Tensor, hl2_saved: torch.Tensor,
-                     ws: torch.Tensor, h_debug: Optional[torch.Tensor] = None, stream=None):
+                     ws: torch.Tensor, hq_out: Optional[Mx4] = None, stream=None):
     s1, s2 = fc1.struct(), fc2.struct()
+    hq = hq_out.struct() if hq_out is not None else None
     _check(lib().fourtune_mlp_fwd(ctypes.byref(s1), ctypes.byref(s2), _ptr(x), _dt(x),
                                   x.shape[0], _ptr(y), _dt(y), _ptr(xl1_saved), _ptr(pre_saved),
-                                  _ptr(hl2_saved), _ptr(h_debug), _ptr(ws),
-                                  ws.numel() if ws is not None else 0, _stream(stream)))
+                                  _ptr(hl2_saved), ctypes.byref(hq) if hq is not None else None,
+                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def fourtune_mlp_bwd(fc1: Linear, fc2: Linear, dy: torch.Tensor, x: torch.Tensor,
                      xl1_saved: torch.Tensor, pre_saved: torch.Tensor, hl2_saved: torch.Tensor,
                      dx: torch.Tensor, d_a1, d_b1, d_a2, d_b2, ws: torch.Tensor,
-                     dp_debug: Optional[torch.Tensor] = None, stream=None):
+                     dpq_out: Optional[Mx4] = None, stream=None):
     s1, s2 = fc1.struct(), fc2.struct()
+    dq = dpq_out.struct() if dpq_out is not None else None
     _check(lib().fourtune_mlp_bwd(ctypes.byref(s1), ctypes.byref(s2), _ptr(dy), _dt(dy), _ptr(x),
                                   _dt(x), _ptr(xl1_saved), _ptr(pre_saved), _ptr(hl2_saved),
                                   x.shape[0], _ptr(dx), _dt(dx), _ptr(d_a1), _ptr(d_b1),
-                                  _ptr(d_a2), _ptr(d_b2), _ptr(dp_debug), _ptr(ws),
-                                  ws.numel() if ws is not None else 0, _stream(stream)))
+                                  _ptr(d_a2), _ptr(d_b2), ctypes.byref(dq) if dq is not None else None,
+                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
 
 
 def fourtune_status_string(status: int) -> str:
@@ -304,3 +306,33 @@ def linear_backward(L: Linear, dy: torch.Tensor, x: torch.Tensor, xl: torch.Tens
     ws = workspace(fourtune_linear_workspace_bytes(m, L), x.device) if ws is None else ws
     fourtune_linear_bwd(L, dy, x, xl, dx, da, db, ws, gq_out=gq_out, stream=stream)
     return dx, da, db
+
+
+def mlp_forward(fc1: Linear, fc2: Linear, x: torch.Tensor, y_dtype=torch.bfloat16, ws=None,
+                hq_out=None, stream=None):
+    """Allocating helper: returns (y, saved) with saved = dict(xl1, pre, hl2)."""
+    m, dev = x.shape[0], x.device
+    y = torch.empty((m, fc2.n), dtype=y_dtype, device=dev)
+    saved = dict(xl1=torch.empty((m, fc1.rank + fc1.stab_rank), dtype=torch.bfloat16, device=dev),
+                 pre=torch.empty((m, fc1.n), dtype=torch.bfloat16, device=dev),
+                 hl2=torch.empty((m, fc2.rank + fc2.stab_rank), dtype=torch.bfloat16, device=dev))
+    ws = workspace(fourtune_mlp_workspace_bytes(m, fc1, fc2), dev) if ws is None else ws
+    fourtune_mlp_fwd(fc1, fc2, x, y, saved["xl1"], saved["pre"], saved["hl2"], ws, hq_out=hq_out,
+                     stream=stream)
+    return y, saved
+
+
+def mlp_backward(fc1: Linear, fc2: Linear, dy: torch.Tensor, x: torch.Tensor, saved: dict,
+                 dx_dtype=torch.bfloat16, ws=None, dpq_out=None, stream=None):
+    """Allocating helper: returns dict(dX, dA1, dB1, dA2, dB2)."""
+    m, dev = x.shape[0], x.device
+    dx = torch.empty((m, fc1.k), dtype=dx_dtype, device=dev)
+    g = dict(dA1=torch.empty((fc1.rank, fc1.k), dtype=torch.float32, device=dev),
+             dB1=torch.empty((fc1.n, fc1.rank), dtype=torch.float32, device=dev),
+             dA2=torch.empty((fc2.rank, fc2.k), dtype=torch.float32, device=dev),
+             dB2=torch.empty((fc2.n, fc2.rank), dtype=torch.float32, device=dev))
+    ws = workspace(fourtune_mlp_workspace_bytes(m, fc1, fc2), dev) if ws is None else ws
+    fourtune_mlp_bwd(fc1, fc2, dy, x, saved["xl1"], saved["pre"], saved["hl2"], dx, g["dA1"], g["dB1"],
+                     g["dA2"], g["dB2"], ws, dpq_out=dpq_out, stream=stream)
+    g["dX"] = dx
+    return g

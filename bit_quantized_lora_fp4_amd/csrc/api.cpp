@@ -3,6 +3,7 @@
 // mutable state besides the thread-local error text.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -217,8 +218,17 @@ ft_status check_m(int64_t m, const ft_linear* L, const char* who) {
   return FT_OK;
 }
 
+// Epilogue options of the 4-bit GEMMs (the MLP's FC1 forward and FC2 backward).
+struct Epi {
+  int kind = ft::GEMM_EPI_NONE;
+  const void* pre = nullptr;
+  uint8_t* q_codes = nullptr;
+  uint8_t* q_scales = nullptr;
+};
+
 ft_status run_gemm_fwd(const ft_linear* L, const uint8_t* xq_codes, const uint8_t* xq_scales,
-                       const void* xl, int64_t m, void* y, ft_dtype y_dt, hipStream_t st) {
+                       const void* xl, int64_t m, void* y, ft_dtype y_dt, hipStream_t st,
+                       const Epi& e = Epi()) {
   ft::GemmArgs g{};
   g.a_codes = xq_codes; g.a_scales = xq_scales;
   g.b_codes = L->r.codes; g.b_scales = L->r.scales; g.b_pitch = L->k / 2;
@@ -228,11 +238,13 @@ ft_status run_gemm_fwd(const ft_linear* L, const uint8_t* xq_codes, const uint8_
   g.up1 = static_cast<const ft::bf16_t*>(L->stab_up); g.up1_ld = L->stab_rank;
   g.up_split = (int)L->rank;
   g.out = y; g.ldo = L->n;
+  g.epi = e.kind; g.pre = static_cast<const ft::bf16_t*>(e.pre); g.q_codes = e.q_codes; g.q_scales = e.q_scales;
   return hip_check(ft::launch_gemm_mx4(g, false, y_dt == FT_BF16, st), "gemm_fwd");
 }
 
 ft_status run_gemm_bwd(const ft_linear* L, const uint8_t* gq_codes, const uint8_t* gq_scales,
-                       const void* gb, int64_t m, void* dx, ft_dtype dx_dt, hipStream_t st) {
+                       const void* gb, int64_t m, void* dx, ft_dtype dx_dt, hipStream_t st,
+                       const Epi& e = Epi()) {
   ft::GemmArgs g{};
   g.a_codes = gq_codes; g.a_scales = gq_scales;
   g.b_codes = L->r.codes; g.b_scales = L->r.scales; g.b_pitch = L->k / 2;
@@ -242,7 +254,48 @@ ft_status run_gemm_bwd(const ft_linear* L, const uint8_t* gq_codes, const uint8_
   g.up1 = static_cast<const ft::bf16_t*>(L->stab_down); g.up1_ld = L->k;
   g.up_split = (int)L->rank;
   g.out = dx; g.ldo = L->k;
+  g.epi = e.kind; g.pre = static_cast<const ft::bf16_t*>(e.pre); g.q_codes = e.q_codes; g.q_scales = e.q_scales;
   return hip_check(ft::launch_gemm_mx4(g, true, dx_dt == FT_BF16, st), "gemm_bwd");
+}
+
+// The fused quantize / down-projection kernel on the rows of x [m x cols] (row stride
+// cols). down = true reads the linear's [A; L1] rows (input side), false its
+// [B | L2] (output side).
+ft_status run_quant_down(int mode, const ft_linear* L, bool down, const void* x, bool x_bf16, int64_t m,
+                         int64_t cols, uint8_t* codes, uint8_t* scales, void* low, float* partials,
+                         hipStream_t st, const char* what) {
+  ft::QuantDownArgs qd{};
+  qd.mode = mode;
+  qd.x = x; qd.M = m; qd.K = cols; qd.ldx = cols;
+  qd.codes = codes; qd.scales = scales;
+  qd.d0 = static_cast<const ft::bf16_t*>(down ? L->lora_a : L->lora_b);
+  qd.d1 = static_cast<const ft::bf16_t*>(down ? L->stab_down : L->stab_up);
+  qd.r0 = (int)L->rank; qd.rt = (int)(L->rank + L->stab_rank); qd.u_cols = !down;
+  qd.low = static_cast<ft::bf16_t*>(low);
+  qd.partials = partials;
+  return hip_check(ft::launch_quant_down(qd, x_bf16, st), what);
+}
+
+size_t qd_partials(int64_t m, int64_t cols, const ft_linear* L) {
+  return ft::quant_down_partial_bytes(m, cols, (int)L->rank, (int)(L->rank + L->stab_rank));
+}
+
+size_t lg_partials(int64_t m, const ft_linear* L) {
+  return ft::lora_grad_partial_bytes(m, L->k, L->n, (int)L->rank);
+}
+
+// LoRA gradients of one linear: dA = GB_A^T bf16(x) (or bf16(GELU(x))), dB = bf16(g)^T XL_A.
+ft_status run_lora_grad(const ft_linear* L, int64_t m, const void* gb, const void* x, bool x_bf16, bool gelu_x,
+                        const void* xl, const void* g, bool g_bf16, float* dA, float* dB, float* partials,
+                        hipStream_t st, const char* what) {
+  if (L->rank == 0) return FT_OK;
+  const int64_t rt = L->rank + L->stab_rank;
+  ft::LoraGradArgs lg{};
+  lg.M = m; lg.r = (int)L->rank;
+  lg.gb = static_cast<const ft::bf16_t*>(gb); lg.ld_gb = rt; lg.x = x; lg.x_bf16 = x_bf16; lg.K = L->k; lg.dA = dA;
+  lg.xl = static_cast<const ft::bf16_t*>(xl); lg.ld_xl = rt; lg.g = g; lg.g_bf16 = g_bf16; lg.N = L->n; lg.dB = dB;
+  lg.partials = partials; lg.gelu_x = gelu_x;
+  return hip_check(ft::launch_lora_grad(lg, st), what);
 }
 
 }  // namespace
@@ -279,6 +332,7 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const void* x, ft_dtype x_dt, 
   uint8_t* xq_scales = xq_out ? xq_out->scales : lay.xq_scales;
 
   ft::QuantDownArgs qd{};
+  qd.mode = ft::QD_QUANT;
   qd.x = x; qd.M = m; qd.K = L->k; qd.ldx = L->k;
   qd.codes = xq_codes; qd.scales = xq_scales;
   qd.d0 = static_cast<const ft::bf16_t*>(L->lora_a);
@@ -320,6 +374,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
   uint8_t* gq_scales = gq_out ? gq_out->scales : lay.gq_scales;
 
   ft::QuantDownArgs qd{};
+  qd.mode = ft::QD_QUANT;
   qd.x = dy; qd.M = m; qd.K = L->n; qd.ldx = L->n;
   qd.codes = gq_codes; qd.scales = gq_scales;
   qd.d0 = static_cast<const ft::bf16_t*>(L->lora_b);
@@ -373,18 +428,165 @@ ft_status fourtune_gemm_bwd(const ft_linear* L, const ft_mx4* gq, const void* gb
   return ok();
 }
 
-size_t fourtune_mlp_workspace_bytes(int64_t, const ft_linear*, const ft_linear*) { return 0; }
+}  // extern "C"
 
-ft_status fourtune_mlp_fwd(const ft_linear*, const ft_linear*, const void*, ft_dtype, int64_t,
-                           void*, ft_dtype, void*, void*, void*, float*, void*, size_t, void*) {
-  return fail(FT_ERR_UNSUPPORTED, "mlp_fwd: not built yet");
+namespace {
+
+struct MlpFwdLayout {
+  uint8_t *xq_codes, *xq_scales, *hq_codes, *hq_scales;
+  float* partials;
+  size_t bytes;
+};
+
+MlpFwdLayout mlp_fwd_layout(void* ws, int64_t m, const ft_linear* fc1, const ft_linear* fc2, bool need_hq) {
+  Carver c(ws);
+  MlpFwdLayout f{};
+  const int64_t d = fc1->k, fdim = fc1->n;
+  f.xq_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, d));
+  f.xq_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, d));
+  if (need_hq) {
+    f.hq_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, fdim));
+    f.hq_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, fdim));
+  }
+  const size_t p1 = qd_partials(m, d, fc1), p2 = qd_partials(m, fdim, fc2);
+  f.partials = c.take<float>(p1 > p2 ? p1 : p2);
+  f.bytes = c.used;
+  return f;
 }
 
-ft_status fourtune_mlp_bwd(const ft_linear*, const ft_linear*, const void*, ft_dtype, const void*,
-                           ft_dtype, const void*, const void*, const void*, int64_t, void*,
-                           ft_dtype, float*, float*, float*, float*, float*, void*, size_t,
-                           void*) {
-  return fail(FT_ERR_UNSUPPORTED, "mlp_bwd: not built yet");
+struct MlpBwdLayout {
+  uint8_t *gq_codes, *gq_scales, *dpq_codes, *dpq_scales;
+  ft::bf16_t *gb2, *gb1, *dp;
+  float* partials;
+  size_t bytes;
+};
+
+MlpBwdLayout mlp_bwd_layout(void* ws, int64_t m, const ft_linear* fc1, const ft_linear* fc2, bool need_dpq) {
+  Carver c(ws);
+  MlpBwdLayout b{};
+  const int64_t fdim = fc1->n, dout = fc2->n;
+  b.gq_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, dout));
+  b.gq_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, dout));
+  b.gb2 = c.take<ft::bf16_t>((size_t)m * (fc2->rank + fc2->stab_rank) * 2);
+  b.dp = c.take<ft::bf16_t>((size_t)m * fdim * 2);
+  if (need_dpq) {
+    b.dpq_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, fdim));
+    b.dpq_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, fdim));
+  }
+  b.gb1 = c.take<ft::bf16_t>((size_t)m * (fc1->rank + fc1->stab_rank) * 2);
+  size_t p = qd_partials(m, dout, fc2);
+  p = std::max(p, qd_partials(m, fdim, fc1));
+  p = std::max(p, lg_partials(m, fc2));
+  p = std::max(p, lg_partials(m, fc1));
+  b.partials = c.take<float>(p);
+  b.bytes = c.used;
+  return b;
+}
+
+ft_status check_mlp(const ft_linear* fc1, const ft_linear* fc2, int64_t m, const char* who) {
+  TRY(check_linear(fc1, who));
+  TRY(check_linear(fc2, who));
+  REQUIRE(fc1->n == fc2->k, FT_ERR_SHAPE, "%s: fc1 has %lld outputs, fc2 %lld inputs", who,
+          (long long)fc1->n, (long long)fc2->k);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m > 0) {
+    TRY(check_m(m, fc1, who));
+    TRY(check_m(m, fc2, who));
+  }
+  return FT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fourtune_mlp_workspace_bytes(int64_t m, const ft_linear* fc1, const ft_linear* fc2) {
+  if (fc1 == nullptr || fc2 == nullptr || m < 0) return 0;
+  const size_t f = mlp_fwd_layout(nullptr, m, fc1, fc2, true).bytes;
+  const size_t b = mlp_bwd_layout(nullptr, m, fc1, fc2, true).bytes;
+  return f > b ? f : b;
+}
+
+ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const void* x, ft_dtype x_dt, int64_t m,
+                           void* y, ft_dtype y_dt, void* xl1_saved, void* pre_saved, void* hl2_saved,
+                           ft_mx4* hq_out, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "mlp_fwd";
+  TRY(check_mlp(fc1, fc2, m, who));
+  REQUIRE(dtype_ok(x_dt) && dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  if (m == 0) return ok();
+  TRY(check_tensor(x, who, "x"));
+  TRY(check_tensor(y, who, "y"));
+  TRY(check_tensor(pre_saved, who, "pre_saved"));
+  if (fc1->rank + fc1->stab_rank > 0) TRY(check_tensor(xl1_saved, who, "xl1_saved"));
+  if (fc2->rank + fc2->stab_rank > 0) TRY(check_tensor(hl2_saved, who, "hl2_saved"));
+  if (hq_out) TRY(check_mx4(hq_out, m, fc1->n, "mlp_fwd: hq_out"));
+  const MlpFwdLayout lay = mlp_fwd_layout(ws, m, fc1, fc2, hq_out == nullptr);
+  REQUIRE(ws != nullptr && ws_bytes >= lay.bytes, FT_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed",
+          who, ws_bytes, lay.bytes);
+  REQUIRE(aligned16(ws), FT_ERR_ALIGN, "%s: workspace misaligned", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t d = fc1->k, fdim = fc1->n;
+  uint8_t* hq_codes = hq_out ? hq_out->codes : lay.hq_codes;
+  uint8_t* hq_scales = hq_out ? hq_out->scales : lay.hq_scales;
+
+  TRY(run_quant_down(ft::QD_QUANT, fc1, true, x, x_dt == FT_BF16, m, d, lay.xq_codes, lay.xq_scales, xl1_saved,
+                     lay.partials, st, "mlp_fwd quant_down(X)"));
+  Epi e;
+  e.kind = ft::GEMM_EPI_GELU_Q; e.q_codes = hq_codes; e.q_scales = hq_scales;
+  TRY(run_gemm_fwd(fc1, lay.xq_codes, lay.xq_scales, xl1_saved, m, pre_saved, FT_BF16, st, e));
+  if (fc2->rank + fc2->stab_rank > 0)
+    TRY(run_quant_down(ft::QD_GELU_DOWN, fc2, true, pre_saved, true, m, fdim, nullptr, nullptr, hl2_saved,
+                       lay.partials, st, "mlp_fwd down(GELU(P))"));
+  TRY(run_gemm_fwd(fc2, hq_codes, hq_scales, hl2_saved, m, y, y_dt, st));
+  return ok();
+}
+
+ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const void* dy, ft_dtype dy_dt,
+                           const void* x, ft_dtype x_dt, const void* xl1_saved, const void* pre_saved,
+                           const void* hl2_saved, int64_t m, void* dx, ft_dtype dx_dt, float* d_a1, float* d_b1,
+                           float* d_a2, float* d_b2, ft_mx4* dpq_out, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "mlp_bwd";
+  TRY(check_mlp(fc1, fc2, m, who));
+  REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  if (m == 0) return ok();
+  TRY(check_tensor(dy, who, "dy"));
+  TRY(check_tensor(dx, who, "dx"));
+  TRY(check_tensor(pre_saved, who, "pre_saved"));
+  if (fc1->rank > 0) {
+    TRY(check_tensor(x, who, "x"));
+    TRY(check_tensor(xl1_saved, who, "xl1_saved"));
+    TRY(check_tensor(d_a1, who, "d_a1"));
+    TRY(check_tensor(d_b1, who, "d_b1"));
+  }
+  if (fc2->rank > 0) {
+    TRY(check_tensor(hl2_saved, who, "hl2_saved"));
+    TRY(check_tensor(d_a2, who, "d_a2"));
+    TRY(check_tensor(d_b2, who, "d_b2"));
+  }
+  if (dpq_out) TRY(check_mx4(dpq_out, m, fc1->n, "mlp_bwd: dpq_out"));
+  const MlpBwdLayout lay = mlp_bwd_layout(ws, m, fc1, fc2, dpq_out == nullptr);
+  REQUIRE(ws != nullptr && ws_bytes >= lay.bytes, FT_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed",
+          who, ws_bytes, lay.bytes);
+  REQUIRE(aligned16(ws), FT_ERR_ALIGN, "%s: workspace misaligned", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t fdim = fc1->n, dout = fc2->n;
+  uint8_t* dpq_codes = dpq_out ? dpq_out->codes : lay.dpq_codes;
+  uint8_t* dpq_scales = dpq_out ? dpq_out->scales : lay.dpq_scales;
+
+  TRY(run_quant_down(ft::QD_QUANT, fc2, false, dy, dy_dt == FT_BF16, m, dout, lay.gq_codes, lay.gq_scales,
+                     lay.gb2, lay.partials, st, "mlp_bwd quant_down(dY)"));
+  Epi e;
+  e.kind = ft::GEMM_EPI_DGELU_Q; e.pre = pre_saved; e.q_codes = dpq_codes; e.q_scales = dpq_scales;
+  TRY(run_gemm_bwd(fc2, lay.gq_codes, lay.gq_scales, lay.gb2, m, lay.dp, FT_BF16, st, e));
+  TRY(run_lora_grad(fc2, m, lay.gb2, pre_saved, true, true, hl2_saved, dy, dy_dt == FT_BF16, d_a2, d_b2,
+                    lay.partials, st, "mlp_bwd lora_grad(fc2)"));
+  if (fc1->rank + fc1->stab_rank > 0)
+    TRY(run_quant_down(ft::QD_DOWN, fc1, false, lay.dp, true, m, fdim, nullptr, nullptr, lay.gb1, lay.partials, st,
+                       "mlp_bwd down(dP)"));
+  TRY(run_gemm_bwd(fc1, dpq_codes, dpq_scales, lay.gb1, m, dx, dx_dt, st));
+  TRY(run_lora_grad(fc1, m, lay.gb1, x, x_dt == FT_BF16, false, xl1_saved, lay.dp, true, d_a1, d_b1,
+                    lay.partials, st, "mlp_bwd lora_grad(fc1)"));
+  return ok();
 }
 
 }  // extern "C"

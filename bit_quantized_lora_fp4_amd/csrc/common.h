@@ -84,6 +84,38 @@ __device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
   return (a > b ? a : b) << 16;
 }
 
+// ---------------------------------------------------------------- GELU (tanh form)
+// GELU(p) = p/2 (1 + tanh(u)), u = sqrt(2/pi) (p + 0.044715 p^3) (FourTune §3.3 "MLP
+// Fusion" applies GELU between the two linears of an MLP), evaluated without
+// cancellation as p * s with s = (1 + tanh(u))/2 = 1 / (1 + e^(-2u)); e^(-2u) comes from
+// the hardware base-2 exponential and s from the hardware reciprocal, so the relative
+// error stays within a few fp32 ulps also where GELU is tiny (large negative p).
+// Derivative: s + p (1 - tanh^2(u))/2 du/dp = s (1 + 2 p (1 - s) du/dp).
+// Large |u| saturates correctly (e -> 0 or inf); NaN propagates.
+constexpr float GELU_K0 = 0.7978845608028654f;  // sqrt(2/pi)
+constexpr float GELU_K1 = 0.044715f;
+constexpr float M2_LOG2E = -2.8853900817779268f;  // -2 / ln(2)
+__device__ __forceinline__ float gelu_f(float p) {
+  const float u = GELU_K0 * (p + GELU_K1 * p * p * p);
+  const float e = __builtin_amdgcn_exp2f(u * M2_LOG2E);
+  return p * __builtin_amdgcn_rcpf(1.0f + e);
+}
+__device__ __forceinline__ float gelu_grad_f(float p) {
+  const float u = GELU_K0 * (p + GELU_K1 * p * p * p);
+  const float e = __builtin_amdgcn_exp2f(u * M2_LOG2E);
+  const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+  const float du = GELU_K0 * (1.0f + 3.0f * GELU_K1 * p * p);
+  // 1 - s, formed without overflow (e may be huge or infinite) or cancellation
+  const float es = e > 1.0f ? 1.0f - sg : e * sg;
+  const float g = sg * (1.0f + 2.0f * p * es * du);
+  // |p| > 16: the derivative is 1 (or 0) to fp32 precision; p^3 may overflow there
+  return fabsf(p) > 16.0f ? (p > 0.0f ? 1.0f : 0.0f) : g;
+}
+// 8 bf16 (4 words) -> bf16(GELU(x)) for each, rounded to nearest even
+__device__ __forceinline__ uint32_t gelu_bf16x2(uint32_t w) {
+  return pack_bf16x2(gelu_f(bf16_lo(w)), gelu_f(bf16_hi(w)));
+}
+
 // ---------------------------------------------------------------- LDS transposed reads
 typedef __attribute__((address_space(3))) char lds_char;
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -129,6 +161,12 @@ __device__ __forceinline__ uint32_t buf_load4(bufres r, uint32_t off) {
 }
 __device__ __forceinline__ uint32_t buf_load1(bufres r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ v2i buf_load8(bufres r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(bufres r, uint32_t off, v2i v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }
 __device__ __forceinline__ void buf_store4(bufres r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);

@@ -32,7 +32,17 @@ struct GemmArgs {
   int up_split;
   void* out;                // [M x N] fp32 or bf16, row stride ldo
   int64_t ldo;
+  // MLP epilogues (bf16 output only; FourTune §3.3 "MLP Fusion"):
+  //   GEMM_EPI_GELU_Q : out = P^ = bf16(result); Q(GELU(P^)) -> q_codes/q_scales
+  //   GEMM_EPI_DGELU_Q: dP = result * GELU'(pre); out = bf16(dP); Q(dP) -> q_codes/q_scales
+  //                     (pre = the saved P^ [M x N] bf16, row stride N)
+  int epi;
+  const bf16_t* pre;
+  uint8_t* q_codes;         // [M x N/2]
+  uint8_t* q_scales;        // [ceil(M/32) x N/32]
 };
+
+enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_Q = 1, GEMM_EPI_DGELU_Q = 2 };
 
 hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipStream_t stream);
 // Longest reduction the GEMM supports (its block scales are staged in LDS once).
@@ -47,7 +57,11 @@ constexpr int64_t GEMM_MAX_KRED = 16384;
 // The K range is split S = quant_down_splits(M, K, rt) ways; with S > 1 the launch
 // needs quant_down_partial_bytes(M, K, r0, rt) bytes of fp32 partials, which a second
 // kernel sums in a fixed order.
+// mode: QD_QUANT (as above); QD_GELU_DOWN: no quantization, the down-projection reads
+// bf16(GELU(x)) (x = the saved P^, bf16); QD_DOWN: no quantization (x bf16).
+enum { QD_QUANT = 0, QD_GELU_DOWN = 1, QD_DOWN = 2 };
 struct QuantDownArgs {
+  int mode;
   const void* x;
   int64_t M, K, ldx;
   uint8_t* codes;
@@ -93,6 +107,7 @@ struct LoraGradArgs {
   float* dB;             // [N x r]
   // scratch
   float* partials;       // lora_grad_partial_bytes(M, K, N, r) bytes
+  bool gelu_x;           // the dA job reads bf16(GELU(x)) instead of bf16(x) (x bf16)
   // set by the launcher
   int tile_offset;
   int ntiles;

@@ -131,7 +131,40 @@ __device__ __forceinline__ void tile_of(int bid, int nwg, int tiles_m, int tiles
   tn = in_band / gm;
 }
 
-template <bool TRANS_B, bool OUT_BF16>
+// One 32x32 accumulator tile = one 32x32 block of the output. Quantize the fp32 values
+// v (accumulator layout: lane l holds row l%32, register 4g+c column 8g + 4(l/32) + c)
+// to MXFP4 and store codes and the scale byte. Lanes l and l+32 first trade column
+// groups with v_permlane32_swap so that lane l holds columns 0..15 of its row and lane
+// l+32 columns 16..31: each lane then writes 8 contiguous code bytes.
+__device__ __forceinline__ void quant_tile_store(const float (&v)[16], int lane, int64_t row, bool row_ok,
+                                                 bool blk_ok, int64_t blk_row, int64_t col0, bufres rcodes,
+                                                 bufres rscales, int64_t cpitch, int64_t nkb) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) m = umax(m, __builtin_bit_cast(uint32_t, v[r]) & 0x7FFFFFFFu);
+  const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
+  const float scale = e8m0_to_f32_scale(sb);
+  float w[16];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    // (g0, g2) and (g1, g3): lanes 32..63 of the first take lanes 0..31 of the second
+    const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[c]),
+                                                    __builtin_bit_cast(uint32_t, v[8 + c]), false, false);
+    const auto q = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, v[4 + c]),
+                                                    __builtin_bit_cast(uint32_t, v[12 + c]), false, false);
+    w[c] = __builtin_bit_cast(float, (uint32_t)p[0]);
+    w[4 + c] = __builtin_bit_cast(float, (uint32_t)p[1]);
+    w[8 + c] = __builtin_bit_cast(float, (uint32_t)q[0]);
+    w[12 + c] = __builtin_bit_cast(float, (uint32_t)q[1]);
+  }
+  v2i cw = {(int)cvt8_f32(w, scale), (int)cvt8_f32(w + 8, scale)};
+  if (sb == 0xFFu) cw = v2i{0, 0};
+  const int half = lane >> 5;
+  buf_store8(rcodes, sel_off(row_ok && blk_ok, (uint32_t)(row * cpitch + ((col0 + 16 * half) >> 1))), cw);
+  buf_store1(rscales, sel_off(blk_ok && lane == 0, (uint32_t)(blk_row * nkb + (col0 >> 5))), sb);
+}
+
+template <bool TRANS_B, bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   __shared__ __align__(16) char smem_raw[LDS_BYTES];
   lds_char* smem = (lds_char*)(smem_raw);
@@ -438,6 +471,43 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     }
   }
 
+  // ---------------------------------------------------------------- MLP epilogues
+  // backward (FC2's dX GEMM): dP = dH * GELU'(P^) in place, Q(dP) from the fp32 values;
+  // the store below then writes bf16(dP). The forward epilogue (Q(GELU(P^))) runs after
+  // the store, from the bf16 P^ the store staged in LDS.
+  if constexpr (EPI == GEMM_EPI_DGELU_Q) {
+    const bufres rqc = make_buf(g.q_codes, (uint64_t)g.M * (g.N >> 1));
+    const bufres rqs = make_buf(g.q_scales, (uint64_t)((g.M + 31) >> 5) * (g.N >> 5));
+    const bufres rpre = make_buf(g.pre, (uint64_t)g.M * g.N * 2);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int64_t brow = m0 + wm * 128 + 32 * j;  // first row of this block row
+      const int64_t row = brow + (lane & 31);
+      const bool row_ok = row < g.M;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int64_t col0 = n0 + wn * 128 + 32 * i;
+        v2i pw[TI][4];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int64_t col = col0 + 8 * gq + 4 * half;
+          pw[i][gq] = buf_load8(rpre, sel_off(row_ok && col < g.N, (uint32_t)((row * g.N + col) * 2)));
+        }
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t pwd = (uint32_t)((r & 2) ? pw[i][r >> 2].y : pw[i][r >> 2].x);
+          const float p = (r & 1) ? bf16_hi(pwd) : bf16_lo(pwd);
+          acc[i][j][r] = acc[i][j][r] * gelu_grad_f(p);  // dP = dH * GELU'(P^)
+          v[r] = acc[i][j][r];
+        }
+        quant_tile_store(v, lane, row, row_ok, brow < g.M && col0 < g.N, brow >> 5, col0, rqc, rqs, g.N >> 1,
+                         g.N >> 5);
+        __builtin_amdgcn_sched_barrier(0);  // one tile at a time: bounded register use
+      }
+    }
+  }
+
   // ---------------------------------------------------------------- store
   // Each wave stages its 128 x 128 result in LDS (the stages are free now), then 16
   // consecutive lanes write 256 contiguous bytes of one output row per instruction.
@@ -469,6 +539,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       const int64_t row = orow0 + r, col = ocol0 + c;
       if (row < g.M && col < g.N)
         *reinterpret_cast<v4i*>(reinterpret_cast<bf16_t*>(g.out) + row * g.ldo + col) = v;
+    }
+    if constexpr (EPI == GEMM_EPI_GELU_Q) {
+      // FC1 forward: H = GELU(P^) from the staged bf16 P^ (the stored values), then Q(H)
+      // per 32x32 block: lane l takes row l%32 of the block and its 16 columns
+      // 16*(l/32) .. +16, so its 8 code bytes are contiguous.
+      const bufres rqc = make_buf(g.q_codes, (uint64_t)g.M * (g.N >> 1));
+      const bufres rqs = make_buf(g.q_scales, (uint64_t)((g.M + 31) >> 5) * (g.N >> 5));
+#pragma unroll 1
+      for (int t = 0; t < TI * TJ; ++t) {
+        const int j = t >> 2, i = t & 3;
+        const int lr = 32 * j + (lane & 31), lc = 32 * i + 16 * half;
+        const v4i a = lds_read_b128(wbuf + lr * OP + lc * 2);
+        const v4i b = lds_read_b128(wbuf + lr * OP + lc * 2 + 16);
+        const uint32_t wd[8] = {(uint32_t)a.x, (uint32_t)a.y, (uint32_t)a.z, (uint32_t)a.w,
+                                (uint32_t)b.x, (uint32_t)b.y, (uint32_t)b.z, (uint32_t)b.w};
+        float h[16];
+        uint32_t m = 0;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          h[2 * q] = gelu_f(bf16_lo(wd[q]));
+          h[2 * q + 1] = gelu_f(bf16_hi(wd[q]));
+          m = umax(m, umax(__builtin_bit_cast(uint32_t, h[2 * q]) & 0x7FFFFFFFu,
+                           __builtin_bit_cast(uint32_t, h[2 * q + 1]) & 0x7FFFFFFFu));
+        }
+        const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
+        const float scale = e8m0_to_f32_scale(sb);
+        v2i cw = {(int)cvt8_f32(h, scale), (int)cvt8_f32(h + 8, scale)};
+        if (sb == 0xFFu) cw = v2i{0, 0};
+        const int64_t brow = orow0 + 32 * j, row = brow + (lane & 31), col0 = ocol0 + 32 * i;
+        const bool blk_ok = brow < g.M && col0 < g.N;
+        buf_store8(rqc, sel_off(blk_ok && row < g.M, (uint32_t)(row * (g.N >> 1) + ((col0 + 16 * half) >> 1))), cw);
+        buf_store1(rqs, sel_off(blk_ok && lane == 0, (uint32_t)((brow >> 5) * (g.N >> 5) + (col0 >> 5))), sb);
+      }
     }
   } else {
     // fp32: two passes of 64 rows (64 x 512 bytes per wave)
@@ -509,18 +612,26 @@ static_assert(GEMM_MAX_KRED == MAX_NKB * 32, "scale staging bound");
 hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipStream_t stream) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (g.Kred > GEMM_MAX_KRED) return hipErrorInvalidValue;
+  if (g.epi != GEMM_EPI_NONE && (!out_bf16 || g.q_codes == nullptr || g.q_scales == nullptr ||
+                                 (g.epi == GEMM_EPI_DGELU_Q && g.pre == nullptr) ||
+                                 (g.epi == GEMM_EPI_GELU_Q) == trans_b))
+    return hipErrorInvalidValue;
   const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
   dim3 grid(tiles), block(256);
-  if (!trans_b) {
+  if (g.epi == GEMM_EPI_GELU_Q) {
+    hipLaunchKernelGGL((k_gemm_mx4<false, true, GEMM_EPI_GELU_Q>), grid, block, 0, stream, g);
+  } else if (g.epi == GEMM_EPI_DGELU_Q) {
+    hipLaunchKernelGGL((k_gemm_mx4<true, true, GEMM_EPI_DGELU_Q>), grid, block, 0, stream, g);
+  } else if (!trans_b) {
     if (out_bf16)
-      hipLaunchKernelGGL((k_gemm_mx4<false, true>), grid, block, 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<false, true, GEMM_EPI_NONE>), grid, block, 0, stream, g);
     else
-      hipLaunchKernelGGL((k_gemm_mx4<false, false>), grid, block, 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<false, false, GEMM_EPI_NONE>), grid, block, 0, stream, g);
   } else {
     if (out_bf16)
-      hipLaunchKernelGGL((k_gemm_mx4<true, true>), grid, block, 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<true, true, GEMM_EPI_NONE>), grid, block, 0, stream, g);
     else
-      hipLaunchKernelGGL((k_gemm_mx4<true, false>), grid, block, 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<true, false, GEMM_EPI_NONE>), grid, block, 0, stream, g);
   }
   return hipGetLastError();
 }

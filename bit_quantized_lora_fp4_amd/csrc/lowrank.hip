@@ -63,13 +63,16 @@ struct Slab {
     }
   }
 
-  __device__ void stage(lds_char* sbig, lds_char* ssmall, int small_pitch, int lane) const {
+  __device__ void stage(lds_char* sbig, lds_char* ssmall, int small_pitch, int lane, bool gelu) const {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = i * 64 + lane;
       v4i v;
       if constexpr (BIG_BF16) {
         v = big[i];
+        if (gelu)  // uniform: bf16(GELU(P^)) for the MLP's second linear
+          v = v4i{(int)gelu_bf16x2((uint32_t)v.x), (int)gelu_bf16x2((uint32_t)v.y),
+                  (int)gelu_bf16x2((uint32_t)v.z), (int)gelu_bf16x2((uint32_t)v.w)};
       } else {
         const v4f a = __builtin_bit_cast(v4f, big[2 * i]), b = __builtin_bit_cast(v4f, big[2 * i + 1]);
         v = v4i{(int)pack_bf16x2(a.x, a.y), (int)pack_bf16x2(a.z, a.w), (int)pack_bf16x2(b.x, b.y),
@@ -106,6 +109,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const LoraGradArgs a) {
   const void* bg = jobA ? a.x : a.g;
   const int64_t nbig = jobA ? a.K : a.N;
   const int64_t q0 = (int64_t)(jobA ? tile : tile - tilesA) * LG_Q;
+  const bool gelu = BIG_BF16 && a.gelu_x && jobA;
   const int64_t per = ((a.M + S - 1) / S + LG_SLAB - 1) / LG_SLAB * LG_SLAB;
   const int64_t mb = split * per, me = min(a.M, mb + per);
 
@@ -125,7 +129,7 @@ __global__ __launch_bounds__(256) void k_lora_grad(const LoraGradArgs a) {
     sl.load(rb, rs, m0 < me ? m0 : a.M, q0, nbig, nbig, ld_sm, a.r, lane);
   };
   auto work = [&](const Slab<BIG_BF16, PT>& sl) {
-    sl.stage(sbig, ssmall, SMALL_PITCH, lane);
+    sl.stage(sbig, ssmall, SMALL_PITCH, lane, gelu);
 #pragma unroll
     for (int ms = 0; ms < LG_SLAB; ms += 16) {
       v4i sa[PT], bb[2];

@@ -210,9 +210,10 @@ __device__ __forceinline__ void lds_tr16_qn_tiles(const lds_char* base, int n0, 
   }
 }
 
-template <typename T, int TP, bool UCOLS>
+template <typename T, int TP, bool UCOLS, int MODE>
 __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   using DS = DStage<TP, UCOLS>;
+  constexpr int NS = MODE == QD_QUANT ? QD_STORES : 0;  // stores per chunk
   constexpr int RTP = 32 * TP;  // padded low-rank width
   constexpr int WAVE_LDS = 2 * DS::BYTES;
   constexpr int RED = QD_WAVES * 2 * TP * 16 * 64 * 4;
@@ -266,6 +267,14 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
     if constexpr (TP > 0) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        v4i xop[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          xop[h] = x.operand(h, s);
+          if constexpr (MODE == QD_GELU_DOWN)  // bf16(GELU(P^)), P^ the saved FC1 output
+            xop[h] = v4i{(int)gelu_bf16x2((uint32_t)xop[h].x), (int)gelu_bf16x2((uint32_t)xop[h].y),
+                         (int)gelu_bf16x2((uint32_t)xop[h].z), (int)gelu_bf16x2((uint32_t)xop[h].w)};
+        }
         v4i dtr[TP];
         if constexpr (UCOLS) lds_tr16_qn_tiles<TP, DS::QSTRIDE>(sd, 16 * s, lane, dtr);
 #pragma unroll
@@ -276,12 +285,13 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             acc[h][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, dv),
-                                                                __builtin_bit_cast(bf16x8, x.operand(h, s)),
+                                                                __builtin_bit_cast(bf16x8, xop[h]),
                                                                 acc[h][t], 0, 0, 0);
         }
       }
     }
     // ---- quantize the chunk's four 32x32 blocks (2 row halves x 2 column blocks)
+    if constexpr (MODE == QD_QUANT)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -319,14 +329,14 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   // same sequence of outstanding memory operations as each later trip, so the
   // compiler's waits for x0 at the top of the loop are no stricter than needed.
 #pragma unroll
-  for (int i = 0; i < QD_STORES; ++i) {
+  for (int i = 0; i < NS; ++i) {
     uint32_t off = BUF_OOB + 16u * i;  // distinct, opaque: none may be merged away
     asm volatile("" : "+v"(off));
     buf_store4(rcodes, off, 0u);
   }
   asm volatile("" ::: "memory");
   fetch(sd1, ch + QD_WAVES);
-  if constexpr (TP > 0) wait_vmcnt<NX + QD_STORES + ND>();  // operand of chunk ch in sd0
+  if constexpr (TP > 0) wait_vmcnt<NX + NS + ND>();  // operand of chunk ch in sd0
   __builtin_amdgcn_sched_barrier(0);
   // (scheduling barriers keep each half's arithmetic after the wait that guards it)
   for (; ch < ch1; ch += 2 * QD_WAVES) {
@@ -337,7 +347,7 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
     if constexpr (TP > 0) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // sd0 reads done before it is refilled
       fetch(sd0, ch + 2 * QD_WAVES);
-      wait_vmcnt<NX + QD_STORES + ND>();  // operand of chunk ch + 4 in sd1
+      wait_vmcnt<NX + NS + ND>();  // operand of chunk ch + 4 in sd1
     }
     __builtin_amdgcn_sched_barrier(0);
     x0.load(rx, row_off, row_ok, cstart(ch + 2 * QD_WAVES), a.K, half);
@@ -347,7 +357,7 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
     if constexpr (TP > 0) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       fetch(sd1, ch + 3 * QD_WAVES);
-      wait_vmcnt<NX + QD_STORES + ND>();  // operand of chunk ch + 8 in sd0
+      wait_vmcnt<NX + NS + ND>();  // operand of chunk ch + 8 in sd0
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -421,15 +431,15 @@ __global__ __launch_bounds__(256) void k_sum_partials(const float* __restrict__ 
   *reinterpret_cast<uint2*>(low + row * rt + oc) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
 }
 
-template <typename T, bool UCOLS>
+template <typename T, bool UCOLS, int MODE>
 hipError_t launch_t(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
   dim3 grid((unsigned)((a.M + QD_ROWS - 1) / QD_ROWS), (unsigned)splits), block(256);
   switch (tp) {
-    case 0: hipLaunchKernelGGL((k_quant_down<T, 0, UCOLS>), grid, block, 0, stream, a); break;
-    case 1: hipLaunchKernelGGL((k_quant_down<T, 1, UCOLS>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_quant_down<T, 2, UCOLS>), grid, block, 0, stream, a); break;
-    case 3: hipLaunchKernelGGL((k_quant_down<T, 3, UCOLS>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_quant_down<T, 4, UCOLS>), grid, block, 0, stream, a); break;
+    case 0: hipLaunchKernelGGL((k_quant_down<T, 0, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((k_quant_down<T, 1, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_quant_down<T, 2, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL((k_quant_down<T, 3, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_quant_down<T, 4, UCOLS, MODE>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -461,10 +471,17 @@ hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t st
   const int S = quant_down_splits(a.M, a.K, a.rt);
   if (S > 1 && a.partials == nullptr) return hipErrorInvalidValue;
   hipError_t e;
-  if (a.u_cols)
-    e = x_bf16 ? launch_t<bf16_t, true>(a, tp, S, stream) : launch_t<float, true>(a, tp, S, stream);
-  else
-    e = x_bf16 ? launch_t<bf16_t, false>(a, tp, S, stream) : launch_t<float, false>(a, tp, S, stream);
+  if (a.mode == QD_GELU_DOWN) {  // the saved FC1 output P^: bf16, [A2; L1_2] rows
+    if (!x_bf16 || a.u_cols || tp == 0) return hipErrorInvalidValue;
+    e = launch_t<bf16_t, false, QD_GELU_DOWN>(a, tp, S, stream);
+  } else if (a.mode == QD_DOWN) {  // dP^ (bf16) against [B1 | L2_1]
+    if (!x_bf16 || !a.u_cols || tp == 0) return hipErrorInvalidValue;
+    e = launch_t<bf16_t, true, QD_DOWN>(a, tp, S, stream);
+  } else if (a.u_cols) {
+    e = x_bf16 ? launch_t<bf16_t, true, QD_QUANT>(a, tp, S, stream) : launch_t<float, true, QD_QUANT>(a, tp, S, stream);
+  } else {
+    e = x_bf16 ? launch_t<bf16_t, false, QD_QUANT>(a, tp, S, stream) : launch_t<float, false, QD_QUANT>(a, tp, S, stream);
+  }
   if (e != hipSuccess || S == 1) return e;
   const int64_t items = a.M * 32 * tp / 4;
   hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a.partials, S,

@@ -154,36 +154,49 @@ ft_status fourtune_gemm_fwd(const ft_linear *L, const ft_mx4 *xq, const void *xl
 ft_status fourtune_gemm_bwd(const ft_linear *L, const ft_mx4 *gq, const void *gb, int64_t m,
                             void *dx, ft_dtype dx_dt, void *stream);
 
-/* Workspace bytes needed by fourtune_mlp_fwd and fourtune_mlp_bwd for m rows. */
+/* Workspace bytes needed by fourtune_mlp_fwd and fourtune_mlp_bwd for m rows
+ * (same contract as the linear's workspace). */
 size_t fourtune_mlp_workspace_bytes(int64_t m, const ft_linear *fc1, const ft_linear *fc2);
 
 /* fourtune_mlp_fwd -- FC1 -> GELU (tanh form) -> FC2 (FourTune §3.3 "MLP Fusion").
- * fc1: d -> f, fc2: f -> d (fc1->n == fc2->k, fc2->n == fc1->k). The FC1 GEMM's
- * epilogue stores P^ = bf16(FC1 output) (kept for the backward), computes
- * H = GELU(P^) in fp32 and writes FC2's 4-bit operand Q(H) and partial sums of
- * bf16(H) [A2;L1_2]^T directly; H itself is never written to memory.
- *   x         [m x d] fp32 or bf16 (x_dt)
- *   y         [m x d] fp32 or bf16 (y_dt), overwritten
+ * fc1: d -> f, fc2: f -> d (fc1->n == fc2->k). Kernels, in order:
+ *   1. one pass over X: Q(X) and XL1 = bf16(X^ [A1;L1_1]^T)            (§3.3 "LoRA Fusion")
+ *   2. FC1's 4-bit GEMM + up-projection; its epilogue stores P^ = bf16(FC1 output),
+ *      forms H = GELU(P^) in fp32 and writes FC2's 4-bit operand Q(H); H itself is
+ *      never written to memory                                          (§3.3 "MLP Fusion")
+ *   3. HL2 = bf16(bf16(GELU(P^)) [A2;L1_2]^T) from the saved P^
+ *   4. FC2's 4-bit GEMM + up-projection: y = Q(H) Q(R2)^T + HL2 [B2|L2_2]^T.
+ *   x         [m x d] fp32 or bf16 (x_dt), contiguous
+ *   y         [m x fc2->n] fp32 or bf16 (y_dt), overwritten
  *   xl1_saved [m x rt1] bf16, pre_saved [m x f] bf16, hl2_saved [m x rt2] bf16:
  *             overwritten; pass them to the backward.
- *   h_debug   optional [m x f] fp32: receives H (for checks), may be NULL. */
+ *   hq_out    optional (may be NULL): receives Q(H) ([m x f] MXFP4) instead of the
+ *             workspace holding it.
+ * f must be at most 16384 (it is FC2's reduction length). */
 ft_status fourtune_mlp_fwd(const ft_linear *fc1, const ft_linear *fc2, const void *x,
                            ft_dtype x_dt, int64_t m, void *y, ft_dtype y_dt, void *xl1_saved,
-                           void *pre_saved, void *hl2_saved, float *h_debug, void *ws,
+                           void *pre_saved, void *hl2_saved, ft_mx4 *hq_out, void *ws,
                            size_t ws_bytes, void *stream);
 
-/* fourtune_mlp_bwd -- backward of the MLP pair. FC2's dX GEMM epilogue forms
- * dP = dH * GELU'(P^) and writes FC1's 4-bit gradient operand Q(dP) and its
- * down-projection partials directly; FC1's backward then runs as in
- * fourtune_linear_bwd with G = dP.
- *   dy [m x d] (dy_dt); x, xl1_saved, pre_saved, hl2_saved from the forward;
- *   dx [m x d] (dx_dt); d_a1 [r1 x d], d_b1 [f x r1], d_a2 [r2 x f], d_b2 [d x r2] fp32;
- *   dp_debug optional [m x f] fp32: receives dP, may be NULL. */
+/* fourtune_mlp_bwd -- backward of the MLP pair (FourTune §3.2 for each linear, §3.3
+ * "MLP Fusion" for the GELU). Kernels, in order:
+ *   1. one pass over dY: Q(dY) and GB2 = bf16(dY^ [B2|L2_2])
+ *   2. FC2's transposed 4-bit GEMM + up-projection gives dH; its epilogue forms
+ *      dP = dH * GELU'(P^) in fp32, writes Q(dP) (FC1's 4-bit gradient operand) and
+ *      stores dP^ = bf16(dP)
+ *   3. FC2's LoRA gradients: dA2 = GB2_A^T bf16(GELU(P^)), dB2 = dY^^T HL2_A
+ *   4. GB1 = bf16(dP^ [B1|L2_1])
+ *   5. FC1's transposed 4-bit GEMM + up-projection: dx = Q(dP) Q(R1) + GB1 [A1;L1_1]
+ *   6. FC1's LoRA gradients: dA1 = GB1_A^T X^, dB1 = dP^^T XL1_A.
+ *   dy [m x fc2->n] (dy_dt); x, xl1_saved, pre_saved, hl2_saved from the forward;
+ *   dx [m x d] (dx_dt), overwritten; d_a1 [r1 x d], d_b1 [f x r1], d_a2 [r2 x f],
+ *   d_b2 [fc2->n x r2] fp32, overwritten (may be NULL when that rank is 0).
+ *   dpq_out optional (may be NULL): receives Q(dP) ([m x f] MXFP4). */
 ft_status fourtune_mlp_bwd(const ft_linear *fc1, const ft_linear *fc2, const void *dy,
                            ft_dtype dy_dt, const void *x, ft_dtype x_dt, const void *xl1_saved,
                            const void *pre_saved, const void *hl2_saved, int64_t m, void *dx,
                            ft_dtype dx_dt, float *d_a1, float *d_b1, float *d_a2, float *d_b2,
-                           float *dp_debug, void *ws, size_t ws_bytes, void *stream);
+                           ft_mx4 *dpq_out, void *ws, size_t ws_bytes, void *stream);
 
 /* Static text of a status code. */
 const char *fourtune_status_string(ft_status s);
