@@ -65,16 +65,15 @@ __device__ __forceinline__ uint32_t cvt8_f32(const float* v, float scale) {
 }
 
 // ---------------------------------------------------------------- bf16 helpers
-// fp32 -> bf16 round-to-nearest-even on the bit pattern (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16, round to nearest even (NaN kept quiet): the gfx950 conversion
+// v_cvt_pk_bf16_f32, which the compiler emits for a float2 -> bf16x2 vector conversion.
+// Checked bit for bit against the integer formulation (bias 0x7FFF plus the kept bit's
+// parity, then truncation) on 16.7M patterns including ties, denormals and NaNs.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.0f) & 0xFFFFu; }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 

@@ -41,14 +41,17 @@ namespace ft {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;    // output tile (rows, cols), reduction step
+constexpr int BM = 256, BN = 256, BK = 256;    // output tile (rows, cols), reduction step
 constexpr int TI = 4, TJ = 4;                  // 32x32 MFMA tiles per wave: R side, act side
-constexpr int TILE_BYTES = 256 * BK / 2;       // 16 KB of codes per operand tile per step
+constexpr int SUBSTEPS = BK / 64;              // MFMA reduction substeps per step
+constexpr int TILE_BYTES = 256 * BK / 2;       // 32 KB of codes per operand tile per step
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // activation tile + R tile
-constexpr int STAGES = 4;
-constexpr int SEGS = TILE_BYTES / 1024 / 4;    // 1 KB load segments per wave per tile (4)
+constexpr int STAGES = 2;
+constexpr int SEGS = TILE_BYTES / 1024 / 4;    // 1 KB load segments per wave per tile (8)
 constexpr int SCALE_BYTES = 8192;              // LDS for the two operands' block scales
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES + SCALE_BYTES;
+constexpr int TOUCH_BYTES = 1024;              // landing slots of the L2 prefetch loads
+constexpr int LDS_BYTES = STAGES * STAGE_BYTES + SCALE_BYTES + TOUCH_BYTES;
+constexpr int TOUCHES = 2;                     // prefetch loads per wave per step
 constexpr int MAX_NKB = SCALE_BYTES / 2 / 8;   // 8 block rows per operand: Kred <= 16384
 constexpr int SW = 8 * MAX_NKB / 4 / 256;      // scale words staged per thread per operand (4)
 
@@ -90,9 +93,8 @@ __device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
 // across it; unlike __syncthreads() it does not drain loads that may stay in flight.
 template <int N>
 __device__ __forceinline__ void vm_barrier() {
-  static_assert(N == 0 || N == 16, "vmcnt immediate");
-  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 // Four transposed 16x16-nibble reads (two output-column fragments) and the wait for
@@ -193,10 +195,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   const bufres rsr = make_buf(g.b_scales, (uint64_t)((r_rows + 31) >> 5) * nkb_r);
 
   // ---- per-lane DMA sources: segment q (1 KB) of a tile; lane l fills the 16-byte LDS
-  // slot 16*l of the segment.
-  //   activation / forward-R tile (64-byte rows): rows 16q + l/4, slot unit l%4
-  //   backward-R tile (128-byte rows, reduction rows x 256 output columns):
-  //     rows 8q + l/8, slot unit l%8
+  // slot 16*l of the segment. Every tile has 128-byte rows (whole cache lines):
+  //   activation / forward-R tile: 256 rows x 256 reduction elements
+  //   backward-R tile: 256 reduction rows x 256 output columns
+  // rows 8q + l/8, slot unit l%8, holding global unit (l%8) ^ swz8(row).
   uint32_t a_base[SEGS], r_base[SEGS];
   bool a_ok[SEGS], r_ok[SEGS];
   int a_k[SEGS], r_k[SEGS];  // reduction offset within the step (elements)
@@ -204,13 +206,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   for (int i = 0; i < SEGS; ++i) {
     const int q = wave * SEGS + i;
     {
-      const int row = 16 * q + (lane >> 2), c16 = (lane & 3) ^ swz4(row);
+      const int row = 8 * q + (lane >> 3), c16 = (lane & 7) ^ swz8(row);
       a_k[i] = c16 * 32;
       a_ok[i] = m0 + row < g.M;
       a_base[i] = (uint32_t)((m0 + row) * a_pitch + c16 * 16);
     }
     if constexpr (!TRANS_B) {
-      const int row = 16 * q + (lane >> 2), c16 = (lane & 3) ^ swz4(row);
+      const int row = 8 * q + (lane >> 3), c16 = (lane & 7) ^ swz8(row);
       r_k[i] = c16 * 32;
       r_ok[i] = n0 + row < g.N;
       r_base[i] = (uint32_t)((n0 + row) * g.b_pitch + c16 * 16);
@@ -229,13 +231,45 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     for (int i = 0; i < SEGS; ++i) {
       const int q = wave * SEGS + i;
       const bool ka = live && a_ok[i] && (int64_t)kt * BK + a_k[i] < Kred;
-      buf_load16_lds(ra, st + q * 1024, ka ? a_base[i] + (uint32_t)kt * (BK / 2) : BUF_OOB);
+      buf_load16_lds(ra, st + q * 1024, sel_off(ka, a_base[i] + (uint32_t)kt * (BK / 2)));
       const bool kr = live && r_ok[i] && (int64_t)kt * BK + r_k[i] < Kred;
       uint32_t ro;
       if constexpr (!TRANS_B) ro = r_base[i] + (uint32_t)kt * (BK / 2);
       else ro = r_base[i] + (uint32_t)((int64_t)kt * BK * g.b_pitch);
-      buf_load16_lds(rr, st + TILE_BYTES + q * 1024, kr ? ro : BUF_OOB);
+      buf_load16_lds(rr, st + TILE_BYTES + q * 1024, sel_off(kr, ro));
     }
+  };
+
+  // ---- L2 prefetch of a later step: one 4-byte load per 128-byte line of both operand
+  // tiles (lane l of wave w touches row 64w + l), landing in a dummy LDS slot. Issued
+  // after a step's stage loads and allowed to stay in flight across the step's wait,
+  // it turns the stage loads of the step after into L2 hits.
+  lds_char* touch = smem + STAGES * STAGE_BYTES + SCALE_BYTES + wave * 256;
+  const int trow = wave * 64 + lane;
+  const bool ta_ok = m0 + trow < g.M;
+  const uint32_t ta_base = (uint32_t)((m0 + trow) * a_pitch);
+  uint32_t tr_base;
+  bool tr_ok;
+  if constexpr (!TRANS_B) {
+    tr_ok = n0 + trow < g.N;
+    tr_base = (uint32_t)((n0 + trow) * g.b_pitch);
+  } else {
+    tr_ok = n0 < g.N;
+    tr_base = (uint32_t)(trow * g.b_pitch + (n0 >> 1));
+  }
+  auto prefetch = [&](int kt) {
+    const bool live = kt < KT;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)touch, 4,
+                                             (int)sel_off(live && ta_ok, ta_base + (uint32_t)kt * (BK / 2)), 0, 0, 0);
+    uint32_t ro;
+    bool rk = live && tr_ok;
+    if constexpr (!TRANS_B) ro = tr_base + (uint32_t)kt * (BK / 2);
+    else {
+      ro = tr_base + (uint32_t)((int64_t)kt * BK * g.b_pitch);
+      rk = rk && (int64_t)kt * BK + trow < Kred;
+    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)touch, 4,
+                                             (int)sel_off(rk, ro), 0, 0, 0);
   };
 
   // ---- block scales for the whole reduction, staged once:
@@ -245,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   // Rows are padded to a multiple of 4 bytes (zeros) for 32-bit reads. The loads are
   // issued before the first stages' and written to LDS after them, so their latency
   // overlaps.
-  const int sp = (int)((nkb + 3) & ~3);
+  const int sp = (int)((nkb + 7) & ~7);  // a step reads 8 scale bytes (two words)
   lds_char* sSA = smem + STAGES * STAGE_BYTES;
   lds_char* sSR = sSA + SCALE_BYTES / 2;
   const int wpr = sp / 4;  // words per staged row
@@ -326,26 +360,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     const lds_char* st = stages + (kt % STAGES) * STAGE_BYTES;
     const lds_char* sX = st;
     const lds_char* sR = st + TILE_BYTES;
-    uint32_t xs[TJ], rs[TI];
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
-      xs[j] = *(const __attribute__((address_space(3))) uint32_t*)(sSA + (wm * 4 + j) * sp + kt * 4) >> (8 * half);
+    for (int s = 0; s < SUBSTEPS; ++s) {
+      // a 32-bit scale read gives two substeps' blocks; shifted by this lane's half,
+      // substep s's byte sits at position 2*(s%2) (op_sel)
+      uint32_t xs[TJ], rs[TI];
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
-      rs[i] = *(const __attribute__((address_space(3))) uint32_t*)(sSR + (wn * 4 + i) * sp + kt * 4) >> (8 * half);
+      for (int j = 0; j < TJ; ++j)
+        xs[j] = *(const __attribute__((address_space(3))) uint32_t*)(sSA + (wm * 4 + j) * sp + kt * (BK / 32) +
+                                                                     4 * (s >> 1)) >> (8 * half);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+      for (int i = 0; i < TI; ++i)
+        rs[i] = *(const __attribute__((address_space(3))) uint32_t*)(sSR + (wn * 4 + i) * sp + kt * (BK / 32) +
+                                                                     4 * (s >> 1)) >> (8 * half);
       v4i xf[TJ], rf[TI];
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int row = wm * 128 + 32 * j + (lane & 31);
-        xf[j] = lds_read_b128(sX + off64(row, 2 * s + half));
+        xf[j] = lds_read_b128(sX + off128(row, 2 * s + half));
       }
       if constexpr (!TRANS_B) {
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
           const int row = wn * 128 + 32 * i + (lane & 31);
-          rf[i] = lds_read_b128(sR + off64(row, 2 * s + half));
+          rf[i] = lds_read_b128(sR + off128(row, 2 * s + half));
         }
       } else {
         // output column c = wn*128 + 32i + (lane&31); reduction rows
@@ -367,66 +405,89 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-          if (s == 0) acc[i][j] = mfma_fp4<0, 0>(rf[i], xf[j], acc[i][j], rs[i], xs[j]);
+          if ((s & 1) == 0) acc[i][j] = mfma_fp4<0, 0>(rf[i], xf[j], acc[i][j], rs[i], xs[j]);
           else acc[i][j] = mfma_fp4<2, 2>(rf[i], xf[j], acc[i][j], rs[i], xs[j]);
         }
     }
   };
 
-  // ---------------------------------------------------------------- main loop
-  // Branch-free: past the last step the loads go to out-of-range offsets (zeros into a
-  // stage nobody reads), so every step waits with the same count: the two most recent
-  // steps' 2 x 8 loads may stay in flight.
-  issue_stage(0);
-  issue_stage(1);
-  issue_stage(2);
-  write_scales();
-  vm_barrier<16>();  // step 0 landed; the scale bytes are in LDS
-  for (int kt = 0; kt < KT; ++kt) {
-    issue_stage(kt + 3);
-    compute(kt);
-    // keep this step's MFMAs ahead of the wait: they run while later stages land
-    __builtin_amdgcn_sched_barrier(0);
-    vm_barrier<16>();
-  }
-  vm_barrier<0>();  // the last (out-of-range) stage loads write LDS too
-
-  // ---------------------------------------------------------------- up-projection
+  // ---------------------------------------------------------------- up-projection, part 1
   // acc += up * low^T on bf16 MFMA 32x32x16 (first operand the output-column side),
-  // `low` = XL (forward) or GB (backward), [M x rt] bf16.
+  // `low` = XL (forward) or GB (backward), [M x rt] bf16. Forward: up = [B | L2], row q
+  // (output column) = rt values read straight from memory, the first up_split from up0
+  // (row stride up0_ld), the rest from up1. The first 64 columns of the low-rank side
+  // run here, before the main loop: their loads are issued ahead of the first stage's
+  // (loads complete in order) and their MFMAs overlap that stage's latency.
   const int rt = g.rt;
   const bufres rl = make_buf(g.low, (uint64_t)g.M * rt * 2);
+  auto up_loads_fwd = [&](bufres rl_, bufres ru0, bufres ru1, int t0, v4i (&la)[4][TJ], v4i (&ub)[4][TI]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + 16 * u, j0 = t + 8 * half;
+      const bool live = t < rt;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int64_t row = m0 + wm * 128 + 32 * j + (lane & 31);
+        la[u][j] = buf_load16(rl_, sel_off(live, (uint32_t)((row * rt + j0) * 2)));
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int64_t q = n0 + wn * 128 + 32 * i + (lane & 31);
+        ub[u][i] = (live && t < g.up_split) ? buf_load16(ru0, (uint32_t)((q * g.up0_ld + j0) * 2))
+                                            : buf_load16(ru1, sel_off(live, (uint32_t)((q * g.up1_ld + j0 - g.up_split) * 2)));
+      }
+    }
+  };
+  auto up_mfma_fwd = [&](int t0, const v4i (&la)[4][TJ], const v4i (&ub)[4][TI]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (t0 + 16 * u >= rt) break;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(ub[u][i], la[u][j], acc[i][j]);
+    }
+  };
+  v4i la0[4][TJ], ub0[4][TI];
   if constexpr (!TRANS_B) {
-    // forward: up = [B | L2], row q (output column) = rt values read straight from
-    // memory: the first up_split from up0 (row stride up0_ld), the rest from up1.
+    if (rt > 0) {
+      const bufres ru0 = make_buf(g.up0, (uint64_t)g.N * g.up0_ld * 2);
+      const bufres ru1 = make_buf(g.up1, (uint64_t)g.N * g.up1_ld * 2);
+      up_loads_fwd(rl, ru0, ru1, 0, la0, ub0);
+    }
+  }
+  asm volatile("" ::: "memory");
+
+  // ---------------------------------------------------------------- main loop
+  // Branch-free: past the last step the loads go to out-of-range offsets (zeros into a
+  // stage nobody reads). Two stages: step kt+1's 64 KB land while step kt is multiplied.
+  issue_stage(0);
+  asm volatile("" ::: "memory");
+  prefetch(1);
+  if constexpr (!TRANS_B) {
+    if (rt > 0) up_mfma_fwd(0, la0, ub0);  // runs while step 0 lands
+  }
+  write_scales();
+  vm_barrier<TOUCHES>();  // step 0 landed (the prefetch may not have); scales in LDS
+  for (int kt = 0; kt < KT; ++kt) {
+    issue_stage(kt + 1);  // into the stage step kt-1 used: every wave left it at the barrier
+    asm volatile("" ::: "memory");
+    prefetch(kt + 2);
+    compute(kt);
+    // keep this step's MFMAs ahead of the wait: they run while the next stage lands
+    __builtin_amdgcn_sched_barrier(0);
+    vm_barrier<TOUCHES>();
+  }
+
+  // ---------------------------------------------------------------- up-projection, part 2
+  if constexpr (!TRANS_B) {
+    // forward, rt > 64: the remaining 64-wide slices (the first was done in the prologue)
     const bufres ru0 = make_buf(g.up0, (uint64_t)g.N * g.up0_ld * 2);
     const bufres ru1 = make_buf(g.up1, (uint64_t)g.N * g.up1_ld * 2);
-    for (int t0 = 0; t0 < rt; t0 += 64) {  // up to four 16-steps' operands in flight
+    for (int t0 = 64; t0 < rt; t0 += 64) {
       v4i la[4][TJ], ub[4][TI];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = t0 + 16 * u, j0 = t + 8 * half;
-        const bool live = t < rt;
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int64_t row = m0 + wm * 128 + 32 * j + (lane & 31);
-          la[u][j] = buf_load16(rl, live ? (uint32_t)((row * rt + j0) * 2) : BUF_OOB);
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int64_t q = n0 + wn * 128 + 32 * i + (lane & 31);
-          ub[u][i] = (live && t < g.up_split) ? buf_load16(ru0, (uint32_t)((q * g.up0_ld + j0) * 2))
-                                              : buf_load16(ru1, live ? (uint32_t)((q * g.up1_ld + j0 - g.up_split) * 2) : BUF_OOB);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (t0 + 16 * u >= rt) break;
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(ub[u][i], la[u][j], acc[i][j]);
-      }
+      up_loads_fwd(rl, ru0, ru1, t0, la, ub);
+      up_mfma_fwd(t0, la, ub);
     }
   } else {
     // backward: up = [A; L1] [rt x N] (row j = up0 row j for j < up_split, else up1 row
@@ -537,8 +598,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       const int r = 4 * k + (lane >> 4), c = (lane & 15) * 8;
       const v4i v = lds_read_b128(wbuf + r * OP + c * 2);
       const int64_t row = orow0 + r, col = ocol0 + c;
-      if (row < g.M && col < g.N)
-        *reinterpret_cast<v4i*>(reinterpret_cast<bf16_t*>(g.out) + row * g.ldo + col) = v;
+      if (row < g.M && col < g.N)  // streaming store: the output is not re-read here
+        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(reinterpret_cast<bf16_t*>(g.out) + row * g.ldo + col));
     }
     if constexpr (EPI == GEMM_EPI_GELU_Q) {
       // FC1 forward: H = GELU(P^) from the staged bf16 P^ (the stored values), then Q(H)
@@ -598,7 +659,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
         const v4i v = lds_read_b128(wbuf + r * OPF + c * 4);
         const int64_t row = orow0 + 64 * p + r, col = ocol0 + c;
         if (row < g.M && col < g.N)
-          *reinterpret_cast<v4i*>(reinterpret_cast<float*>(g.out) + row * g.ldo + col) = v;
+          __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(reinterpret_cast<float*>(g.out) + row * g.ldo + col));
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
