@@ -35,6 +35,8 @@
 // (first-operand index, second-operand index). The bf16 MFMA 32x32x16 has the same
 // accumulator layout, 8 bf16 per lane at reduction offset (l/32)*8.
 #include "common.h"
+#include <utility>
+
 #include "gemm.h"
 
 namespace ft {
@@ -50,7 +52,6 @@ constexpr int STAGES = 2;
 constexpr int SEGS = TILE_BYTES / 1024 / 4;    // 1 KB load segments per wave per tile (8)
 constexpr int SCALE_BYTES = 8192;              // LDS for the two operands' block scales
 constexpr int TOUCH_BYTES = 1024;              // landing slots of the L2 prefetch loads
-constexpr int LDS_BYTES = STAGES * STAGE_BYTES + SCALE_BYTES + TOUCH_BYTES;
 constexpr int TOUCHES = 2;                     // prefetch loads per wave per step
 constexpr int MAX_NKB = SCALE_BYTES / 2 / 8;   // 8 block rows per operand: Kred <= 16384
 constexpr int SW = 8 * MAX_NKB / 4 / 256;      // scale words staged per thread per operand (4)
@@ -83,18 +84,32 @@ __device__ __forceinline__ v16f mfma_fp4(v4i r, v4i x, v16f c, uint32_t sr, uint
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, SA, (int)sr, SB, (int)sx);
 }
 
+// substep s (0..3) of a step: op_sel picks byte s of both scale words
+__device__ __forceinline__ v16f mfma_fp4_sub(int s, v4i r, v4i x, v16f c, uint32_t sr, uint32_t sx) {
+  switch (s) {
+    case 0: return mfma_fp4<0, 0>(r, x, c, sr, sx);
+    case 1: return mfma_fp4<1, 1>(r, x, c, sr, sx);
+    case 2: return mfma_fp4<2, 2>(r, x, c, sr, sx);
+    default: return mfma_fp4<3, 3>(r, x, c, sr, sx);
+  }
+}
+
 __device__ __forceinline__ v16f mfma_bf16(v4i a, v4i b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding, then
-// meet the other waves. The memory clobber keeps the compiler from moving LDS accesses
-// across it; unlike __syncthreads() it does not drain loads that may stay in flight.
+// meet the other waves. The wait is the compiler's own s_waitcnt (encoded for gfx9:
+// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at "no wait"), so its counter
+// model knows the stage loads have landed and inserts no further wait for them before
+// the LDS reads; the barrier's memory clobber keeps LDS accesses from moving across.
+// Unlike __syncthreads() it does not drain loads that may stay in flight.
 template <int N>
 __device__ __forceinline__ void vm_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Four transposed 16x16-nibble reads (two output-column fragments) and the wait for
@@ -117,6 +132,29 @@ __device__ __forceinline__ void tr4_x4(const lds_char* p0, const lds_char* p1, c
   f1 = v4i{c.x, c.y, d.x, d.y};
 }
 
+
+// One transposed 16x16-nibble LDS read (ds_read_b64_tr_b4) as a builtin, so the
+// scheduler may place it among MFMAs.
+__device__ __forceinline__ v2i lds_tr4(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr4_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
+}
+
+// Scheduling pattern for NM MFMAs with NR LDS reads of the next substep: the reads go
+// in among the first NM/2 MFMAs, as evenly as the counts allow.
+template <int N>
+__device__ __forceinline__ void sched_ds_reads() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(0x100, N, 0);
+}
+template <int NR, int NM, int... K>
+__device__ __forceinline__ void sched_mix_impl(std::integer_sequence<int, K...>) {
+  constexpr int H = NM / 2;
+  ((__builtin_amdgcn_sched_group_barrier(0x008, 1, 0),
+    sched_ds_reads<(K < H ? NR * (K + 1) / H - NR * K / H : 0)>()), ...);
+}
+template <int NR, int NM>
+__device__ __forceinline__ void sched_mix() {
+  sched_mix_impl<NR, NM>(std::make_integer_sequence<int, NM>{});
+}
 
 // Workgroup -> output tile. Workgroups are dealt round-robin to the 8 XCDs; renumber
 // so each XCD gets a contiguous run of tiles, then walk tiles in bands of GROUP_M
@@ -168,8 +206,15 @@ __device__ __forceinline__ void quant_tile_store(const float (&v)[16], int lane,
 
 template <bool TRANS_B, bool OUT_BF16, int EPI>
 __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
-  __shared__ __align__(16) char smem_raw[LDS_BYTES];
-  lds_char* smem = (lds_char*)(smem_raw);
+  // Separate LDS objects per stage: the compiler then knows a transposed LDS read of one
+  // stage cannot alias the direct-to-LDS loads still filling the other, and does not
+  // drain those loads before the read.
+  __shared__ __align__(16) char st0_raw[STAGE_BYTES];
+  __shared__ __align__(16) char st1_raw[STAGE_BYTES];
+  __shared__ __align__(16) char scale_raw[SCALE_BYTES];
+  __shared__ __align__(16) char touch_raw[TOUCH_BYTES];
+  lds_char* const st0 = (lds_char*)st0_raw;
+  lds_char* const st1 = (lds_char*)st1_raw;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -223,9 +268,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       r_base[i] = (uint32_t)(row * g.b_pitch + (n0 >> 1) + c16 * 16);
     }
   }
-  lds_char* stages = smem;
-  auto issue_stage = [&](int kt) {
-    lds_char* st = stages + (kt % STAGES) * STAGE_BYTES;
+  auto issue_stage = [&](lds_char* st, int kt) {
     const bool live = kt < KT;
 #pragma unroll
     for (int i = 0; i < SEGS; ++i) {
@@ -244,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   // tiles (lane l of wave w touches row 64w + l), landing in a dummy LDS slot. Issued
   // after a step's stage loads and allowed to stay in flight across the step's wait,
   // it turns the stage loads of the step after into L2 hits.
-  lds_char* touch = smem + STAGES * STAGE_BYTES + SCALE_BYTES + wave * 256;
+  lds_char* touch = (lds_char*)touch_raw + wave * 256;
   const int trow = wave * 64 + lane;
   const bool ta_ok = m0 + trow < g.M;
   const uint32_t ta_base = (uint32_t)((m0 + trow) * a_pitch);
@@ -272,15 +315,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
                                              (int)sel_off(rk, ro), 0, 0, 0);
   };
 
-  // ---- block scales for the whole reduction, staged once:
-  //   sSA[j][kb]: activation row block j (0..7) of the tile, reduction block kb
-  //   sSR[i][kb]: R side, output block i (0..7) of the tile (the backward stores the
-  //               transposed scale matrix here, so both directions read alike)
-  // Rows are padded to a multiple of 4 bytes (zeros) for 32-bit reads. The loads are
-  // issued before the first stages' and written to LDS after them, so their latency
-  // overlaps.
+  // ---- block scales for the whole reduction, staged once, step-major: for step kt,
+  // lane half h and block row b (0..7) of the tile's operand, the word at
+  //   64*kt + 32*h + 4*b
+  // holds, in byte s, the scale of reduction block 8*kt + 2*s + h: exactly what lane
+  // half h needs in substep s (op_sel picks byte s). A wave reads its four block rows
+  // of a step with one 16-byte read per operand. The R side of the backward is the
+  // transposed scale matrix (block row b = output block). The loads are issued before
+  // the first stages' and written to LDS after them, so their latency overlaps.
   const int sp = (int)((nkb + 7) & ~7);  // a step reads 8 scale bytes (two words)
-  lds_char* sSA = smem + STAGES * STAGE_BYTES;
+  lds_char* sSA = (lds_char*)scale_raw;
   lds_char* sSR = sSA + SCALE_BYTES / 2;
   const int wpr = sp / 4;  // words per staged row
   uint32_t sa_w[SW], sr_w[SW], st_lo[2], st_hi[2];
@@ -326,13 +370,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       }
     }
   }
+  // reduction blocks 4kw .. 4kw+3 of block row b: bytes 0, 2 go to half 0 and bytes
+  // 1, 3 to half 1, each pair at substeps 2(kw%2), 2(kw%2)+1 of step kw/2
+  auto put_word = [&](lds_char* dst, int b, int kw, uint32_t w) {
+    const int o = 64 * (kw >> 1) + 4 * b + 2 * (kw & 1);
+    *(__attribute__((address_space(3))) uint16_t*)(dst + o) = (uint16_t)((w & 0xFFu) | ((w >> 8) & 0xFF00u));
+    *(__attribute__((address_space(3))) uint16_t*)(dst + o + 32) = (uint16_t)(((w >> 8) & 0xFFu) | ((w >> 16) & 0xFF00u));
+  };
   auto write_scales = [&]() {
 #pragma unroll
     for (int u = 0; u < SW; ++u) {
       const int e = tid + 256 * u, blk = e / max(wpr, 1), kw = e % max(wpr, 1);
       if (e < 8 * wpr) {
-        *(__attribute__((address_space(3))) uint32_t*)(sSA + blk * sp + 4 * kw) = sa_w[u];
-        if constexpr (!TRANS_B) *(__attribute__((address_space(3))) uint32_t*)(sSR + blk * sp + 4 * kw) = sr_w[u];
+        put_word(sSA, blk, kw, sa_w[u]);
+        if constexpr (!TRANS_B) put_word(sSR, blk, kw, sr_w[u]);
       }
     }
     if constexpr (TRANS_B) {
@@ -342,7 +393,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
         if (kb < sp) {  // rows kb in [nkb, sp) are the zero padding
 #pragma unroll
           for (int q = 0; q < 8; ++q)
-            sSR[q * sp + kb] = (char)(((q < 4 ? st_lo[u] : st_hi[u]) >> (8 * (q & 3))) & 0xFFu);
+            sSR[64 * (kb >> 3) + 32 * (kb & 1) + 4 * q + ((kb >> 1) & 3)] =
+                (char)(((q < 4 ? st_lo[u] : st_hi[u]) >> (8 * (q & 3))) & 0xFFu);
         }
       }
     }
@@ -354,60 +406,78 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) acc[i][j] = v16f{};
 
-  // ---- one reduction step of MFMAs. A 32-bit scale read gives the step's 4 reduction
-  // blocks; shifted by this lane's half, substep s's byte sits at position 2s (op_sel).
-  auto compute = [&](int kt) {
-    const lds_char* st = stages + (kt % STAGES) * STAGE_BYTES;
+  // ---- one reduction step of MFMAs, four 64-element substeps. Fragments are double-
+  // buffered in registers: substep s+1's LDS reads are issued between substep s's MFMAs
+  // (sched_group_barrier pins the interleave), so LDS latency hides behind the matrix
+  // pipe instead of stalling it once per fragment. A 32-bit scale read gives two
+  // substeps' blocks; shifted by this lane's half, substep s's byte sits at position
+  // 2*(s%2) (op_sel).
+  struct Frag {
+    v4i x[TJ], r[TI];
+  };
+  // backward: this lane's byte offset of fragment 0 within an R tile, for the
+  // transposed reads (row 32*half + (lane&15), unit 4wn, byte 8*(lane/16 % 2) of the
+  // unit). Kept opaque so each read's address stays one step from its stage: the
+  // compiler then knows which LDS object it reads and that in-flight loads into the
+  // other stage cannot alias it.
+  uint32_t frag_tr = 0;
+  if constexpr (TRANS_B) {
+    const int rb = 32 * half + (lane & 15);
+    frag_tr = (uint32_t)(rb * 128 + (((4 * wn) ^ swz8(rb)) << 4) + ((lane >> 4) & 1) * 8);
+    asm("" : "+v"(frag_tr));
+  }
+  auto load_frag = [&](const lds_char* st, int s, Frag& f) {
     const lds_char* sX = st;
     const lds_char* sR = st + TILE_BYTES;
 #pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int row = wm * 128 + 32 * j + (lane & 31);
+      f.x[j] = lds_read_b128(sX + off128(row, 2 * s + half));
+    }
+    if constexpr (!TRANS_B) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int row = wn * 128 + 32 * i + (lane & 31);
+        f.r[i] = lds_read_b128(sR + off128(row, 2 * s + half));
+      }
+    } else {
+      // output column c = wn*128 + 32i + (lane&31); reduction rows
+      // 64s + 32*half + 16h + (lane&15): two 16x16 nibble transposes per fragment.
+      // off128(64s + 16h + rb, unit) = off128(rb, unit) + 8192s + 2048h (swz8 ignores
+      // row bits 3 and up), and fragment i's unit is 4wn + i, so its offset is the
+      // lane's base with i XORed into the unit field.
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const uint32_t o = frag_tr ^ (uint32_t)(i << 4);
+        const v2i lo = lds_tr4(st + (TILE_BYTES + 8192 * s) + o);
+        const v2i hi = lds_tr4(st + (TILE_BYTES + 8192 * s + 2048) + o);
+        f.r[i] = v4i{lo.x, lo.y, hi.x, hi.y};
+      }
+    }
+  };
+  auto load_scales = [&](int kt, uint32_t (&xs)[TJ], uint32_t (&rs)[TI]) {
+    const v4i a = lds_read_b128(sSA + 64 * kt + 32 * half + 16 * wm);
+    const v4i r = lds_read_b128(sSR + 64 * kt + 32 * half + 16 * wn);
+    xs[0] = a.x, xs[1] = a.y, xs[2] = a.z, xs[3] = a.w;
+    rs[0] = r.x, rs[1] = r.y, rs[2] = r.z, rs[3] = r.w;
+  };
+  auto compute = [&](const lds_char* st, int kt) {
+    Frag f[2];
+    uint32_t xs[TJ], rs[TI];
+    load_scales(kt, xs, rs);
+    load_frag(st, 0, f[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 + TJ + TI * (TRANS_B ? 2 : 1), 0);
+#pragma unroll
     for (int s = 0; s < SUBSTEPS; ++s) {
-      // a 32-bit scale read gives two substeps' blocks; shifted by this lane's half,
-      // substep s's byte sits at position 2*(s%2) (op_sel)
-      uint32_t xs[TJ], rs[TI];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        xs[j] = *(const __attribute__((address_space(3))) uint32_t*)(sSA + (wm * 4 + j) * sp + kt * (BK / 32) +
-                                                                     4 * (s >> 1)) >> (8 * half);
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-        rs[i] = *(const __attribute__((address_space(3))) uint32_t*)(sSR + (wn * 4 + i) * sp + kt * (BK / 32) +
-                                                                     4 * (s >> 1)) >> (8 * half);
-      v4i xf[TJ], rf[TI];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int row = wm * 128 + 32 * j + (lane & 31);
-        xf[j] = lds_read_b128(sX + off128(row, 2 * s + half));
-      }
-      if constexpr (!TRANS_B) {
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int row = wn * 128 + 32 * i + (lane & 31);
-          rf[i] = lds_read_b128(sR + off128(row, 2 * s + half));
-        }
-      } else {
-        // output column c = wn*128 + 32i + (lane&31); reduction rows
-        // 64s + 32*half + 16h + (lane&15): two 16x16 nibble transposes per fragment
-        const int grp = lane >> 4;
-        const int rbase = 64 * s + 32 * (grp >> 1) + (lane & 15);
-        const lds_char* p[TI][2];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          const int c = wn * 128 + 32 * i + 16 * (grp & 1);
-          const int unit = c >> 5, sub8 = ((c >> 4) & 1) << 3;
-          p[i][0] = sR + off128(rbase, unit) + sub8;
-          p[i][1] = sR + off128(rbase + 16, unit) + sub8;
-        }
-        tr4_x4(p[0][0], p[0][1], p[1][0], p[1][1], rf[0], rf[1]);
-        tr4_x4(p[2][0], p[2][1], p[3][0], p[3][1], rf[2], rf[3]);
-      }
+      const Frag& c = f[s & 1];
+      if (s + 1 < SUBSTEPS) load_frag(st, s + 1, f[(s + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          if ((s & 1) == 0) acc[i][j] = mfma_fp4<0, 0>(rf[i], xf[j], acc[i][j], rs[i], xs[j]);
-          else acc[i][j] = mfma_fp4<2, 2>(rf[i], xf[j], acc[i][j], rs[i], xs[j]);
-        }
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_fp4_sub(s, c.r[i], c.x[j], acc[i][j], rs[i], xs[j]);
+      // schedule: the next substep's reads spread over the first half of this one's MFMAs
+      if (s + 1 < SUBSTEPS) sched_mix<TJ + TI * (TRANS_B ? 2 : 1), TI * TJ>();
+      else __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ, 0);
     }
   };
 
@@ -461,7 +531,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   // ---------------------------------------------------------------- main loop
   // Branch-free: past the last step the loads go to out-of-range offsets (zeros into a
   // stage nobody reads). Two stages: step kt+1's 64 KB land while step kt is multiplied.
-  issue_stage(0);
+  issue_stage(st0, 0);
   asm volatile("" ::: "memory");
   prefetch(1);
   if constexpr (!TRANS_B) {
@@ -469,14 +539,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   }
   write_scales();
   vm_barrier<TOUCHES>();  // step 0 landed (the prefetch may not have); scales in LDS
-  for (int kt = 0; kt < KT; ++kt) {
-    issue_stage(kt + 1);  // into the stage step kt-1 used: every wave left it at the barrier
+  // One step: step kt+1's loads go into the stage step kt-1 used (every wave left it at
+  // the last barrier), then step kt's MFMAs run while they land. Unrolled by two so each
+  // step names its stage statically.
+  auto step = [&](lds_char* cur, lds_char* nxt, int kt) {
+    issue_stage(nxt, kt + 1);
     asm volatile("" ::: "memory");
     prefetch(kt + 2);
-    compute(kt);
-    // keep this step's MFMAs ahead of the wait: they run while the next stage lands
     __builtin_amdgcn_sched_barrier(0);
+    compute(cur, kt);
+    __builtin_amdgcn_sched_barrier(0);  // the MFMAs stay ahead of the wait
     vm_barrier<TOUCHES>();
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(st0, st1, kt);
+    if (kt + 1 < KT) step(st1, st0, kt + 1);
   }
 
   // ---------------------------------------------------------------- up-projection, part 2
@@ -515,14 +592,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
         const v4i v = j < g.up_split
                           ? buf_load16(ru0, ok ? (uint32_t)(((int64_t)j * g.up0_ld + col) * 2) : BUF_OOB)
                           : buf_load16(ru1, ok ? (uint32_t)(((int64_t)(j - g.up_split) * g.up1_ld + col) * 2) : BUF_OOB);
-        lds_write_b128(smem + row * DP + c16 * 16, v);
+        lds_write_b128(st0 + row * DP + c16 * 16, v);
       }
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         v4i ub[TI];
 #pragma unroll
-        for (int i = 0; i < TI; ++i) ub[i] = lds_tr16_pair(smem, DP, 16 * u, wn * 128 + 32 * i, lane);
+        for (int i = 0; i < TI; ++i) ub[i] = lds_tr16_pair(st0, DP, 16 * u, wn * 128 + 32 * i, lane);
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -570,13 +647,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   }
 
   // ---------------------------------------------------------------- store
-  // Each wave stages its 128 x 128 result in LDS (the stages are free now), then 16
-  // consecutive lanes write 256 contiguous bytes of one output row per instruction.
-  // acc[i][j]: lane holds output row 32j + l%32 of the wave tile and, in registers
-  // 4g..4g+3, columns 32i + 8g + 4*half .. +4.
+  // Each wave stages its 128 x 128 result in 32 KB of LDS (half a stage; the stages
+  // are free now), then 16 consecutive lanes write 256 contiguous bytes of one output
+  // row per instruction. acc[i][j]: lane holds output row 32j + l%32 of the wave tile
+  // and, in registers 4g..4g+3, columns 32i + 8g + 4*half .. +4. Staged rows are
+  // 256 B (bf16) or 512 B (fp32, 64 rows per pass) with 16-byte units XOR-swizzled
+  // by the row, so column reads across rows and row reads across units both spread
+  // over the banks.
   __syncthreads();
-  lds_char* wbuf = smem + wave * 34816;  // 128 rows x 272 bytes (256 + 16 padding)
-  constexpr int OP = 272;
+  lds_char* wbuf = (wave < 2 ? st0 : st1) + (wave & 1) * 32768;
+  auto wofs = [](int r, int byte) { return r * 256 + ((((byte >> 4) ^ r) & 15) << 4) + (byte & 15); };
+  auto wofs_f = [](int r, int byte) { return r * 512 + ((((byte >> 4) ^ r) & 31) << 4) + (byte & 15); };
   const int64_t orow0 = m0 + wm * 128, ocol0 = n0 + wn * 128;
   if constexpr (OUT_BF16) {
 #pragma unroll
@@ -589,14 +670,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
           const v16f& a = acc[i][j];
           const v2i v = {(int)pack_bf16x2(a[4 * gq], a[4 * gq + 1]),
                          (int)pack_bf16x2(a[4 * gq + 2], a[4 * gq + 3])};
-          *(__attribute__((address_space(3))) v2i*)(wbuf + r * OP + (32 * i + 8 * gq + 4 * half) * 2) = v;
+          *(__attribute__((address_space(3))) v2i*)(wbuf + wofs(r, (32 * i + 8 * gq + 4 * half) * 2)) = v;
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
 #pragma unroll 4
     for (int k = 0; k < 32; ++k) {  // 4 rows x 256 bytes per instruction
       const int r = 4 * k + (lane >> 4), c = (lane & 15) * 8;
-      const v4i v = lds_read_b128(wbuf + r * OP + c * 2);
+      const v4i v = lds_read_b128(wbuf + wofs(r, c * 2));
       const int64_t row = orow0 + r, col = ocol0 + c;
       if (row < g.M && col < g.N)  // streaming store: the output is not re-read here
         __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(reinterpret_cast<bf16_t*>(g.out) + row * g.ldo + col));
@@ -611,8 +692,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       for (int t = 0; t < TI * TJ; ++t) {
         const int j = t >> 2, i = t & 3;
         const int lr = 32 * j + (lane & 31), lc = 32 * i + 16 * half;
-        const v4i a = lds_read_b128(wbuf + lr * OP + lc * 2);
-        const v4i b = lds_read_b128(wbuf + lr * OP + lc * 2 + 16);
+        const v4i a = lds_read_b128(wbuf + wofs(lr, lc * 2));
+        const v4i b = lds_read_b128(wbuf + wofs(lr, lc * 2 + 16));
         const uint32_t wd[8] = {(uint32_t)a.x, (uint32_t)a.y, (uint32_t)a.z, (uint32_t)a.w,
                                 (uint32_t)b.x, (uint32_t)b.y, (uint32_t)b.z, (uint32_t)b.w};
         float h[16];
@@ -636,7 +717,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     }
   } else {
     // fp32: two passes of 64 rows (64 x 512 bytes per wave)
-    constexpr int OPF = 528;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -648,7 +728,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
             const v16f& a = acc[i][j];
-            *(__attribute__((address_space(3))) v4f*)(wbuf + r * OPF + (32 * i + 8 * gq + 4 * half) * 4) =
+            *(__attribute__((address_space(3))) v4f*)(wbuf + wofs_f(r, (32 * i + 8 * gq + 4 * half) * 4)) =
                 v4f{a[4 * gq], a[4 * gq + 1], a[4 * gq + 2], a[4 * gq + 3]};
           }
       }
@@ -656,7 +736,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 #pragma unroll 4
       for (int k = 0; k < 32; ++k) {  // 2 rows x 512 bytes per instruction
         const int r = 2 * k + (lane >> 5), c = (lane & 31) * 4;
-        const v4i v = lds_read_b128(wbuf + r * OPF + c * 4);
+        const v4i v = lds_read_b128(wbuf + wofs_f(r, c * 4));
         const int64_t row = orow0 + 64 * p + r, col = ocol0 + c;
         if (row < g.M && col < g.N)
           __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(reinterpret_cast<float*>(g.out) + row * g.ldo + col));
