@@ -76,7 +76,7 @@ struct QuantDownArgs {
 };
 
 hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t stream);
-// The low-rank side is handled in ceil(r0/32) + ceil((rt-r0)/32) padded 32-wide tiles.
+// Bound on the low-rank width (in 32-wide units) that the fused kernels are built for.
 int quant_down_tiles(int r0, int rt);
 constexpr int QD_MAX_TILES = 4;
 int quant_down_splits(int64_t M, int64_t K, int rt);
