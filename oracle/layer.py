@@ -27,6 +27,12 @@ Precision contract (the points where the GPU rounds to bf16 because its low-rank
 products run on bf16 matrix units; the pages call bf16 LoRA "full precision"):
   Xh = bf16(X), XL = bf16(Xh D^T), Gh = bf16(G), GB = bf16(Gh U), Ph = bf16(pre),
   Hh = bf16(GELU(Ph)), dPh = bf16(dP). All products here are fp64.
+Decision precision of the fused epilogues (reading 10 of the design notes): the MLP's
+Q(H) and Q(dP) quantize values the GPU forms in fp32 inside a GEMM epilogue, so the
+code decisions here are taken on those values rounded to fp32 (H32 = fp32(GELU(Ph)),
+dP32 = fp32(dP)). This matters at ties: Ph is bf16, so GELU(Ph) = Ph in fp32 for
+Ph > ~5.3, and bf16 values such as 7 = 3.5 * 2 sit exactly on an E2M1 threshold,
+which fp64's GELU(7) = 7 - 3e-15 misses.
 ``Prec(quant=False)`` replaces Q by the identity and ``Prec(bf16=False)`` removes the
 bf16 roundings; with both off the layer is exactly linear, which the tests use for
 finite-difference checks.
@@ -132,25 +138,35 @@ def gelu_tanh_grad(p):
     return 0.5 * (1.0 + t) + 0.5 * p * (1.0 - t * t) * du
 
 
+def fp32(x):
+    """Round to fp32 (returned as fp64 values)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
 def mlp_forward(X, fc1: Linear, fc2: Linear, prec: Prec = EXACT, Hq=None):
-    """Returns dict(Y, XL1, P, H, HL2).
+    """Returns dict(Y, XL1, P, H, H32, HL2).
 
     pre = FC1(X); P = bf16(pre) (the saved tensor); H = GELU(P); Y = FC2(H), FC2's
-    4-bit operand being Q(H) and its low-rank input bf16(H). ``Hq`` optionally gives
-    deq Q(H) computed from the GPU's own H.
+    4-bit operand being Q(H32), H32 = fp32(H) (the epilogue's decision precision), and
+    its low-rank input bf16(H). ``Hq`` optionally gives deq Q(H) computed from the
+    GPU's own H.
     """
     pre, XL1 = linear_forward(X, fc1, prec)
     P = _b(pre, prec)
     H = gelu_tanh(P)
+    H32 = fp32(H)
+    if Hq is None and prec.quant:
+        Hq = mx4.fake_quant(H32)
     Y, HL2 = linear_forward(H, fc2, prec, Xq=Hq)
-    return dict(Y=Y, XL1=XL1, P=P, H=H, HL2=HL2)
+    return dict(Y=Y, XL1=XL1, P=P, H=H, H32=H32, HL2=HL2)
 
 
 def mlp_backward(dY, X, saved: dict, fc1: Linear, fc2: Linear, prec: Prec = EXACT,
                  dPq=None, H=None):
-    """Returns dict(dX, dA1, dB1, dA2, dB2, dH, dP).
+    """Returns dict(dX, dA1, dB1, dA2, dB2, dH, dP, dP32).
 
-    FC2 backward with G = dY and input H; dP = dH * GELU'(P); FC1 backward with G = dP.
+    FC2 backward with G = dY and input H; dP = dH * GELU'(P); FC1 backward with G = dP,
+    its 4-bit operand Q(dP32), dP32 = fp32(dP).
     ``dPq`` optionally gives deq Q(dP) computed from the GPU's own dP; ``H`` optionally
     overrides the recomputed GELU(P).
     """
@@ -158,6 +174,9 @@ def mlp_backward(dY, X, saved: dict, fc1: Linear, fc2: Linear, prec: Prec = EXAC
     Hv = gelu_tanh(P) if H is None else H
     dH, dA2, dB2, _ = linear_backward(dY, Hv, saved["HL2"], fc2, prec)
     dP = dH * gelu_tanh_grad(P)
+    dP32 = fp32(dP)
+    if dPq is None and prec.quant:
+        dPq = mx4.fake_quant(dP32)
     dX, dA1, dB1, _ = linear_backward(dP, X, saved["XL1"], fc1, prec, Gq=dPq)
-    return dict(dX=dX, dA1=dA1, dB1=dB1, dA2=dA2, dB2=dB2, dH=dH, dP=dP)
+    return dict(dX=dX, dA1=dA1, dB1=dB1, dA2=dA2, dB2=dB2, dH=dH, dP=dP, dP32=dP32)
 

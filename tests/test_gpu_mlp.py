@@ -4,9 +4,11 @@ Bars (see the module-level helpers):
 * P^ (saved FC1 output), XL1, HL2, Y, dX and the four LoRA gradients: relative
   Frobenius error <= 1e-3 against the fp64 oracle on the same seeded inputs.
 * Q(H) and Q(dP), the 4-bit operands the fused epilogues quantize from fp32 values the
-  GPU computes (GELU of P^, dH * GELU'(P^)): in general cases almost all scale bytes and
-  codes equal the oracle's and every difference is one grid step (the two sides
-  decide in different precisions near a threshold); deq Q(.) within 1e-3.
+  GPU computes (GELU of P^, dH * GELU'(P^)): the oracle decides on its values rounded
+  to fp32; in general cases almost all scale bytes and codes equal the oracle's and
+  every difference is one grid step (the fp32 accumulations of the two sides differ
+  near a threshold, where both codes are valid). Y and dX, which consume those codes,
+  are compared on the rows whose codes all equal the oracle's (at least half of them).
 * Exact-epilogue cases: with on-grid operands and no low-rank branches, FC1's output
   and dH are exact on both sides, so every code and scale byte must equal the
   oracle's except where the oracle's value lies within 2^-16 (relative) of a rounding
@@ -121,17 +123,33 @@ def check_quant_exact(got, T, name):
     assert np.all(step[flips] <= 1), f"{name}: a near-threshold code differs by more than one grid step"
 
 
+def rows_with_oracle_codes(got, T):
+    """Rows whose GPU codes and block scales all equal the oracle's Q(T). Where the two
+    sides' fp32-vs-fp64 values straddle a rounding threshold both codes are valid
+    (check_quant_close bounds how many and by how much); products that consume those
+    codes are unique only on the other rows, which is where they are compared."""
+    gc, gs, wc, ws_ = _codes_scales(got, T)
+    zero_both = ((gc & 7) == 0) & ((wc & 7) == 0)  # +0 and -0 are the same value
+    same = np.all((gc == wc) | zero_both, axis=1)
+    blk_same = np.all(gs == ws_, axis=1)
+    return same & np.repeat(blk_same, 32)[: gc.shape[0]]
+
+
 def _check_all(case, got, fwd, bwd):
+    h_ok = rows_with_oracle_codes(got["hq"], fwd["H32"])
+    p_ok = rows_with_oracle_codes(got["dpq"], bwd["dP32"])
+    log(f"  rows with every Q(H) code equal: {int(h_ok.sum())}/{h_ok.size}, Q(dP): {int(p_ok.sum())}/{p_ok.size}")
+    assert h_ok.mean() >= 0.5 and p_ok.mean() >= 0.5
     errs = {"P": rel_fro(got["P"], fwd["P"]),
             "XL1": rel_fro(got["XL1"], fwd["XL1"]), "HL2": rel_fro(got["HL2"], fwd["HL2"]),
-            "Y": rel_fro(got["Y"], fwd["Y"]), "dX": rel_fro(got["dX"], bwd["dX"])}
+            "Y": rel_fro(got["Y"][h_ok], fwd["Y"][h_ok]), "dX": rel_fro(got["dX"][p_ok], bwd["dX"][p_ok])}
     for k in ("dA1", "dB1", "dA2", "dB2"):
         errs[k] = rel_fro(got[k], bwd[k]) if bwd[k].size else 0.0
     log(f"  rel errors {errs}")
     for k, e in errs.items():
         assert e <= TOL, (k, e)
-    check_quant_close(got["hq"], fwd["H"], "Q(H)")
-    check_quant_close(got["dpq"], bwd["dP"], "Q(dP)")
+    check_quant_close(got["hq"], fwd["H32"], "Q(H)")
+    check_quant_close(got["dpq"], bwd["dP32"], "Q(dP)")
 
 
 MLP_CASES = [
@@ -193,8 +211,8 @@ def test_mlp_exact_epilogue_codes(m):
     got = _run(case)
     fwd, bwd = _oracle(case)
     assert np.array_equal(got["P"], fwd["P"]), "P^ must be exact here"
-    check_quant_exact(got["hq"], fwd["H"], "Q(H)")
-    check_quant_exact(got["dpq"], bwd["dP"], "Q(dP)")
+    check_quant_exact(got["hq"], fwd["H32"], "Q(H)")
+    check_quant_exact(got["dpq"], bwd["dP32"], "Q(dP)")
     # (Y and dX are not barred here: on-grid FC1 outputs put many GELU values within
     # an fp32 ulp of a rounding tie, where either adjacent code is correct)
 

@@ -201,3 +201,19 @@ def test_mlp_backward_finite_differences():
     np.testing.assert_allclose(g["dB1"], _fd(loss, fc1.B, 1e-6), **kw)
     np.testing.assert_allclose(g["dA2"], _fd(loss, fc2.A, 1e-6), **kw)
     np.testing.assert_allclose(g["dB2"], _fd(loss, fc2.B, 1e-6), **kw)
+
+
+def test_mlp_epilogue_decision_in_fp32():
+    """Q(H) is decided on fp32(GELU(P)). With P bf16, GELU(P) rounds to P in fp32 for
+    P above ~5.3, so an element P = 7 in a block whose maximum is 12 (scale 2) sits on
+    the 3 | 4 threshold (7 / 2 = 3.5) and rounds to the even code (4, i.e. 8.0); the
+    fp64 value GELU(7) = 7 - 3e-15 would fall just below it (3, i.e. 6.0)."""
+    P = np.zeros((32, 32))
+    P[0, 0], P[5, 7] = 12.0, 7.0
+    H = layer.gelu_tanh(P)
+    assert H[5, 7] < 7.0 and layer.fp32(H)[5, 7] == 7.0
+    assert mx4.fake_quant(layer.fp32(H))[5, 7] == 8.0
+    assert mx4.fake_quant(H)[5, 7] == 6.0
+    # the MLP's 4-bit operand is taken from the fp32 values
+    fwd_h32 = layer.fp32(H)
+    assert np.array_equal(mx4.fake_quant(fwd_h32), mx4.fake_quant(layer.fp32(layer.gelu_tanh(P))))
