@@ -102,18 +102,29 @@ def time_region(torch, fn, iters):
     return start.elapsed_time(end) / 1000.0
 
 
-def time_each(torch, fn, iters):
-    """Mean duration of fn(i), each bracketed by events on the current stream (the one
-    the library launches on)."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
+def time_graph(torch, fn, iters):
+    """Mean duration of fn(i) launched back to back from a captured HIP graph, timed by
+    events on the stream the graph replays on: no host call overhead between launches,
+    so the figure is the kernels' own time (the library allocates nothing and never
+    synchronizes, so its calls capture as they are)."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
     torch.cuda.synchronize()
-    for i in range(iters):
-        evs[i][0].record()
-        fn(i)
-        evs[i][1].record()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs])) / 1000.0
+    g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1000.0 / iters
 
 
 def traffic_for(m, n, k):
@@ -220,13 +231,19 @@ def main():
         return sets[i % len(sets)]
 
     it = max(args.steps, 10)
-    t_gf = time_each(torch, lambda i: abi.fourtune_gemm_fwd(S(i)["L"], S(i)["xq"], S(i)["xl"], S(i)["y"]), it)
-    t_gb = time_each(torch, lambda i: abi.fourtune_gemm_bwd(S(i)["L"], S(i)["gq"], S(i)["gb"], S(i)["dx"]), it)
-    t_fwd = time_each(torch, lambda i: abi.fourtune_linear_fwd(S(i)["L"], S(i)["x"], S(i)["y"], S(i)["xl"],
-                                                              S(i)["ws"]), it)
-    t_bwd = time_each(torch, lambda i: abi.fourtune_linear_bwd(S(i)["L"], S(i)["dy"], S(i)["x"], S(i)["xl"],
-                                                              S(i)["dx"], S(i)["da"], S(i)["db"], S(i)["ws"]), it)
-    t_q = time_each(torch, lambda i: abi.fourtune_quantize(S(i)["x"], S(i)["xq"]), it)
+    t_gf = time_graph(torch, lambda i: abi.fourtune_gemm_fwd(S(i)["L"], S(i)["xq"], S(i)["xl"], S(i)["y"]), it)
+    t_gb = time_graph(torch, lambda i: abi.fourtune_gemm_bwd(S(i)["L"], S(i)["gq"], S(i)["gb"], S(i)["dx"]), it)
+    t_fwd = time_graph(torch, lambda i: abi.fourtune_linear_fwd(S(i)["L"], S(i)["x"], S(i)["y"], S(i)["xl"],
+                                                               S(i)["ws"]), it)
+    t_bwd = time_graph(torch, lambda i: abi.fourtune_linear_bwd(S(i)["L"], S(i)["dy"], S(i)["x"], S(i)["xl"],
+                                                               S(i)["dx"], S(i)["da"], S(i)["db"], S(i)["ws"]), it)
+    t_q = time_graph(torch, lambda i: abi.fourtune_quantize(S(i)["x"], S(i)["xq"]), it)
+    # the forward's fused quantize + down-projection (and its partial sum) is the rest
+    # of the forward: Q(X) codes and scales, XL, one read of X
+    t_qd = max(t_fwd - t_gf, 1e-9)
+    qd_bytes = m * k * (4 if case["x_dtype"] == "fp32" else 2) + m * k / 2 + ((m + 31) // 32) * (k // 32) \
+        + m * (r + s) * 2
+    qd_gbps = qd_bytes / t_qd / 1e9
     gemm_flops = 2.0 * m * n * k
     tf_gf, tf_gb = gemm_flops / t_gf / 1e12, gemm_flops / t_gb / 1e12
     xbytes = 4 if case["x_dtype"] == "fp32" else 2
@@ -258,12 +275,14 @@ def main():
                      "traffic": traffic_for(m, n, k)},
         "kernels_us": {"gemm_fwd": round(t_gf * 1e6, 2), "gemm_bwd": round(t_gb * 1e6, 2),
                        "linear_fwd": round(t_fwd * 1e6, 2), "linear_bwd": round(t_bwd * 1e6, 2),
-                       "quantize_x": round(t_q * 1e6, 2)},
+                       "quantize_x": round(t_q * 1e6, 2), "fused_quant_down_fwd": round(t_qd * 1e6, 2)},
         "gemm_tflops": {"fwd": round(tf_gf, 1), "bwd": round(tf_gb, 1),
                         "fwd_bwd": round(2 * gemm_flops / (t_gf + t_gb) / 1e12, 1),
                         "frac_of_mxfp4_peak": round(2 * gemm_flops / (t_gf + t_gb) / 1e12 / PEAK_MXFP4_TFLOPS, 4)},
         "quantize_gbps": round(q_gbps, 1),
         "quantize_frac_of_hbm": round(q_gbps / PEAK_HBM_GBPS, 4),
+        "fused_quant_down_gbps": round(qd_gbps, 1),
+        "fused_quant_down_frac_of_hbm": round(qd_gbps / PEAK_HBM_GBPS, 4),
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
