@@ -268,10 +268,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       r_base[i] = (uint32_t)(row * g.b_pitch + (n0 >> 1) + c16 * 16);
     }
   }
-  auto issue_stage = [&](lds_char* st, int kt) {
+  auto issue_seg = [&](lds_char* st, int kt, int i) __attribute__((always_inline)) {
     const bool live = kt < KT;
-#pragma unroll
-    for (int i = 0; i < SEGS; ++i) {
+    {
       const int q = wave * SEGS + i;
       const bool ka = live && a_ok[i] && (int64_t)kt * BK + a_k[i] < Kred;
       buf_load16_lds(ra, st + q * 1024, sel_off(ka, a_base[i] + (uint32_t)kt * (BK / 2)));
@@ -281,6 +280,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       else ro = r_base[i] + (uint32_t)((int64_t)kt * BK * g.b_pitch);
       buf_load16_lds(rr, st + TILE_BYTES + q * 1024, sel_off(kr, ro));
     }
+  };
+  auto issue_stage = [&](lds_char* st, int kt) {
+#pragma unroll
+    for (int i = 0; i < SEGS; ++i) issue_seg(st, kt, i);
   };
 
   // ---- L2 prefetch of a later step: one 4-byte load per 128-byte line of both operand
@@ -426,7 +429,22 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     frag_tr = (uint32_t)(rb * 128 + (((4 * wn) ^ swz8(rb)) << 4) + ((lane >> 4) & 1) * 8);
     asm("" : "+v"(frag_tr));
   }
-  auto load_frag = [&](const lds_char* st, int s, Frag& f) {
+  auto load_x = [&](const lds_char* st, int s, int j) __attribute__((always_inline)) -> v4i {
+    const int row = wm * 128 + 32 * j + (lane & 31);
+    return lds_read_b128(st + off128(row, 2 * s + half));
+  };
+  auto load_r = [&](const lds_char* st, int s, int i) __attribute__((always_inline)) -> v4i {
+    if constexpr (!TRANS_B) {
+      const int row = wn * 128 + 32 * i + (lane & 31);
+      return lds_read_b128(st + TILE_BYTES + off128(row, 2 * s + half));
+    } else {
+      const uint32_t o = frag_tr ^ (uint32_t)(i << 4);
+      const v2i lo = lds_tr4(st + (TILE_BYTES + 8192 * s) + o);
+      const v2i hi = lds_tr4(st + (TILE_BYTES + 8192 * s + 2048) + o);
+      return v4i{lo.x, lo.y, hi.x, hi.y};
+    }
+  };
+  auto load_frag = [&](const lds_char* st, int s, Frag& f) __attribute__((always_inline)) {
     const lds_char* sX = st;
     const lds_char* sR = st + TILE_BYTES;
 #pragma unroll
@@ -461,25 +479,41 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     xs[0] = a.x, xs[1] = a.y, xs[2] = a.z, xs[3] = a.w;
     rs[0] = r.x, rs[1] = r.y, rs[2] = r.z, rs[3] = r.w;
   };
-  auto compute = [&](const lds_char* st, int kt) {
+  // One step in 16 scheduling regions of 4 MFMAs (one R fragment against the four
+  // activation fragments). Region (s, q) also issues the LDS reads of fragments q of
+  // substep s+1 and, in the first two substeps, one 1 KB segment of each operand of
+  // step kt+1's stage: the direct-to-LDS loads then go out between MFMAs instead of
+  // all at once ahead of them (a wave stalls at issue while the load queue is full,
+  // and could not start its MFMAs until its last load was accepted).
+  auto compute = [&](const lds_char* st, int kt, lds_char* nxt) __attribute__((always_inline)) {
     Frag f[2];
     uint32_t xs[TJ], rs[TI];
     load_scales(kt, xs, rs);
     load_frag(st, 0, f[0]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 + TJ + TI * (TRANS_B ? 2 : 1), 0);
 #pragma unroll
     for (int s = 0; s < SUBSTEPS; ++s) {
       const Frag& c = f[s & 1];
-      if (s + 1 < SUBSTEPS) load_frag(st, s + 1, f[(s + 1) & 1]);
+      Frag& nf = f[(s + 1) & 1];
 #pragma unroll
-      for (int i = 0; i < TI; ++i)
+      for (int q = 0; q < TI; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        // the region's loads first (in program order: the empty asm statements that
+        // pin the MFMAs also fence the scheduler), then its four MFMAs
+        if (s < 2) issue_seg(nxt, kt + 1, TI * s + q);
+        if (s + 1 < SUBSTEPS) {
+          nf.x[q] = load_x(st, s + 1, q);
+          nf.r[q] = load_r(st, s + 1, q);
+        }
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_fp4_sub(s, c.r[i], c.x[j], acc[i][j], rs[i], xs[j]);
-      // schedule: the next substep's reads spread over the first half of this one's MFMAs
-      if (s + 1 < SUBSTEPS) sched_mix<TJ + TI * (TRANS_B ? 2 : 1), TI * TJ>();
-      else __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ, 0);
+        for (int j = 0; j < TJ; ++j) {
+          acc[q][j] = mfma_fp4_sub(s, c.r[q], c.x[j], acc[q][j], rs[q], xs[j]);
+          asm volatile("" : "+a"(acc[q][j]));  // keeps the MFMA in this region (no sinking)
+        }
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
+
 
   // ---------------------------------------------------------------- up-projection, part 1
   // acc += up * low^T on bf16 MFMA 32x32x16 (first operand the output-column side),
@@ -542,13 +576,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   // One step: step kt+1's loads go into the stage step kt-1 used (every wave left it at
   // the last barrier), then step kt's MFMAs run while they land. Unrolled by two so each
   // step names its stage statically.
-  auto step = [&](lds_char* cur, lds_char* nxt, int kt) {
-    issue_stage(nxt, kt + 1);
+  auto step = [&](lds_char* cur, lds_char* nxt, int kt) __attribute__((always_inline)) {
+    compute(cur, kt, nxt);  // also issues step kt+1's stage loads into nxt
     asm volatile("" ::: "memory");
-    prefetch(kt + 2);
+    prefetch(kt + 2);       // the last two loads before the wait: they may stay in flight
     __builtin_amdgcn_sched_barrier(0);
-    compute(cur, kt);
-    __builtin_amdgcn_sched_barrier(0);  // the MFMAs stay ahead of the wait
     vm_barrier<TOUCHES>();
   };
   for (int kt = 0; kt < KT; kt += 2) {
