@@ -17,13 +17,14 @@
 //
 // Tiling. A workgroup of 4 waves computes a 256 x 256 output tile, each wave a
 // 128 x 128 quarter as 4 x 4 tiles of V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP4 x FP4,
-// one E8M0 scale per lane = per 32 reduction elements). The reduction advances 128
-// elements per step. Each step's two code tiles (16 KB each) are brought into one of
-// four LDS stages by direct-to-LDS buffer loads issued three steps ahead, so the
-// memory latency of a step hides behind three steps of MFMAs. The block scales of the
-// workgroup's rows and columns for the whole reduction are staged into LDS once, before
-// the main loop. LDS rows are XOR-swizzled in 16-byte units so fragment reads hit
-// distinct banks.
+// one E8M0 scale per lane = per 32 reduction elements). The reduction advances 256
+// elements per step. A step's two code tiles (32 KB each, 128-byte rows: whole cache
+// lines) land in one of two LDS stages by direct-to-LDS buffer loads issued during the
+// step before, one 1 KB segment per scheduling region so the loads go out between
+// MFMAs; a 4-byte touch per line pulls the step after that into L2. The block scales
+// of the workgroup's rows and columns for the whole reduction are staged into LDS
+// once, before the main loop. Each stage is its own LDS object, so the compiler knows
+// which loads a fragment read can alias.
 //
 // Operand order. The MFMA's first operand is the Q(R) side (output columns), the second
 // the activation side (output rows): a lane's accumulator registers 4g..4g+3 then hold
@@ -48,7 +49,6 @@ constexpr int TI = 4, TJ = 4;                  // 32x32 MFMA tiles per wave: R s
 constexpr int SUBSTEPS = BK / 64;              // MFMA reduction substeps per step
 constexpr int TILE_BYTES = 256 * BK / 2;       // 32 KB of codes per operand tile per step
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // activation tile + R tile
-constexpr int STAGES = 2;
 constexpr int SEGS = TILE_BYTES / 1024 / 4;    // 1 KB load segments per wave per tile (8)
 constexpr int SCALE_BYTES = 8192;              // LDS for the two operands' block scales
 constexpr int TOUCH_BYTES = 1024;              // landing slots of the L2 prefetch loads
@@ -64,15 +64,9 @@ __device__ __forceinline__ void lds_write_b128(lds_char* p, v4i v) {
   *reinterpret_cast<__attribute__((address_space(3))) v4i*>(p) = v;
 }
 
-// Activation / forward-R tiles have 64-byte rows (four 16-byte units); unit c of row
-// r is stored at unit c ^ swz4(r). swz4 is distinct over the four rows of either
-// parity among 8 consecutive rows and over rows r, r+4, r+8, r+12, so 16-byte reads of
-// one logical unit by consecutive rows meet distinct banks whether LDS serves 8 or 16
-// lanes per cycle.
-__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int off64(int row, int c16) { return row * 64 + ((c16 ^ swz4(row)) << 4); }
-// Backward-R tiles have 128-byte rows (eight units); swz8 is distinct over each parity
-// class of 16 consecutive rows, as the 16-lane transposed reads need.
+// Stage tiles have 128-byte rows (eight 16-byte units); unit c of row r is stored at
+// unit c ^ swz8(r). swz8 is distinct over each parity class of 16 consecutive rows, so
+// the 32-row fragment reads and the 16-lane transposed reads meet distinct banks.
 __device__ __forceinline__ int swz8(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
 __device__ __forceinline__ int off128(int row, int c16) { return row * 128 + ((c16 ^ swz8(row)) << 4); }
 
@@ -112,25 +106,6 @@ __device__ __forceinline__ void vm_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// Four transposed 16x16-nibble reads (two output-column fragments) and the wait for
-// them in one block: the LDS-bound loads still in flight write other stages, and
-// issuing the reads here keeps the compiler from draining those loads first.
-__device__ __forceinline__ void tr4_x4(const lds_char* p0, const lds_char* p1, const lds_char* p2,
-                                       const lds_char* p3, v4i& f0, v4i& f1) {
-  v2i a, b, c, d;
-  asm volatile(
-      "ds_read_b64_tr_b4 %0, %4\n\t"
-      "ds_read_b64_tr_b4 %1, %5\n\t"
-      "ds_read_b64_tr_b4 %2, %6\n\t"
-      "ds_read_b64_tr_b4 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
-      : "v"((uint32_t)(uintptr_t)p0), "v"((uint32_t)(uintptr_t)p1), "v"((uint32_t)(uintptr_t)p2),
-        "v"((uint32_t)(uintptr_t)p3)
-      : "memory");
-  f0 = v4i{a.x, a.y, b.x, b.y};
-  f1 = v4i{c.x, c.y, d.x, d.y};
-}
 
 
 // One transposed 16x16-nibble LDS read (ds_read_b64_tr_b4) as a builtin, so the
@@ -380,10 +355,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   }
   // reduction blocks 4kw .. 4kw+3 of block row b: bytes 0, 2 go to half 0 and bytes
   // 1, 3 to half 1, each pair at substeps 2(kw%2), 2(kw%2)+1 of step kw/2
+  // The staging stores are written from inline asm: they run while stage 0 and the
+  // first prefetch are in flight, and the compiler, seeing plain LDS stores there,
+  // would wait for every load in flight first (the prefetch included). Their
+  // completion is awaited by the lgkmcnt wait before the barrier that follows.
   auto put_word = [&](lds_char* dst, int b, int kw, uint32_t w) {
-    const int o = 64 * (kw >> 1) + 4 * b + 2 * (kw & 1);
-    *(__attribute__((address_space(3))) uint16_t*)(dst + o) = (uint16_t)((w & 0xFFu) | ((w >> 8) & 0xFF00u));
-    *(__attribute__((address_space(3))) uint16_t*)(dst + o + 32) = (uint16_t)(((w >> 8) & 0xFFu) | ((w >> 16) & 0xFF00u));
+    const uint32_t o = (uint32_t)(uintptr_t)(dst + 64 * (kw >> 1) + 4 * b + 2 * (kw & 1));
+    const uint32_t lo = (w & 0xFFu) | ((w >> 8) & 0xFF00u), hi = ((w >> 8) & 0xFFu) | ((w >> 16) & 0xFF00u);
+    asm volatile("ds_write_b16 %0, %1\n\tds_write_b16 %0, %2 offset:32" ::"v"(o), "v"(lo), "v"(hi) : "memory");
   };
   auto write_scales = [&]() {
 #pragma unroll
@@ -400,9 +379,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
         const int kb = tid + 256 * u;
         if (kb < sp) {  // rows kb in [nkb, sp) are the zero padding
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            sSR[64 * (kb >> 3) + 32 * (kb & 1) + 4 * q + ((kb >> 1) & 3)] =
-                (char)(((q < 4 ? st_lo[u] : st_hi[u]) >> (8 * (q & 3))) & 0xFFu);
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t o = (uint32_t)(uintptr_t)(sSR + 64 * (kb >> 3) + 32 * (kb & 1) + 4 * q + ((kb >> 1) & 3));
+            const uint32_t v = ((q < 4 ? st_lo[u] : st_hi[u]) >> (8 * (q & 3))) & 0xFFu;
+            asm volatile("ds_write_b8 %0, %1" ::"v"(o), "v"(v) : "memory");
+          }
         }
       }
     }
@@ -560,11 +541,57 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     }
   };
   v4i la0[4][TJ], ub0[4][TI];
+  // backward: the first 64 low-rank rows go through two 32-row slabs of [A; L1] staged
+  // in stage 1 (free until the main loop's first step refills it) by direct-to-LDS
+  // loads issued ahead of stage 0's; GB values in la0
+  constexpr int DP = BN * 2 + 32;  // slab row pitch (bytes) of the epilogue's slabs
+  constexpr int DP1 = BN * 2;      // prologue slab pitch: one load instruction fills 2 rows
+  const int rt1 = rt < 64 ? rt : 64;
+  auto slab_dma = [&](int jc, int i) __attribute__((always_inline)) {
+    const bufres ru0 = make_buf(g.up0, (uint64_t)g.up_split * g.up0_ld * 2);
+    const bufres ru1 = make_buf(g.up1, (uint64_t)(rt - g.up_split) * g.up1_ld * 2);
+    const int r0 = 2 * wave + 8 * i;              // this wave's two rows (uniform)
+    const bool first = jc + r0 < g.up_split;      // up_split is even: both rows agree
+    const int j = jc + r0 + (lane >> 5);
+    const int64_t col = n0 + 8 * (lane & 31);
+    const bool ok = col < g.N && j < rt;
+    const uint32_t off = first ? (uint32_t)(((int64_t)j * g.up0_ld + col) * 2)
+                               : (uint32_t)(((int64_t)(j - g.up_split) * g.up1_ld + col) * 2);
+    buf_load16_lds(first ? ru0 : ru1, st1 + (jc / 32) * 32 * DP1 + r0 * DP1, sel_off(ok, off));
+  };
+  auto slab_unit = [&](int jc, int i) __attribute__((always_inline)) -> v4i {
+    const bufres ru0 = make_buf(g.up0, (uint64_t)g.up_split * g.up0_ld * 2);
+    const bufres ru1 = make_buf(g.up1, (uint64_t)(rt - g.up_split) * g.up1_ld * 2);
+    const int c = tid + 256 * i, row = c >> 5, c16 = c & 31;
+    const int j = jc + row;
+    const int64_t col = n0 + 8 * c16;
+    const bool ok = col < g.N && j < rt;
+    // both sources are read (the other one at an out-of-range offset, which returns
+    // zeros), so the row's source is a select, not a branch around each load
+    const bool first = j < g.up_split;
+    return buf_load16(ru0, sel_off(ok && first, (uint32_t)(((int64_t)j * g.up0_ld + col) * 2))) |
+           buf_load16(ru1, sel_off(ok && !first, (uint32_t)(((int64_t)(j - g.up_split) * g.up1_ld + col) * 2)));
+  };
   if constexpr (!TRANS_B) {
     if (rt > 0) {
       const bufres ru0 = make_buf(g.up0, (uint64_t)g.N * g.up0_ld * 2);
       const bufres ru1 = make_buf(g.up1, (uint64_t)g.N * g.up1_ld * 2);
       up_loads_fwd(rl, ru0, ru1, 0, la0, ub0);
+    }
+  } else {
+    if (rt > 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)  // low-rank columns 16u + 8*half .. +8 (u < rt1/16)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int64_t row = m0 + wm * 128 + 32 * j + (lane & 31);
+          la0[u][j] = buf_load16(rl, sel_off(16 * u < rt1, (uint32_t)((row * rt + 16 * u + 8 * half) * 2)));
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        slab_dma(0, i);
+        slab_dma(32, i);  // rows past rt load zeros
+      }
     }
   }
   asm volatile("" ::: "memory");
@@ -577,8 +604,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   prefetch(1);
   if constexpr (!TRANS_B) {
     if (rt > 0) up_mfma_fwd(0, la0, ub0);  // runs while step 0 lands
+  } else {
+    if (rt > 0) {  // runs while step 0 lands
+      // the slabs landed (they were issued ahead of stage 0's loads and the prefetch)
+      vm_barrier<2 * SEGS + TOUCHES>();
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // branch-free: past rt the slab and la0 are zeros
+        v4i ub[TI];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          // lds_tr16_pair's lane pattern, addresses one step from the stage object so
+          // the compiler sees which LDS object they read
+          const int gq = lane >> 4, sq = lane & 15;
+          const int col = wn * 128 + 32 * i + 16 * (gq & 1) + 4 * (sq & 3);
+          const int m = 32 * (u >> 1) + 16 * (u & 1) + 8 * (gq >> 1) + (sq >> 2);
+          const int o = m * DP1 + col * 2;
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(st1 + o));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(st1 + (o + 4 * DP1)));
+          ub[i] = v4i{(int)(((uint32_t)(uint16_t)lo.x) | ((uint32_t)(uint16_t)lo.y << 16)),
+                      (int)(((uint32_t)(uint16_t)lo.z) | ((uint32_t)(uint16_t)lo.w << 16)),
+                      (int)(((uint32_t)(uint16_t)hi.x) | ((uint32_t)(uint16_t)hi.y << 16)),
+                      (int)(((uint32_t)(uint16_t)hi.z) | ((uint32_t)(uint16_t)hi.w << 16))};
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(ub[i], la0[u][j], acc[i][j]);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slab reads done before stage 1 is refilled
+    }
   }
   write_scales();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the staging stores are done
   vm_barrier<TOUCHES>();  // step 0 landed (the prefetch may not have); scales in LDS
   // One step: step kt+1's loads go into the stage step kt-1 used (every wave left it at
   // the last barrier), then step kt's MFMAs run while they land. Unrolled by two so each
@@ -606,14 +664,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       up_mfma_fwd(t0, la, ub);
     }
   } else {
-    // backward: up = [A; L1] [rt x N] (row j = up0 row j for j < up_split, else up1 row
-    // j - up_split; row strides up*_ld). The MFMA wants 8 consecutive j per output
-    // column, so 32-row slabs of the tile's 256 columns are staged in LDS (free after
-    // the main loop) and read transposed with ds_read_b64_tr_b16.
-    constexpr int DP = BN * 2 + 32;  // slab row pitch (bytes), padded against bank conflicts
-    const bufres ru0 = make_buf(g.up0, (uint64_t)g.up_split * g.up0_ld * 2);
-    const bufres ru1 = make_buf(g.up1, (uint64_t)(rt - g.up_split) * g.up1_ld * 2);
-    for (int jc = 0; jc < rt; jc += 32) {
+    // backward, rt > 64: the remaining 32-row slabs of up = [A; L1] [rt x N] (row j =
+    // up0 row j for j < up_split, else up1 row j - up_split; the first 64 were done in
+    // the prologue). The MFMA wants 8 consecutive j per output column, so each slab of
+    // the tile's 256 columns is staged in LDS (free after the main loop) and read
+    // transposed with ds_read_b64_tr_b16.
+    for (int jc = 64; jc < rt; jc += 32) {
       v4i la[2][TJ];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -623,16 +679,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
           la[u][j] = buf_load16(rl, (uint32_t)((row * rt + jc + 16 * u + 8 * half) * 2));
         }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, row = c >> 5, c16 = c & 31;
-        const int j = jc + row;
-        const int64_t col = n0 + 8 * c16;
-        const bool ok = col < g.N;
-        const v4i v = j < g.up_split
-                          ? buf_load16(ru0, ok ? (uint32_t)(((int64_t)j * g.up0_ld + col) * 2) : BUF_OOB)
-                          : buf_load16(ru1, ok ? (uint32_t)(((int64_t)(j - g.up_split) * g.up1_ld + col) * 2) : BUF_OOB);
-        lds_write_b128(st0 + row * DP + c16 * 16, v);
-      }
+      for (int i = 0; i < 4; ++i)
+        lds_write_b128(st0 + (i * 8 + (tid >> 5)) * DP + (tid & 31) * 16, slab_unit(jc, i));
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
