@@ -572,12 +572,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     return buf_load16(ru0, sel_off(ok && first, (uint32_t)(((int64_t)j * g.up0_ld + col) * 2))) |
            buf_load16(ru1, sel_off(ok && !first, (uint32_t)(((int64_t)(j - g.up_split) * g.up1_ld + col) * 2)));
   };
+  // ---------------------------------------------------------------- main loop
+  // Branch-free: past the last step the loads go to out-of-range offsets (zeros into a
+  // stage nobody reads). Two stages: step kt+1's 64 KB land while step kt is multiplied.
+  // Prologue. Forward: the first 64 low-rank columns' operands go out ahead of stage 0
+  // and their MFMAs run while it lands. Backward: stage 0 first, then the operands
+  // (GB values and the [A; L1] slabs, which land with it), one wait for all, then the
+  // MFMAs. (Each order measured faster for its direction.)
   if constexpr (!TRANS_B) {
     if (rt > 0) {
       const bufres ru0 = make_buf(g.up0, (uint64_t)g.N * g.up0_ld * 2);
       const bufres ru1 = make_buf(g.up1, (uint64_t)g.N * g.up1_ld * 2);
       up_loads_fwd(rl, ru0, ru1, 0, la0, ub0);
     }
+  }
+  asm volatile("" ::: "memory");
+  issue_stage(st0, 0);
+  asm volatile("" ::: "memory");
+  if constexpr (!TRANS_B) {
+    if (rt > 0) up_mfma_fwd(0, la0, ub0);  // runs while stage 0 lands
   } else {
     if (rt > 0) {
 #pragma unroll
@@ -594,20 +607,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       }
     }
   }
-  asm volatile("" ::: "memory");
-
-  // ---------------------------------------------------------------- main loop
-  // Branch-free: past the last step the loads go to out-of-range offsets (zeros into a
-  // stage nobody reads). Two stages: step kt+1's 64 KB land while step kt is multiplied.
-  issue_stage(st0, 0);
-  asm volatile("" ::: "memory");
-  prefetch(1);
-  if constexpr (!TRANS_B) {
-    if (rt > 0) up_mfma_fwd(0, la0, ub0);  // runs while step 0 lands
-  } else {
-    if (rt > 0) {  // runs while step 0 lands
-      // the slabs landed (they were issued ahead of stage 0's loads and the prefetch)
-      vm_barrier<2 * SEGS + TOUCHES>();
+  write_scales();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the staging stores are done
+  vm_barrier<0>();  // step 0, the low-rank operands and the slabs landed; scales in LDS
+  if constexpr (TRANS_B) {
+    if (rt > 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {  // branch-free: past rt the slab and la0 are zeros
         v4i ub[TI];
@@ -632,12 +636,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(ub[i], la0[u][j], acc[i][j]);
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slab reads done before stage 1 is refilled
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // slab reads done before stage 1 is refilled
     }
   }
-  write_scales();
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the staging stores are done
-  vm_barrier<TOUCHES>();  // step 0 landed (the prefetch may not have); scales in LDS
+  // (after the slab reads: the compiler would make them wait for this load)
+  prefetch(1);
   // One step: step kt+1's loads go into the stage step kt-1 used (every wave left it at
   // the last barrier), then step kt's MFMAs run while they land. Unrolled by two so each
   // step names its stage statically.
