@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
     python bench.py --calibrate-copy     (a plain 512 MiB device copy, for counter scaling)
+    python bench.py --ablation           (fusion ablation; one JSON line of its own)
 
 One step = the whole hot path once over one batch: the layer's forward (fused
 quantize + down-projection, 4-bit GEMM + up-projection) and backward (fused quantize +
@@ -47,6 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="fusion ablation: bf16 LoRA, unfused and fused W4A4G4 at c2 (linear), c3 (MLP)")
     return ap.parse_args()
 
 
@@ -151,6 +154,164 @@ def calibrate_copy():
     return 0
 
 
+# --------------------------------------------------------------------------- fusion ablation
+def _torch_lora_linear(torch, case, dev="cuda"):
+    """Standard bf16 LoRA linear (frozen W, adapter A, B; no stabilizer, nothing
+    quantized): the baseline the pages compare against. Right-hand operands are kept
+    contiguous; only left operands are transposed views."""
+    bf = torch.bfloat16
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(bf)
+
+    W = d(case["R"].astype(np.float32) + case["L2"].astype(np.float32) @ case["L1"].astype(np.float32))
+    A, B = d(case["A"]), d(case["B"])
+    return dict(W=W, Wt=W.t().contiguous(), A=A, At=A.t().contiguous(), B=B, Bt=B.t().contiguous())
+
+
+def _lora_fwd(torch, p, x):
+    xa = torch.mm(x, p["At"])
+    return torch.mm(x, p["Wt"]) + torch.mm(xa, p["Bt"]), xa
+
+
+def _lora_bwd(torch, p, dy, x, xa):
+    gb = torch.mm(dy, p["B"])
+    dx = torch.mm(dy, p["W"]) + torch.mm(gb, p["A"])
+    da = torch.mm(gb.t(), x)
+    db = torch.mm(dy.t(), xa)
+    return dx, da, db
+
+
+def ablation(args):
+    """Layer-level reproduction of the structure of the pages' fusion breakdown (FourTune
+    §4, Figure 9): the same W4A4G4 layer unfused (every step a launch, intermediates in
+    HBM), with LoRA fusion only, fully fused; and a standard bf16 LoRA layer. Times are
+    per fwd+bwd, from HIP graph replays (kernel time) and from plain back-to-back calls
+    bracketed by events (what a caller sees, launch overheads included)."""
+    import torch
+    import torch.nn.functional as F
+    from bit_quantized_lora_fp4_amd import abi
+    from synth import workloads as wl
+
+    abi.lib()
+    it = max(args.steps, 10)
+    res = {}
+
+    def both(fn, n_sets):
+        for i in range(args.warmup):
+            fn(i % n_sets)
+        torch.cuda.synchronize()
+        eager = time_region(torch, lambda i: fn(i % n_sets), it) / it
+        return dict(graph_ms=round(1e3 * time_graph(torch, lambda i: fn(i % n_sets), it), 4),
+                    eager_ms=round(1e3 * eager, 4))
+
+    # ---- one linear, c2
+    log("[ablation] c2 linear")
+    case = wl.linear_case("c2")
+    m, k = case["X"].shape
+    n = case["R"].shape[0]
+    sets = build_sets(case, 2, torch, abi)
+    for s in sets:
+        s["ws_ab"] = abi.workspace(abi.fourtune_ablation_workspace_bytes(m, s["L"]))
+        s["lora"] = _torch_lora_linear(torch, case)
+        s["xa"] = torch.empty((m, s["L"].rank), dtype=torch.bfloat16, device="cuda")
+
+    def lin_fused(i):
+        step(abi, sets[i])
+
+    def lin_unfused(i):
+        s = sets[i]
+        abi.fourtune_linear_fwd_unfused(s["L"], s["x"], s["y"], s["xl"], s["ws_ab"])
+        abi.fourtune_linear_bwd_unfused(s["L"], s["dy"], s["x"], s["xl"], s["dx"], s["da"], s["db"], s["ws_ab"])
+
+    def lin_bf16(i):
+        s = sets[i]
+        y, xa = _lora_fwd(torch, s["lora"], s["x"])
+        _lora_bwd(torch, s["lora"], s["dy"], s["x"], xa)
+
+    lin = dict(bf16_lora=both(lin_bf16, 2), w4_unfused=both(lin_unfused, 2), w4_fused=both(lin_fused, 2))
+    for key in ("graph_ms", "eager_ms"):
+        lin[f"lora_fusion_speedup_{key[:-3]}"] = round(lin["w4_unfused"][key] / lin["w4_fused"][key], 3)
+        lin[f"fused_vs_bf16_lora_{key[:-3]}"] = round(lin["bf16_lora"][key] / lin["w4_fused"][key], 3)
+    lin["shape"] = dict(m=m, n=n, k=k, lora_rank=case["A"].shape[0], stab_rank=case["L1"].shape[0])
+    res["linear_c2"] = lin
+    del sets
+    torch.cuda.empty_cache()
+
+    # ---- the MLP pair, c3
+    log("[ablation] c3 MLP")
+    mc = wl.mlp_case("c3")
+    m, dm = mc["X"].shape
+    f = mc["fc1"]["R"].shape[0]
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+
+    def dv(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(
+            torch.bfloat16 if dt == "bf16" else torch.float32)
+
+    msets = []
+    for i in range(2):
+        p1, p2 = mc["fc1"], mc["fc2"]
+        fc1 = abi.make_linear(dv(p1["R"], "fp32"), dv(p1["A"], "bf16"), dv(p1["B"], "bf16"), dv(p1["L1"], "bf16"),
+                              dv(p1["L2"], "bf16"))
+        fc2 = abi.make_linear(dv(p2["R"], "fp32"), dv(p2["A"], "bf16"), dv(p2["B"], "bf16"), dv(p2["L1"], "bf16"),
+                              dv(p2["L2"], "bf16"))
+        rt1, rt2 = fc1.rank + fc1.stab_rank, fc2.rank + fc2.stab_rank
+        s = dict(fc1=fc1, fc2=fc2, x=dv(mc["X"], mc["x_dtype"]), dy=dv(mc["dY"], mc["dy_dtype"]),
+                 y=torch.empty((m, dm), **bf), dx=torch.empty((m, dm), **bf),
+                 xl1=torch.empty((m, rt1), **bf), pre=torch.empty((m, f), **bf), h=torch.empty((m, f), **bf),
+                 hl2=torch.empty((m, rt2), **bf),
+                 g=[torch.empty((fc1.rank, dm), **f32), torch.empty((f, fc1.rank), **f32),
+                    torch.empty((fc2.rank, f), **f32), torch.empty((dm, fc2.rank), **f32)],
+                 ws=abi.workspace(abi.fourtune_mlp_workspace_bytes(m, fc1, fc2)),
+                 ws_ab=abi.workspace(abi.fourtune_ablation_workspace_bytes(m, fc1, fc2)),
+                 l1=_torch_lora_linear(torch, p1), l2=_torch_lora_linear(torch, p2))
+        msets.append(s)
+    torch.cuda.synchronize()
+
+    def mlp_level(lf):
+        def fn(i):
+            s = msets[i]
+            abi.fourtune_mlp_fwd_unfused(s["fc1"], s["fc2"], lf, s["x"], s["y"], s["xl1"], s["pre"], s["h"],
+                                         s["hl2"], s["ws_ab"])
+            abi.fourtune_mlp_bwd_unfused(s["fc1"], s["fc2"], lf, s["dy"], s["x"], s["xl1"], s["pre"], s["h"],
+                                         s["hl2"], s["dx"], *s["g"], s["ws_ab"])
+        return fn
+
+    def mlp_fused(i):
+        s = msets[i]
+        abi.fourtune_mlp_fwd(s["fc1"], s["fc2"], s["x"], s["y"], s["xl1"], s["pre"], s["hl2"], s["ws"])
+        abi.fourtune_mlp_bwd(s["fc1"], s["fc2"], s["dy"], s["x"], s["xl1"], s["pre"], s["hl2"], s["dx"], *s["g"],
+                             s["ws"])
+
+    def mlp_bf16(i):
+        s = msets[i]
+        p, xa1 = _lora_fwd(torch, s["l1"], s["x"])
+        h = F.gelu(p, approximate="tanh")
+        y, xa2 = _lora_fwd(torch, s["l2"], h)
+        dh, _, _ = _lora_bwd(torch, s["l2"], s["dy"], h, xa2)
+        dp = torch.ops.aten.gelu_backward(dh, p, approximate="tanh")
+        _lora_bwd(torch, s["l1"], dp, s["x"], xa1)
+
+    mlp = dict(bf16_lora=both(mlp_bf16, 2), w4_unfused=both(mlp_level(False), 2),
+               w4_lora_fused=both(mlp_level(True), 2), w4_all_fused=both(mlp_fused, 2))
+    for key in ("graph_ms", "eager_ms"):
+        tag = key[:-3]
+        mlp[f"lora_fusion_speedup_{tag}"] = round(mlp["w4_unfused"][key] / mlp["w4_lora_fused"][key], 3)
+        mlp[f"mlp_fusion_speedup_{tag}"] = round(mlp["w4_lora_fused"][key] / mlp["w4_all_fused"][key], 3)
+        mlp[f"all_fused_vs_bf16_lora_{tag}"] = round(mlp["bf16_lora"][key] / mlp["w4_all_fused"][key], 3)
+    mlp["shape"] = dict(m=m, d=dm, f=f, lora_rank=mc["fc1"]["A"].shape[0], stab_rank=mc["fc1"]["L1"].shape[0])
+    res["mlp_c3"] = mlp
+    out = {"metric": "fusion ablation: fwd+bwd time per variant (FourTune Fig. 9 structure)", "unit": "ms",
+           "higher_is_better": False, "n_gpus": 1, "iters": it, "data": "synthetic",
+           "pages_for_context": {"lora_fusion_speedup": 1.82, "mlp_fusion_speedup": 1.10,
+                                 "all_fused_vs_bf16_lora": 2.52},
+           **res}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------------------- CPU side
 def cpu_baseline(case, seconds):
     """The oracle as it stands, fwd+bwd on a row sample of the same layer."""
@@ -194,6 +355,8 @@ def main():
         return 2
     if args.calibrate_copy:
         return calibrate_copy()
+    if args.ablation:
+        return ablation(args)
     import torch
     from bit_quantized_lora_fp4_amd import abi
     from synth import workloads as wl

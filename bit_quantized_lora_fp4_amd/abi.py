@@ -71,6 +71,23 @@ _SIGS = {
                                         ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_i64,
                                         c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_vp,
                                         ctypes.POINTER(FtMx4), c_vp, c_sz, c_vp]),
+    "fourtune_ablation_workspace_bytes": (c_sz, [c_i64, ctypes.POINTER(FtLinear),
+                                                 ctypes.POINTER(FtLinear)]),
+    "fourtune_linear_fwd_unfused": (ctypes.c_int, [ctypes.POINTER(FtLinear), c_vp, ctypes.c_int,
+                                                   c_i64, c_vp, ctypes.c_int, c_vp, c_vp, c_sz,
+                                                   c_vp]),
+    "fourtune_linear_bwd_unfused": (ctypes.c_int, [ctypes.POINTER(FtLinear), c_vp, ctypes.c_int,
+                                                   c_vp, ctypes.c_int, c_vp, c_i64, c_vp,
+                                                   ctypes.c_int, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "fourtune_mlp_fwd_unfused": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear),
+                                                ctypes.c_int, c_vp, ctypes.c_int, c_i64, c_vp,
+                                                ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                                c_vp]),
+    "fourtune_mlp_bwd_unfused": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear),
+                                                ctypes.c_int, c_vp, ctypes.c_int, c_vp,
+                                                ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp,
+                                                ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                                                c_vp]),
     "fourtune_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fourtune_last_error": (ctypes.c_char_p, []),
 }
@@ -260,6 +277,56 @@ def fourtune_mlp_bwd(fc1: Linear, fc2: Linear, dy: torch.Tensor, x: torch.Tensor
                                   x.shape[0], _ptr(dx), _dt(dx), _ptr(d_a1), _ptr(d_b1),
                                   _ptr(d_a2), _ptr(d_b2), ctypes.byref(dq) if dq is not None else None,
                                   _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def fourtune_ablation_workspace_bytes(m: int, fc1: Linear, fc2: Optional[Linear] = None) -> int:
+    s1 = fc1.struct()
+    s2 = fc2.struct() if fc2 is not None else None
+    return lib().fourtune_ablation_workspace_bytes(m, ctypes.byref(s1),
+                                                   ctypes.byref(s2) if s2 is not None else None)
+
+
+def fourtune_linear_fwd_unfused(L: Linear, x: torch.Tensor, y: torch.Tensor,
+                                xl_saved: torch.Tensor, ws: torch.Tensor, stream=None):
+    s = L.struct()
+    _check(lib().fourtune_linear_fwd_unfused(ctypes.byref(s), _ptr(x), _dt(x), x.shape[0], _ptr(y),
+                                             _dt(y), _ptr(xl_saved), _ptr(ws), ws.numel(),
+                                             _stream(stream)))
+
+
+def fourtune_linear_bwd_unfused(L: Linear, dy: torch.Tensor, x: torch.Tensor,
+                                xl_saved: torch.Tensor, dx: torch.Tensor,
+                                d_lora_a: Optional[torch.Tensor], d_lora_b: Optional[torch.Tensor],
+                                ws: torch.Tensor, stream=None):
+    s = L.struct()
+    _check(lib().fourtune_linear_bwd_unfused(ctypes.byref(s), _ptr(dy), _dt(dy), _ptr(x), _dt(x),
+                                             _ptr(xl_saved), x.shape[0], _ptr(dx), _dt(dx),
+                                             _ptr(d_lora_a), _ptr(d_lora_b), _ptr(ws), ws.numel(),
+                                             _stream(stream)))
+
+
+def fourtune_mlp_fwd_unfused(fc1: Linear, fc2: Linear, lora_fused: bool, x: torch.Tensor,
+                             y: torch.Tensor, xl1_saved: torch.Tensor, pre_saved: torch.Tensor,
+                             h_saved: torch.Tensor, hl2_saved: torch.Tensor, ws: torch.Tensor,
+                             stream=None):
+    s1, s2 = fc1.struct(), fc2.struct()
+    _check(lib().fourtune_mlp_fwd_unfused(ctypes.byref(s1), ctypes.byref(s2), int(bool(lora_fused)),
+                                          _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y),
+                                          _ptr(xl1_saved), _ptr(pre_saved), _ptr(h_saved),
+                                          _ptr(hl2_saved), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def fourtune_mlp_bwd_unfused(fc1: Linear, fc2: Linear, lora_fused: bool, dy: torch.Tensor,
+                             x: torch.Tensor, xl1_saved: torch.Tensor, pre_saved: torch.Tensor,
+                             h_saved: torch.Tensor, hl2_saved: torch.Tensor, dx: torch.Tensor,
+                             d_a1, d_b1, d_a2, d_b2, ws: torch.Tensor, stream=None):
+    s1, s2 = fc1.struct(), fc2.struct()
+    _check(lib().fourtune_mlp_bwd_unfused(ctypes.byref(s1), ctypes.byref(s2), int(bool(lora_fused)),
+                                          _ptr(dy), _dt(dy), _ptr(x), _dt(x), _ptr(xl1_saved),
+                                          _ptr(pre_saved), _ptr(h_saved), _ptr(hl2_saved),
+                                          x.shape[0], _ptr(dx), _dt(dx), _ptr(d_a1), _ptr(d_b1),
+                                          _ptr(d_a2), _ptr(d_b2), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
 
 
 def fourtune_status_string(status: int) -> str:

@@ -590,3 +590,215 @@ ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const voi
 }
 
 }  // extern "C"
+
+// ================================================================ fusion ablation
+// The same layer computed with the fusions taken apart (FourTune §4, "Kernel Fusion
+// Breakdown"): each step a launch of its own, its intermediates stored in HBM as bf16.
+namespace {
+
+// The linear without its low-rank branches: the 4-bit backbone alone.
+ft_linear backbone_only(const ft_linear* L) {
+  ft_linear b = *L;
+  b.rank = 0;
+  b.stab_rank = 0;
+  b.lora_a = b.lora_b = b.stab_down = b.stab_up = nullptr;
+  return b;
+}
+
+// out = base + low [B | L2]^T (forward) or base + low [A; L1] (backward)
+ft_status run_up_add(const ft_linear* L, bool bwd, const void* base, const void* low, int64_t m, void* out,
+                     ft_dtype out_dt, hipStream_t st, const char* what) {
+  ft::UpAddArgs u{};
+  u.base = static_cast<const ft::bf16_t*>(base);
+  u.low = static_cast<const ft::bf16_t*>(low);
+  u.v0 = static_cast<const ft::bf16_t*>(bwd ? L->lora_a : L->lora_b);
+  u.v1 = static_cast<const ft::bf16_t*>(bwd ? L->stab_down : L->stab_up);
+  u.M = m;
+  u.C = bwd ? L->k : L->n;
+  u.rt = (int)(L->rank + L->stab_rank);
+  u.r0 = (int)L->rank;
+  u.out = out;
+  return hip_check(ft::launch_up_add(u, bwd, out_dt == FT_BF16, st), what);
+}
+
+struct UnfusedLayout {
+  uint8_t* q_codes;    // Q(X) or Q(dY)
+  uint8_t* q_scales;
+  ft::bf16_t* low;     // GB (backward)
+  ft::bf16_t* stored;  // the 4-bit product before the up-projection, bf16
+  float* partials;
+  size_t bytes;
+};
+
+UnfusedLayout unfused_layout(void* ws, int64_t m, const ft_linear* L, bool bwd) {
+  Carver c(ws);
+  UnfusedLayout u{};
+  const int64_t rt = L->rank + L->stab_rank;
+  const int64_t qcols = bwd ? L->n : L->k, ocols = bwd ? L->k : L->n;
+  u.q_codes = c.take<uint8_t>(ft_mx4_codes_bytes(m, qcols));
+  u.q_scales = c.take<uint8_t>(ft_mx4_scales_bytes(m, qcols));
+  if (bwd) u.low = c.take<ft::bf16_t>((size_t)m * rt * 2);
+  if (rt > 0) u.stored = c.take<ft::bf16_t>((size_t)m * ocols * 2);
+  size_t p = qd_partials(m, qcols, L);
+  if (bwd) p = std::max(p, lg_partials(m, L));
+  u.partials = c.take<float>(p);
+  u.bytes = c.used;
+  return u;
+}
+
+size_t linear_ablation_bytes(int64_t m, const ft_linear* L) {
+  size_t b = fourtune_linear_workspace_bytes(m, L);
+  b = std::max(b, unfused_layout(nullptr, m, L, false).bytes);
+  b = std::max(b, unfused_layout(nullptr, m, L, true).bytes);
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fourtune_ablation_workspace_bytes(int64_t m, const ft_linear* fc1, const ft_linear* fc2) {
+  if (fc1 == nullptr || m < 0) return 0;
+  size_t b = linear_ablation_bytes(m, fc1);
+  if (fc2 == nullptr) return b;
+  b = std::max(b, linear_ablation_bytes(m, fc2));
+  return 2 * round_up((size_t)m * fc1->n * 2, 256) + b;
+}
+
+ft_status fourtune_linear_fwd_unfused(const ft_linear* L, const void* x, ft_dtype x_dt, int64_t m, void* y,
+                                      ft_dtype y_dt, void* xl_saved, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "linear_fwd_unfused";
+  TRY(check_linear(L, who));
+  REQUIRE(dtype_ok(x_dt) && dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m == 0) return ok();
+  TRY(check_m(m, L, who));
+  REQUIRE(m < (int64_t)65535 * 32, FT_ERR_UNSUPPORTED, "%s: m=%lld too large", who, (long long)m);
+  const int64_t rt = L->rank + L->stab_rank;
+  TRY(check_tensor(x, who, "x"));
+  TRY(check_tensor(y, who, "y"));
+  if (rt > 0) TRY(check_tensor(xl_saved, who, "xl_saved"));
+  const UnfusedLayout lay = unfused_layout(ws, m, L, false);
+  REQUIRE(ws != nullptr && ws_bytes >= lay.bytes, FT_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
+          ws_bytes, lay.bytes);
+  REQUIRE(aligned16(ws), FT_ERR_ALIGN, "%s: workspace misaligned", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ft_linear bb = backbone_only(L);
+  TRY(hip_check(ft::launch_quantize(x, x_dt == FT_BF16, m, L->k, L->k, lay.q_codes, lay.q_scales, st),
+                "linear_fwd_unfused quantize"));
+  if (rt == 0) {
+    TRY(run_gemm_fwd(&bb, lay.q_codes, lay.q_scales, nullptr, m, y, y_dt, st));
+    return ok();
+  }
+  TRY(run_quant_down(ft::QD_DOWN, L, true, x, x_dt == FT_BF16, m, L->k, nullptr, nullptr, xl_saved, lay.partials, st,
+                     "linear_fwd_unfused down"));
+  TRY(run_gemm_fwd(&bb, lay.q_codes, lay.q_scales, nullptr, m, lay.stored, FT_BF16, st));
+  TRY(run_up_add(L, false, lay.stored, xl_saved, m, y, y_dt, st, "linear_fwd_unfused up_add"));
+  return ok();
+}
+
+ft_status fourtune_linear_bwd_unfused(const ft_linear* L, const void* dy, ft_dtype dy_dt, const void* x,
+                                      ft_dtype x_dt, const void* xl_saved, int64_t m, void* dx, ft_dtype dx_dt,
+                                      float* d_lora_a, float* d_lora_b, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "linear_bwd_unfused";
+  TRY(check_linear(L, who));
+  REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m == 0) return ok();
+  TRY(check_m(m, L, who));
+  REQUIRE(m < (int64_t)65535 * 32, FT_ERR_UNSUPPORTED, "%s: m=%lld too large", who, (long long)m);
+  const int64_t rt = L->rank + L->stab_rank;
+  TRY(check_tensor(dy, who, "dy"));
+  TRY(check_tensor(dx, who, "dx"));
+  if (L->rank > 0) {
+    TRY(check_tensor(x, who, "x"));
+    TRY(check_tensor(xl_saved, who, "xl_saved"));
+    TRY(check_tensor(d_lora_a, who, "d_lora_a"));
+    TRY(check_tensor(d_lora_b, who, "d_lora_b"));
+  }
+  const UnfusedLayout lay = unfused_layout(ws, m, L, true);
+  REQUIRE(ws != nullptr && ws_bytes >= lay.bytes, FT_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
+          ws_bytes, lay.bytes);
+  REQUIRE(aligned16(ws), FT_ERR_ALIGN, "%s: workspace misaligned", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const ft_linear bb = backbone_only(L);
+  TRY(hip_check(ft::launch_quantize(dy, dy_dt == FT_BF16, m, L->n, L->n, lay.q_codes, lay.q_scales, st),
+                "linear_bwd_unfused quantize"));
+  if (rt == 0) {
+    TRY(run_gemm_bwd(&bb, lay.q_codes, lay.q_scales, nullptr, m, dx, dx_dt, st));
+    return ok();
+  }
+  TRY(run_quant_down(ft::QD_DOWN, L, false, dy, dy_dt == FT_BF16, m, L->n, nullptr, nullptr, lay.low, lay.partials,
+                     st, "linear_bwd_unfused down"));
+  TRY(run_gemm_bwd(&bb, lay.q_codes, lay.q_scales, nullptr, m, lay.stored, FT_BF16, st));
+  TRY(run_up_add(L, true, lay.stored, lay.low, m, dx, dx_dt, st, "linear_bwd_unfused up_add"));
+  TRY(run_lora_grad(L, m, lay.low, x, x_dt == FT_BF16, false, xl_saved, dy, dy_dt == FT_BF16, d_lora_a, d_lora_b,
+                    lay.partials, st, "linear_bwd_unfused lora_grad"));
+  return ok();
+}
+
+ft_status fourtune_mlp_fwd_unfused(const ft_linear* fc1, const ft_linear* fc2, int lora_fused, const void* x,
+                                   ft_dtype x_dt, int64_t m, void* y, ft_dtype y_dt, void* xl1_saved,
+                                   void* pre_saved, void* h_saved, void* hl2_saved, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  const char* who = "mlp_fwd_unfused";
+  TRY(check_mlp(fc1, fc2, m, who));
+  if (m == 0) return ok();
+  TRY(check_tensor(pre_saved, who, "pre_saved"));
+  TRY(check_tensor(h_saved, who, "h_saved"));
+  if (lora_fused) {
+    TRY(fourtune_linear_fwd(fc1, x, x_dt, m, pre_saved, FT_BF16, xl1_saved, nullptr, ws, ws_bytes, stream));
+  } else {
+    TRY(fourtune_linear_fwd_unfused(fc1, x, x_dt, m, pre_saved, FT_BF16, xl1_saved, ws, ws_bytes, stream));
+  }
+  TRY(hip_check(ft::launch_gelu(static_cast<const ft::bf16_t*>(pre_saved), static_cast<ft::bf16_t*>(h_saved),
+                                m * fc1->n, static_cast<hipStream_t>(stream)),
+                "mlp_fwd_unfused gelu"));
+  if (lora_fused) {
+    TRY(fourtune_linear_fwd(fc2, h_saved, FT_BF16, m, y, y_dt, hl2_saved, nullptr, ws, ws_bytes, stream));
+  } else {
+    TRY(fourtune_linear_fwd_unfused(fc2, h_saved, FT_BF16, m, y, y_dt, hl2_saved, ws, ws_bytes, stream));
+  }
+  return ok();
+}
+
+ft_status fourtune_mlp_bwd_unfused(const ft_linear* fc1, const ft_linear* fc2, int lora_fused, const void* dy,
+                                   ft_dtype dy_dt, const void* x, ft_dtype x_dt, const void* xl1_saved,
+                                   const void* pre_saved, const void* h_saved, const void* hl2_saved, int64_t m,
+                                   void* dx, ft_dtype dx_dt, float* d_a1, float* d_b1, float* d_a2, float* d_b2,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "mlp_bwd_unfused";
+  TRY(check_mlp(fc1, fc2, m, who));
+  if (m == 0) return ok();
+  TRY(check_tensor(pre_saved, who, "pre_saved"));
+  TRY(check_tensor(h_saved, who, "h_saved"));
+  REQUIRE(ws != nullptr && aligned16(ws), FT_ERR_WORKSPACE, "%s: workspace missing or misaligned", who);
+  const size_t inter = round_up((size_t)m * fc1->n * 2, 256);
+  REQUIRE(ws_bytes >= 2 * inter, FT_ERR_WORKSPACE, "%s: workspace of %zu bytes, more than %zu needed", who,
+          ws_bytes, 2 * inter);
+  Carver c(ws);
+  ft::bf16_t* dh = c.take<ft::bf16_t>(inter);
+  ft::bf16_t* dp = c.take<ft::bf16_t>(inter);
+  void* rest = static_cast<char*>(ws) + c.used;
+  const size_t rest_bytes = ws_bytes - c.used;
+  if (lora_fused) {
+    TRY(fourtune_linear_bwd(fc2, dy, dy_dt, h_saved, FT_BF16, hl2_saved, m, dh, FT_BF16, d_a2, d_b2, nullptr, rest,
+                            rest_bytes, stream));
+  } else {
+    TRY(fourtune_linear_bwd_unfused(fc2, dy, dy_dt, h_saved, FT_BF16, hl2_saved, m, dh, FT_BF16, d_a2, d_b2, rest,
+                                    rest_bytes, stream));
+  }
+  TRY(hip_check(ft::launch_gelu_bwd(static_cast<const ft::bf16_t*>(pre_saved), dh, dp, m * fc1->n,
+                                    static_cast<hipStream_t>(stream)),
+                "mlp_bwd_unfused gelu_bwd"));
+  if (lora_fused) {
+    TRY(fourtune_linear_bwd(fc1, dp, FT_BF16, x, x_dt, xl1_saved, m, dx, dx_dt, d_a1, d_b1, nullptr, rest,
+                            rest_bytes, stream));
+  } else {
+    TRY(fourtune_linear_bwd_unfused(fc1, dp, FT_BF16, x, x_dt, xl1_saved, m, dx, dx_dt, d_a1, d_b1, rest, rest_bytes,
+                                    stream));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -58,7 +58,7 @@ constexpr int64_t GEMM_MAX_KRED = 16384;
 // needs quant_down_partial_bytes(M, K, r0, rt) bytes of fp32 partials, which a second
 // kernel sums in a fixed order.
 // mode: QD_QUANT (as above); QD_GELU_DOWN: no quantization, the down-projection reads
-// bf16(GELU(x)) (x = the saved P^, bf16); QD_DOWN: no quantization (x bf16).
+// bf16(GELU(x)) (x = the saved P^, bf16); QD_DOWN: no quantization.
 enum { QD_QUANT = 0, QD_GELU_DOWN = 1, QD_DOWN = 2 };
 struct QuantDownArgs {
   int mode;
@@ -114,6 +114,25 @@ struct LoraGradArgs {
 };
 
 hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream);
+
+// Unfused pieces for the fusion ablation (the fused path never uses them):
+//   out[M x C] = base[M x C] (bf16) + low[M x rt] * V, fp32 accumulation, one rounding
+//   forward : V = U^T, U row q = v0[q*r0 .. +r0] ++ v1[q*(rt-r0) .. +(rt-r0)] ([B | L2])
+//   backward: V = D,   D row j = v0 row j (j < r0) or v1 row j - r0, row stride C ([A; L1])
+// rt a multiple of 32 up to 128, r0 a multiple of 16, C a multiple of 8.
+struct UpAddArgs {
+  const bf16_t* base;
+  const bf16_t* low;
+  const bf16_t* v0;
+  const bf16_t* v1;
+  int64_t M, C;
+  int rt, r0;
+  void* out;  // fp32 or bf16
+};
+hipError_t launch_up_add(const UpAddArgs& a, bool bwd, bool out_bf16, hipStream_t stream);
+// h = bf16(GELU(p)), dp = bf16(dh * GELU'(p)) over n elements (n a multiple of 8)
+hipError_t launch_gelu(const bf16_t* p, bf16_t* h, int64_t n, hipStream_t stream);
+hipError_t launch_gelu_bwd(const bf16_t* p, const bf16_t* dh, bf16_t* dp, int64_t n, hipStream_t stream);
 int lora_grad_splits(int64_t M, int64_t K, int64_t N);
 int lora_grad_tiles(int64_t K, int64_t N);
 size_t lora_grad_partial_bytes(int64_t M, int64_t K, int64_t N, int r);

@@ -475,9 +475,12 @@ hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t st
   if (a.mode == QD_GELU_DOWN) {  // the saved FC1 output P^: bf16, [A2; L1_2] rows
     if (!x_bf16 || a.u_cols || tp == 0) return hipErrorInvalidValue;
     e = launch_t<bf16_t, false, QD_GELU_DOWN>(a, tp, S, stream);
-  } else if (a.mode == QD_DOWN) {  // dP^ (bf16) against [B1 | L2_1]
-    if (!x_bf16 || !a.u_cols || tp == 0) return hipErrorInvalidValue;
-    e = launch_t<bf16_t, true, QD_DOWN>(a, tp, S, stream);
+  } else if (a.mode == QD_DOWN) {  // down-projection alone, either side
+    if (tp == 0) return hipErrorInvalidValue;
+    if (a.u_cols)
+      e = x_bf16 ? launch_t<bf16_t, true, QD_DOWN>(a, tp, S, stream) : launch_t<float, true, QD_DOWN>(a, tp, S, stream);
+    else
+      e = x_bf16 ? launch_t<bf16_t, false, QD_DOWN>(a, tp, S, stream) : launch_t<float, false, QD_DOWN>(a, tp, S, stream);
   } else if (a.u_cols) {
     e = x_bf16 ? launch_t<bf16_t, true, QD_QUANT>(a, tp, S, stream) : launch_t<float, true, QD_QUANT>(a, tp, S, stream);
   } else {

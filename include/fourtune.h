@@ -198,6 +198,46 @@ ft_status fourtune_mlp_bwd(const ft_linear *fc1, const ft_linear *fc2, const voi
                            ft_dtype dx_dt, float *d_a1, float *d_b1, float *d_a2, float *d_b2,
                            ft_mx4 *dpq_out, void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- fusion ablation
+ * The same layer with the fusions taken apart, for measuring what they save (FourTune
+ * §4, "Kernel Fusion Breakdown", Figure 9: LoRA fusion over the unfused 4-bit
+ * baseline, then MLP fusion on top). Every step is a launch of its own and every
+ * intermediate goes through HBM in bf16:
+ *   linear forward : Q(X) (quantizer); XL = bf16(X^ [A;L1]^T) (down-projection alone);
+ *                    Y0 = bf16(Q(X) Q(R)^T) (4-bit GEMM alone);
+ *                    y = Y0 + XL [B|L2]^T (up-projection + add, one rounding)
+ *   linear backward: Q(dY); GB = bf16(dY^ [B|L2]); dX0 = bf16(Q(dY) Q(R));
+ *                    dx = dX0 + GB [A;L1]; dA, dB as in fourtune_linear_bwd
+ *   MLP            : H = bf16(GELU(P^)) stored and fed to FC2 (so FC2's 4-bit operand
+ *                    is Q(H) of the bf16 H); backward dH stored in bf16, then
+ *                    dP^ = bf16(dH GELU'(P^)) in its own pass.
+ * The results differ from the fused entry points only by those bf16 roundings.
+ * Arguments are those of the fused entry points; the workspace is
+ * fourtune_ablation_workspace_bytes(m, fc1, fc2) bytes (fc2 = NULL for one linear).
+ * lora_fused != 0 builds the MLP from the fused linears (fourtune_linear_fwd/bwd) with
+ * GELU still separate; 0 from the unfused ones. h_saved [m x f] bf16 receives H in the
+ * forward and is read by the backward. */
+size_t fourtune_ablation_workspace_bytes(int64_t m, const ft_linear *fc1, const ft_linear *fc2);
+ft_status fourtune_linear_fwd_unfused(const ft_linear *L, const void *x, ft_dtype x_dt, int64_t m,
+                                      void *y, ft_dtype y_dt, void *xl_saved, void *ws,
+                                      size_t ws_bytes, void *stream);
+ft_status fourtune_linear_bwd_unfused(const ft_linear *L, const void *dy, ft_dtype dy_dt,
+                                      const void *x, ft_dtype x_dt, const void *xl_saved,
+                                      int64_t m, void *dx, ft_dtype dx_dt, float *d_lora_a,
+                                      float *d_lora_b, void *ws, size_t ws_bytes, void *stream);
+ft_status fourtune_mlp_fwd_unfused(const ft_linear *fc1, const ft_linear *fc2, int lora_fused,
+                                   const void *x, ft_dtype x_dt, int64_t m, void *y,
+                                   ft_dtype y_dt, void *xl1_saved, void *pre_saved,
+                                   void *h_saved, void *hl2_saved, void *ws, size_t ws_bytes,
+                                   void *stream);
+ft_status fourtune_mlp_bwd_unfused(const ft_linear *fc1, const ft_linear *fc2, int lora_fused,
+                                   const void *dy, ft_dtype dy_dt, const void *x, ft_dtype x_dt,
+                                   const void *xl1_saved, const void *pre_saved,
+                                   const void *h_saved, const void *hl2_saved, int64_t m,
+                                   void *dx, ft_dtype dx_dt, float *d_a1, float *d_b1,
+                                   float *d_a2, float *d_b2, void *ws, size_t ws_bytes,
+                                   void *stream);
+
 /* Static text of a status code. */
 const char *fourtune_status_string(ft_status s);
 /* Detail of the last failing call on this thread ("" if none). */

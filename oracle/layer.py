@@ -180,3 +180,61 @@ def mlp_backward(dY, X, saved: dict, fc1: Linear, fc2: Linear, prec: Prec = EXAC
     dX, dA1, dB1, _ = linear_backward(dP, X, saved["XL1"], fc1, prec, Gq=dPq)
     return dict(dX=dX, dA1=dA1, dB1=dB1, dA2=dA2, dB2=dB2, dH=dH, dP=dP, dP32=dP32)
 
+
+
+# ----------------------------------------------------------------------------------
+# Unfused forms (FourTune §4 "Kernel Fusion Breakdown": the fusions taken apart)
+# ----------------------------------------------------------------------------------
+# Reading: without fusion every step is its own pass and its result is stored in HBM
+# in bf16 before the next step reads it. Compared with the fused forms above, this
+# adds exactly these roundings: the 4-bit product before the up-projection is added
+# (Y0, dX0; a layer without low-rank branches has no up-projection, its 4-bit product
+# is the output itself and is not rounded in between), the MLP's GELU output H, and
+# FC2's input gradient dH.
+def linear_forward_unfused(X, lin: Linear, prec: Prec = EXACT):
+    """Returns (Y, XL). Y = bf16(deq Q(X) deq Q(R)^T) + XL U^T, XL = bf16(bf16(X) D^T)."""
+    X = np.asarray(X, dtype=np.float64)
+    XL = _b(_b(X, prec) @ lin.D().T, prec)
+    Y0 = _q(X, prec) @ _q(lin.R, prec).T
+    if XL.shape[1] == 0:
+        return Y0, XL
+    return _b(Y0, prec) + XL @ lin.U().T, XL
+
+
+def linear_backward_unfused(G, X, XL, lin: Linear, prec: Prec = EXACT):
+    """Returns (dX, dA, dB, GB). dX = bf16(deq Q(G) deq Q(R)) + GB D; GB, dA, dB as in
+    the fused form (the LoRA gradients are separate kernels in both)."""
+    G = np.asarray(G, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    r = lin.rank
+    Gh = _b(G, prec)
+    GB = _b(Gh @ lin.U(), prec)
+    dX0 = _q(G, prec) @ _q(lin.R, prec)
+    dX = dX0 if GB.shape[1] == 0 else _b(dX0, prec) + GB @ lin.D()
+    dA = GB[:, :r].T @ _b(X, prec)
+    dB = Gh.T @ XL[:, :r]
+    return dX, dA, dB, GB
+
+
+def mlp_forward_unfused(X, fc1: Linear, fc2: Linear, prec: Prec = EXACT, lora_fused=False):
+    """Returns dict(Y, XL1, P, H, HL2). P = bf16(FC1(X)); H = bf16(GELU(P)) is stored and
+    is FC2's input (its 4-bit operand Q(H) and its down-projection both read it).
+    ``lora_fused`` builds the MLP from the fused linears, otherwise from the unfused."""
+    fwd = linear_forward if lora_fused else linear_forward_unfused
+    pre, XL1 = fwd(X, fc1, prec)
+    P = _b(pre, prec)
+    H = _b(gelu_tanh(P), prec)
+    Y, HL2 = fwd(H, fc2, prec)
+    return dict(Y=Y, XL1=XL1, P=P, H=H, HL2=HL2)
+
+
+def mlp_backward_unfused(dY, X, saved: dict, fc1: Linear, fc2: Linear, prec: Prec = EXACT,
+                         lora_fused=False):
+    """Returns dict(dX, dA1, dB1, dA2, dB2, dH, dP). dH = bf16(FC2 backward with input H);
+    dP = bf16(dH GELU'(P)); FC1 backward with G = dP."""
+    bwd = linear_backward if lora_fused else linear_backward_unfused
+    dH, dA2, dB2, _ = bwd(dY, saved["H"], saved["HL2"], fc2, prec)
+    dH = _b(dH, prec)
+    dP = _b(dH * gelu_tanh_grad(saved["P"]), prec)
+    dX, dA1, dB1, _ = bwd(dP, X, saved["XL1"], fc1, prec)
+    return dict(dX=dX, dA1=dA1, dB1=dB1, dA2=dA2, dB2=dB2, dH=dH, dP=dP)

@@ -1,0 +1,247 @@
+"""GPU parity of the fusion-ablation entry points (the layer with its fusions taken
+apart, FourTune §4 "Kernel Fusion Breakdown") against the oracle's unfused forms.
+
+Bar: Q(X)-consuming outputs and the stored intermediates within a relative Frobenius
+error of 1e-3 of the fp64 oracle (bf16 outputs against the oracle rounded to bf16),
+the same bar as the fused path. The unfused forms round the stored 4-bit product, H and
+dH to bf16 (oracle/layer.py states the reading); the oracle applies the same roundings
+to its own exact values. Small cases cover ragged rows, every low-rank configuration
+(LoRA only, stabilizer only, none, the widest) and fp32 inputs; the bench's workloads
+(c2's linear, c3's MLP at both levels) are checked at full size on sampled rows and
+sampled LoRA-gradient entries, as in the fused full-size tests.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_lora_fp4_amd import abi
+from oracle import layer, mx4
+from synth import workloads as wl
+from tests.gpu_util import dev, host, log, rel_fro
+from tests.test_gpu_fullsize import (_bf, _block_rows, _chunked, _col_blocks, _errs_ok, _f64, _gpu_lin,
+                                     _lin64, _rows)
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+def _check(errs):
+    log(f"  rel errors {errs}")
+    for k, e in errs.items():
+        assert e <= TOL, (k, e)
+
+
+# ------------------------------------------------------------------------------ linear
+LIN_CASES = [
+    # m, n, k, r, s, x_dtype, out_dtype
+    (256, 512, 512, 16, 16, "fp32", torch.float32),
+    (200, 352, 480, 32, 0, "bf16", torch.float32),   # ragged M, no stabilizer
+    (96, 256, 320, 0, 32, "bf16", torch.bfloat16),   # no LoRA
+    (64, 128, 160, 0, 0, "bf16", torch.float32),     # backbone alone
+    (300, 640, 384, 64, 64, "bf16", torch.bfloat16),  # widest low-rank part
+]
+
+
+@pytest.mark.parametrize("m,n,k,r,s,xdt,odt", LIN_CASES)
+def test_linear_unfused_small(m, n, k, r, s, xdt, odt):
+    log(f"unfused linear m={m} n={n} k={k} r={r} s={s} x={xdt} out={odt}")
+    d = wl.random_linear(m, n, k, r, s, seed=m + 3 * n + k, x_dtype=xdt, dy_dtype=xdt)
+    L = _gpu_lin(d)
+    x, dy = dev(d["X"], xdt), dev(d["dY"], xdt)
+    ws = abi.workspace(abi.fourtune_ablation_workspace_bytes(m, L))
+    y = torch.empty((m, n), dtype=odt, device="cuda")
+    xl = torch.empty((m, r + s), dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty((m, k), dtype=odt, device="cuda")
+    da = torch.empty((r, k), dtype=torch.float32, device="cuda")
+    db = torch.empty((n, r), dtype=torch.float32, device="cuda")
+    abi.fourtune_linear_fwd_unfused(L, x, y, xl, ws)
+    abi.fourtune_linear_bwd_unfused(L, dy, x, xl, dx, da, db, ws)
+    torch.cuda.synchronize()
+
+    lin = _lin64(d)
+    X, G = _f64(d["X"]), _f64(d["dY"])
+    Y, XL = layer.linear_forward_unfused(X, lin)
+    dX, dA, dB, _ = layer.linear_backward_unfused(G, X, XL, lin)
+    rnd = _bf if odt == torch.bfloat16 else (lambda a: a)
+    errs = dict(Y=rel_fro(host(y), rnd(Y)), dX=rel_fro(host(dx), rnd(dX)))
+    if r + s:
+        errs["XL"] = rel_fro(host(xl), XL)
+    if r:
+        errs["dA"] = rel_fro(host(da), dA)
+        errs["dB"] = rel_fro(host(db), dB)
+    _check(errs)
+
+
+def test_linear_unfused_matches_fused_within_its_rounding():
+    """The unfused and fused linears compute the same layer: their outputs differ only
+    by the stored product's bf16 rounding, and the LoRA gradients (same kernel, same
+    inputs) are bitwise equal."""
+    d = wl.random_linear(300, 544, 384, 32, 32, seed=41)
+    m, n, k = 300, 544, 384
+    L = _gpu_lin(d)
+    x, dy = dev(d["X"]), dev(d["dY"])
+    ws = abi.workspace(abi.fourtune_ablation_workspace_bytes(m, L))
+    outs = []
+    for fused in (True, False):
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        xl = torch.empty((m, 64), dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty((m, k), dtype=torch.float32, device="cuda")
+        da = torch.empty((32, k), dtype=torch.float32, device="cuda")
+        db = torch.empty((n, 32), dtype=torch.float32, device="cuda")
+        if fused:
+            abi.fourtune_linear_fwd(L, x, y, xl, ws)
+            abi.fourtune_linear_bwd(L, dy, x, xl, dx, da, db, ws)
+        else:
+            abi.fourtune_linear_fwd_unfused(L, x, y, xl, ws)
+            abi.fourtune_linear_bwd_unfused(L, dy, x, xl, dx, da, db, ws)
+        torch.cuda.synchronize()
+        outs.append([host(t) for t in (y, xl, dx, da, db)])
+    (yf, xlf, dxf, daf, dbf), (yu, xlu, dxu, dau, dbu) = outs
+    assert np.array_equal(xlf, xlu)
+    assert np.array_equal(daf, dau) and np.array_equal(dbf, dbu)
+    assert 0 < rel_fro(yu, yf) < 4e-3 and 0 < rel_fro(dxu, dxf) < 4e-3
+
+
+# --------------------------------------------------------------------------------- MLP
+MLP_CASES = [
+    # m, d, f, r, s, x_dtype
+    (256, 512, 1024, 16, 16, "bf16"),
+    (130, 256, 512, 32, 32, "bf16"),
+    (96, 256, 512, 0, 32, "fp32"),
+]
+
+
+def _run_mlp(case, lora_fused, out_dtype=torch.float32):
+    m = case["X"].shape[0]
+    fc1, fc2 = _gpu_lin(case["fc1"]), _gpu_lin(case["fc2"])
+    x, dy = dev(case["X"], case["x_dtype"]), dev(case["dY"], case["dy_dtype"])
+    f, dm = fc1.n, fc2.n
+    rt1, rt2 = fc1.rank + fc1.stab_rank, fc2.rank + fc2.stab_rank
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((m, dm), dtype=out_dtype, device="cuda")
+    xl1, pre, h, hl2 = (torch.empty((m, rt1), **bf), torch.empty((m, f), **bf), torch.empty((m, f), **bf),
+                        torch.empty((m, rt2), **bf))
+    dx = torch.empty((m, fc1.k), dtype=out_dtype, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    g = dict(dA1=torch.empty((fc1.rank, fc1.k), **f32), dB1=torch.empty((f, fc1.rank), **f32),
+             dA2=torch.empty((fc2.rank, f), **f32), dB2=torch.empty((dm, fc2.rank), **f32))
+    ws = abi.workspace(abi.fourtune_ablation_workspace_bytes(m, fc1, fc2))
+    abi.fourtune_mlp_fwd_unfused(fc1, fc2, lora_fused, x, y, xl1, pre, h, hl2, ws)
+    abi.fourtune_mlp_bwd_unfused(fc1, fc2, lora_fused, dy, x, xl1, pre, h, hl2, dx, g["dA1"], g["dB1"],
+                                 g["dA2"], g["dB2"], ws)
+    torch.cuda.synchronize()
+    out = dict(Y=y, XL1=xl1, P=pre, H=h, HL2=hl2, dX=dx, **g)
+    return out
+
+
+@pytest.mark.parametrize("lora_fused", [False, True])
+@pytest.mark.parametrize("m,d,f,r,s,xdt", MLP_CASES)
+def test_mlp_unfused_small(m, d, f, r, s, xdt, lora_fused):
+    log(f"unfused mlp m={m} d={d} f={f} r={r} s={s} x={xdt} lora_fused={lora_fused}")
+    case = wl.random_mlp(m, d, f, r, s, seed=m + d + f + 7, x_dtype=xdt, dy_dtype=xdt)
+    got = {k: host(v) for k, v in _run_mlp(case, lora_fused).items()}
+    fc1, fc2 = _lin64(case["fc1"]), _lin64(case["fc2"])
+    X, G = _f64(case["X"]), _f64(case["dY"])
+    fwd = layer.mlp_forward_unfused(X, fc1, fc2, lora_fused=lora_fused)
+    bwd = layer.mlp_backward_unfused(G, X, fwd, fc1, fc2, lora_fused=lora_fused)
+    errs = {k: rel_fro(got[k], fwd[k]) for k in ("Y", "P", "H")}
+    errs["dX"] = rel_fro(got["dX"], bwd["dX"])
+    if r + s:
+        errs["XL1"] = rel_fro(got["XL1"], fwd["XL1"])
+        errs["HL2"] = rel_fro(got["HL2"], fwd["HL2"])
+    if r:
+        for k in ("dA1", "dB1", "dA2", "dB2"):
+            errs[k] = rel_fro(got[k], bwd[k])
+    _check(errs)
+
+
+# ----------------------------------------------------------------- bench workloads, full size
+@pytest.mark.timeout(600)
+def test_linear_unfused_c2_full_size_sampled():
+    log("unfused linear c2, full size")
+    d = wl.linear_case("c2")
+    X, G, R = d["X"], d["dY"], d["R"]
+    m, k = X.shape
+    n, r = R.shape[0], d["A"].shape[0]
+    L = _gpu_lin(d)
+    x, dy = dev(X, d["x_dtype"]), dev(G, d["dy_dtype"])
+    ws = abi.workspace(abi.fourtune_ablation_workspace_bytes(m, L))
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    y, xl, dx = torch.empty((m, n), **bf), torch.empty((m, r + d["L1"].shape[0]), **bf), torch.empty((m, k), **bf)
+    da = torch.empty((r, k), dtype=torch.float32, device="cuda")
+    db = torch.empty((n, r), dtype=torch.float32, device="cuda")
+    abi.fourtune_linear_fwd_unfused(L, x, y, xl, ws)
+    abi.fourtune_linear_bwd_unfused(L, dy, x, xl, dx, da, db, ws)
+    torch.cuda.synchronize()
+    del x, dy
+
+    rng = np.random.default_rng(zlib.crc32(b"unfused/c2"))
+    _, rows = _block_rows(m, rng)
+    ncols, kcols = _col_blocks(n, rng), _col_blocks(k, rng)
+    lin = _lin64(d)
+    D, U = lin.D(), lin.U()
+    Xr, Gr = _f64(X[rows]), _f64(G[rows])
+    XL_o = _bf(_bf(Xr) @ D.T)
+    Y_o = _bf(mx4.fake_quant(Xr) @ mx4.fake_quant(R[ncols]).T) + XL_o @ U[ncols].T
+    GB_o = _bf(_bf(Gr) @ U)
+    dX_o = _bf(mx4.fake_quant(Gr) @ mx4.fake_quant(R[:, kcols])) + GB_o @ D[:, kcols]
+    errs = dict(XL=rel_fro(_rows(xl, rows), XL_o), Y=rel_fro(_rows(y, rows)[:, ncols], _bf(Y_o)),
+                dX=rel_fro(_rows(dx, rows)[:, kcols], _bf(dX_o)))
+    jsel = np.unique([0, r // 2, r - 1])
+    GBA = _chunked(lambda lo, hi: _bf(_bf(G[lo:hi]) @ U[:, jsel]), m)
+    XLA = _chunked(lambda lo, hi: _bf(_bf(X[lo:hi]) @ D[jsel].T), m)
+    errs["dA"] = rel_fro(host(da)[jsel][:, kcols], GBA.T @ _bf(X[:, kcols]))
+    errs["dB"] = rel_fro(host(db)[ncols][:, jsel], _f64(G[:, ncols]).T @ XLA)
+    _errs_ok(errs)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("lora_fused", [False, True])
+def test_mlp_unfused_c3_full_size_sampled(lora_fused):
+    log(f"unfused MLP c3, full size, lora_fused={lora_fused}")
+    case = wl.mlp_case("c3")
+    X, G = case["X"], case["dY"]
+    p1, p2 = case["fc1"], case["fc2"]
+    m, dm = X.shape
+    f = p1["R"].shape[0]
+    r1, r2 = p1["A"].shape[0], p2["A"].shape[0]
+    got = _run_mlp(case, lora_fused, out_dtype=torch.bfloat16)
+
+    rng = np.random.default_rng(zlib.crc32(f"unfused/c3/{lora_fused}".encode()))
+    _, rows = _block_rows(m, rng)
+    dcols, fcols = _col_blocks(dm, rng), _col_blocks(f, rng)
+    l1, l2 = _lin64(p1), _lin64(p2)
+    D1, U1, D2, U2 = l1.D(), l1.U(), l2.D(), l2.U()
+    Rd1, Rd2 = mx4.fake_quant(p1["R"]), mx4.fake_quant(p2["R"])
+    st = (lambda a: a) if lora_fused else _bf  # the stored 4-bit product of an unfused linear
+
+    Xr, Gr = _f64(X[rows]), _f64(G[rows])
+    XL1_o = _bf(_bf(Xr) @ D1.T)
+    P_o = _bf(st(mx4.fake_quant(Xr) @ Rd1.T) + XL1_o @ U1.T)
+    H_o = _bf(layer.gelu_tanh(P_o))
+    HL2_o = _bf(H_o @ D2.T)
+    Y_o = st(mx4.fake_quant(H_o) @ Rd2[dcols].T) + HL2_o @ U2[dcols].T
+    GB2_o = _bf(_bf(Gr) @ U2)
+    dH_o = _bf(st(mx4.fake_quant(Gr) @ Rd2) + GB2_o @ D2)
+    dP_o = _bf(dH_o * layer.gelu_tanh_grad(P_o))
+    GB1_o = _bf(dP_o @ U1)
+    dX_o = st(mx4.fake_quant(dP_o) @ Rd1[:, dcols]) + GB1_o @ D1[:, dcols]
+    errs = dict(XL1=rel_fro(_rows(got["XL1"], rows), XL1_o), P=rel_fro(_rows(got["P"], rows), P_o),
+                H=rel_fro(_rows(got["H"], rows), H_o), HL2=rel_fro(_rows(got["HL2"], rows), HL2_o),
+                Y=rel_fro(_rows(got["Y"], rows)[:, dcols], _bf(Y_o)),
+                dX=rel_fro(_rows(got["dX"], rows)[:, dcols], _bf(dX_o)))
+
+    log("  oracle: sampled LoRA-gradient entries (reductions over all rows)")
+    Xd_all = _chunked(lambda lo, hi: mx4.fake_quant(X[lo:hi]), m, step=2048)
+    XL1_all = _chunked(lambda lo, hi: _bf(_bf(X[lo:hi]) @ D1.T), m)
+    Pf = _bf(st(Xd_all @ Rd1[fcols].T) + XL1_all @ U1[fcols].T)
+    Gd_all = _chunked(lambda lo, hi: mx4.fake_quant(G[lo:hi]), m, step=2048)
+    GB2_all = _chunked(lambda lo, hi: _bf(_bf(G[lo:hi]) @ U2), m)
+    dPf = _bf(_bf(st(Gd_all @ Rd2[:, fcols]) + GB2_all @ D2[:, fcols]) * layer.gelu_tanh_grad(Pf))
+    j2 = np.unique([0, r2 // 2, r2 - 1])
+    errs["dA2"] = rel_fro(host(got["dA2"])[j2][:, fcols], GB2_all[:, j2].T @ _bf(layer.gelu_tanh(Pf)))
+    j1 = np.unique([0, r1 // 2, r1 - 1])
+    errs["dB1"] = rel_fro(host(got["dB1"])[fcols][:, j1], dPf.T @ XL1_all[:, j1])
+    _errs_ok(errs)
