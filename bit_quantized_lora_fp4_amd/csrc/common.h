@@ -91,23 +91,30 @@ __device__ __forceinline__ uint32_t bf16x2_absmax_bits(uint32_t w) {
 // error stays within a few fp32 ulps also where GELU is tiny (large negative p).
 // Derivative: s + p (1 - tanh^2(u))/2 du/dp = s (1 + 2 p (1 - s) du/dp).
 // Large |u| saturates correctly (e -> 0 or inf); NaN propagates.
-constexpr float GELU_K0 = 0.7978845608028654f;  // sqrt(2/pi)
-constexpr float GELU_K1 = 0.044715f;
-constexpr float M2_LOG2E = -2.8853900817779268f;  // -2 / ln(2)
+constexpr double GELU_K0 = 0.7978845608028654;  // sqrt(2/pi)
+constexpr double GELU_K1 = 0.044715;
+constexpr double LN_2 = 0.6931471805599453;
+// -2u / ln 2 = p (A0 + A1 p^2): the exponent of e^(-2u) in base 2
+constexpr float GELU_A0 = (float)(-2.0 * GELU_K0 / LN_2);
+constexpr float GELU_A1 = (float)(-2.0 * GELU_K0 * GELU_K1 / LN_2);
+// 2 du/dp = B0 + B1 p^2
+constexpr float GELU_B0 = (float)(2.0 * GELU_K0);
+constexpr float GELU_B1 = (float)(6.0 * GELU_K0 * GELU_K1);
 __device__ __forceinline__ float gelu_f(float p) {
-  const float u = GELU_K0 * (p + GELU_K1 * p * p * p);
-  const float e = __builtin_amdgcn_exp2f(u * M2_LOG2E);
+  const float e = __builtin_amdgcn_exp2f(p * __builtin_fmaf(GELU_A1, p * p, GELU_A0));
   return p * __builtin_amdgcn_rcpf(1.0f + e);
 }
 __device__ __forceinline__ float gelu_grad_f(float p) {
-  const float u = GELU_K0 * (p + GELU_K1 * p * p * p);
-  const float e = __builtin_amdgcn_exp2f(u * M2_LOG2E);
+  const float p2 = p * p;
+  const float e = __builtin_amdgcn_exp2f(p * __builtin_fmaf(GELU_A1, p2, GELU_A0));
   const float sg = __builtin_amdgcn_rcpf(1.0f + e);
-  const float du = GELU_K0 * (1.0f + 3.0f * GELU_K1 * p * p);
   // 1 - s, formed without overflow (e may be huge or infinite) or cancellation
   const float es = e > 1.0f ? 1.0f - sg : e * sg;
-  const float g = sg * (1.0f + 2.0f * p * es * du);
-  // |p| > 16: the derivative is 1 (or 0) to fp32 precision; p^3 may overflow there
+  float g = sg * __builtin_fmaf(p * es, __builtin_fmaf(GELU_B1, p2, GELU_B0), 1.0f);
+  // |p| > 16: the derivative is 1 (or 0) to fp32 precision; p^3 may overflow there.
+  // g is pinned as computed, so the choice stays a select rather than a branch around
+  // the arithmetic (a branch per element costs more than the arithmetic it skips).
+  asm volatile("" : "+v"(g));
   return fabsf(p) > 16.0f ? (p > 0.0f ? 1.0f : 0.0f) : g;
 }
 // 8 bf16 (4 words) -> bf16(GELU(x)) for each, rounded to nearest even

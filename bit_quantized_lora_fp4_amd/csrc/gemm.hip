@@ -707,6 +707,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     const bufres rqc = make_buf(g.q_codes, (uint64_t)g.M * (g.N >> 1));
     const bufres rqs = make_buf(g.q_scales, (uint64_t)((g.M + 31) >> 5) * (g.N >> 5));
     const bufres rpre = make_buf(g.pre, (uint64_t)g.M * g.N * 2);
+    // P^ is requested two block rows ahead (32 loads in flight), so the tiles below
+    // wait for their loads in turn instead of one round trip each
+    v2i pw[2][TI][4];
+    auto load_pre = [&](int j, v2i (&dst)[TI][4]) __attribute__((always_inline)) {
+      const int64_t row = m0 + wm * 128 + 32 * j + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int64_t col = n0 + wn * 128 + 32 * i + 8 * gq + 4 * half;
+          dst[i][gq] = buf_load8(rpre, sel_off(row < g.M && col < g.N, (uint32_t)((row * g.N + col) * 2)));
+        }
+    };
+    load_pre(0, pw[0]);
+    load_pre(1, pw[1]);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int64_t brow = m0 + wm * 128 + 32 * j;  // first row of this block row
@@ -715,16 +730,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         const int64_t col0 = n0 + wn * 128 + 32 * i;
-        v2i pw[TI][4];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int64_t col = col0 + 8 * gq + 4 * half;
-          pw[i][gq] = buf_load8(rpre, sel_off(row_ok && col < g.N, (uint32_t)((row * g.N + col) * 2)));
-        }
         float v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t pwd = (uint32_t)((r & 2) ? pw[i][r >> 2].y : pw[i][r >> 2].x);
+          const uint32_t pwd = (uint32_t)((r & 2) ? pw[j & 1][i][r >> 2].y : pw[j & 1][i][r >> 2].x);
           const float p = (r & 1) ? bf16_hi(pwd) : bf16_lo(pwd);
           acc[i][j][r] = acc[i][j][r] * gelu_grad_f(p);  // dP = dH * GELU'(P^)
           v[r] = acc[i][j][r];
@@ -733,6 +742,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
                          g.N >> 5);
         __builtin_amdgcn_sched_barrier(0);  // one tile at a time: bounded register use
       }
+      if (j + 2 < TJ) load_pre(j + 2, pw[j & 1]);
     }
   }
 
