@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
     python bench.py --calibrate-copy     (a plain 512 MiB device copy, for counter scaling)
     python bench.py --ablation           (fusion ablation; one JSON line of its own)
+    python bench.py --dit                (every linear of a FLUX-shaped DiT; one JSON line)
 
 One step = the whole hot path once over one batch: the layer's forward (fused
 quantize + down-projection, 4-bit GEMM + up-projection) and backward (fused quantize +
@@ -50,6 +51,10 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--ablation", action="store_true",
                     help="fusion ablation: bf16 LoRA, unfused and fused W4A4G4 at c2 (linear), c3 (MLP)")
+    ap.add_argument("--dit", action="store_true",
+                    help="all linears of a FLUX-shaped DiT (synthetic weights), W4A4G4 vs bf16 LoRA")
+    ap.add_argument("--double-blocks", type=int, default=19)
+    ap.add_argument("--single-blocks", type=int, default=38)
     return ap.parse_args()
 
 
@@ -312,6 +317,179 @@ def ablation(args):
     return 0
 
 
+# --------------------------------------------------------------------------- whole DiT
+HIDDEN, MLP_DIM, QKV_DIM = 3072, 12288, 9216
+DIT_RANK, DIT_STAB = 64, 32
+IMG_TOKENS, TXT_TOKENS = 4096, 512
+
+
+def dit_linears(n_double, n_single):
+    """The token-wise linears of a FLUX.1-dev-shaped DiT at batch 1, as (tokens, kind):
+    a double-stream block holds an image stream (4096 tokens) and a text stream (512
+    tokens) with weights of their own, a single-stream block one stream of 4608 tokens.
+    Each stream has QKV [9216 x 3072], the attention output projection [3072 x 3072]
+    and the MLP 3072 -> 12288 -> 3072 (the single-stream block's fused linears hold
+    the same products: its first linear is QKV and FC1 side by side, its second the
+    output projection and FC2 summed)."""
+    streams = []
+    for _ in range(n_double):
+        streams += [IMG_TOKENS, TXT_TOKENS]
+    streams += [IMG_TOKENS + TXT_TOKENS] * n_single
+    return streams
+
+
+def dit_weight_bytes(n_double, n_single, r=DIT_RANK, s=DIT_STAB):
+    """Weight bytes of the blocks' linears, token-wise and modulation (adaLN: 6 x hidden
+    outputs per stream of a double block, 3 x hidden for a single block), for W4A4G4
+    (MXFP4 codes + one scale byte per 32x32 block, bf16 LoRA and stabilizer factors)
+    and for bf16 LoRA (bf16 weight + bf16 LoRA factors). Embedders, norms and the final
+    layer (under 1% of the parameters) are left out of both."""
+    per_stream = [(QKV_DIM, HIDDEN), (HIDDEN, HIDDEN), (MLP_DIM, HIDDEN), (HIDDEN, MLP_DIM)]
+    lins = []
+    for _ in range(n_double):
+        lins += per_stream * 2 + [(6 * HIDDEN, HIDDEN)] * 2
+    for _ in range(n_single):
+        lins += per_stream + [(3 * HIDDEN, HIDDEN)]
+    w4 = sum(n * k // 2 + (n // 32) * (k // 32) + 2 * (r + s) * (n + k) for n, k in lins)
+    bf = sum(2 * n * k + 2 * r * (n + k) for n, k in lins)
+    params = sum(n * k for n, k in lins)
+    return dict(params=params, w4a4g4_bytes=w4, bf16_lora_bytes=bf, ratio=round(bf / w4, 3),
+                bits_per_weight_w4=round(8 * sum(n * k // 2 + (n // 32) * (k // 32) for n, k in lins) / params, 4))
+
+
+def dit(args):
+    """One training step's linears over a whole FLUX-shaped DiT (FourTune §4 reports a
+    DiT step and its weight memory against bf16 LoRA): every token-wise linear of every
+    block, forward then backward in reverse block order, with weights of its own
+    (synthetic, drawn on the device) and LoRA gradients; attention, norms and
+    modulation are not run. Inputs are synthetic tensors of each stream's shape."""
+    import torch
+    import torch.nn.functional as F
+    from bit_quantized_lora_fp4_amd import abi
+
+    abi.lib()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    streams = dit_linears(args.double_blocks, args.single_blocks)
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    r, s = DIT_RANK, DIT_STAB
+    rt = r + s
+
+    def randn(shape, std, dtype=torch.bfloat16):
+        return (torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32) * std).to(dtype)
+
+    def w4_linear(n, k):
+        R = randn((n, k), 0.02, torch.float32)
+        L = abi.make_linear(R, randn((r, k), 0.01), randn((n, r), 0.01), randn((s, k), 0.01), randn((n, s), 0.01))
+        del R
+        return L
+
+    log(f"[dit] {len(streams)} streams ({args.double_blocks} double, {args.single_blocks} single blocks): "
+        "drawing W4A4G4 weights")
+    # inputs per token count (synthetic; Student-t activations as in the DiT block workload)
+    torch.manual_seed(1234)
+    t3 = torch.distributions.StudentT(torch.tensor(3.0, device="cuda"))
+    xin = {m: (t3.sample((m, HIDDEN)) * 0.5).to(torch.bfloat16) for m in sorted(set(streams))}
+    dyin = {m: randn((m, HIDDEN), 1e-3) for m in xin}
+    dqkv = {m: randn((m, QKV_DIM), 1e-3) for m in xin}
+    big_ws = 0
+    w4 = []
+    for m in streams:
+        blk = dict(m=m, qkv=w4_linear(QKV_DIM, HIDDEN), o=w4_linear(HIDDEN, HIDDEN),
+                   fc1=w4_linear(MLP_DIM, HIDDEN), fc2=w4_linear(HIDDEN, MLP_DIM))
+        blk["xl_qkv"] = torch.empty((m, rt), **bf)
+        blk["xl_o"] = torch.empty((m, rt), **bf)
+        blk["xl1"], blk["hl2"] = torch.empty((m, rt), **bf), torch.empty((m, rt), **bf)
+        blk["pre"] = torch.empty((m, MLP_DIM), **bf)
+        big_ws = max(big_ws, abi.fourtune_linear_workspace_bytes(m, blk["qkv"]),
+                     abi.fourtune_mlp_workspace_bytes(m, blk["fc1"], blk["fc2"]))
+        w4.append(blk)
+    ws = abi.workspace(big_ws)
+    out = {m: dict(qkv=torch.empty((m, QKV_DIM), **bf), o=torch.empty((m, HIDDEN), **bf),
+                   y=torch.empty((m, HIDDEN), **bf), dx=torch.empty((m, HIDDEN), **bf))
+           for m in xin}
+    grads = dict(a_h=torch.empty((r, HIDDEN), **f32), b_qkv=torch.empty((QKV_DIM, r), **f32),
+                 b_h=torch.empty((HIDDEN, r), **f32), b_f=torch.empty((MLP_DIM, r), **f32),
+                 a_f=torch.empty((r, MLP_DIM), **f32))
+    torch.cuda.synchronize()
+
+    def w4_step():
+        for b in w4:
+            m, o = b["m"], out[b["m"]]
+            abi.fourtune_linear_fwd(b["qkv"], xin[m], o["qkv"], b["xl_qkv"], ws)
+            abi.fourtune_linear_fwd(b["o"], xin[m], o["o"], b["xl_o"], ws)
+            abi.fourtune_mlp_fwd(b["fc1"], b["fc2"], xin[m], o["y"], b["xl1"], b["pre"], b["hl2"], ws)
+        g = grads
+        for b in reversed(w4):
+            m, o = b["m"], out[b["m"]]
+            abi.fourtune_mlp_bwd(b["fc1"], b["fc2"], dyin[m], xin[m], b["xl1"], b["pre"], b["hl2"], o["dx"],
+                                 g["a_h"], g["b_f"], g["a_f"], g["b_h"], ws)
+            abi.fourtune_linear_bwd(b["o"], dyin[m], xin[m], b["xl_o"], o["dx"], g["a_h"], g["b_h"], ws)
+            abi.fourtune_linear_bwd(b["qkv"], dqkv[m], xin[m], b["xl_qkv"], o["dx"], g["a_h"], g["b_qkv"], ws)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * time_region(torch, lambda i: fn(), args.steps) / args.steps
+
+    log("[dit] timing W4A4G4")
+    t_w4 = timed(w4_step)
+    mem_w4 = torch.cuda.memory_allocated()
+    del w4, ws
+    torch.cuda.empty_cache()
+
+    log("[dit] drawing bf16 LoRA weights")
+
+    def bf_linear(n, k):
+        W = randn((n, k), 0.02)
+        A, B = randn((r, k), 0.01), randn((n, r), 0.01)
+        return dict(W=W, Wt=W.t().contiguous(), A=A, At=A.t().contiguous(), B=B, Bt=B.t().contiguous())
+
+    bl = [dict(m=m, qkv=bf_linear(QKV_DIM, HIDDEN), o=bf_linear(HIDDEN, HIDDEN), fc1=bf_linear(MLP_DIM, HIDDEN),
+               fc2=bf_linear(HIDDEN, MLP_DIM)) for m in streams]
+    torch.cuda.synchronize()
+
+    def bf_step():
+        saved = []
+        for b in bl:
+            x = xin[b["m"]]
+            _, xa_q = _lora_fwd(torch, b["qkv"], x)
+            _, xa_o = _lora_fwd(torch, b["o"], x)
+            p, xa1 = _lora_fwd(torch, b["fc1"], x)
+            h = F.gelu(p, approximate="tanh")
+            _, xa2 = _lora_fwd(torch, b["fc2"], h)
+            saved.append((xa_q, xa_o, p, xa1, h, xa2))
+        for b, (xa_q, xa_o, p, xa1, h, xa2) in zip(reversed(bl), reversed(saved)):
+            m = b["m"]
+            x = xin[m]
+            dh, _, _ = _lora_bwd(torch, b["fc2"], dyin[m], h, xa2)
+            dp = torch.ops.aten.gelu_backward(dh, p, approximate="tanh")
+            _lora_bwd(torch, b["fc1"], dp, x, xa1)
+            _lora_bwd(torch, b["o"], dyin[m], x, xa_o)
+            _lora_bwd(torch, b["qkv"], dqkv[m], x, xa_q)
+
+    log("[dit] timing bf16 LoRA")
+    t_bf = timed(bf_step)
+    flops_w4 = sum(4.0 * m * HIDDEN * (QKV_DIM + HIDDEN + 2 * MLP_DIM) for m in streams)
+    res = {"metric": "DiT linears fwd+bwd step time, W4A4G4 vs bf16 LoRA (FourTune §4 DiT step)",
+           "unit": "ms", "higher_is_better": False, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "data": "synthetic weights and inputs",
+           "config": {"model": "FLUX.1-dev-shaped DiT linears", "double_blocks": args.double_blocks,
+                      "single_blocks": args.single_blocks, "hidden": HIDDEN, "mlp": MLP_DIM,
+                      "image_tokens": IMG_TOKENS, "text_tokens": TXT_TOKENS, "lora_rank": r, "stab_rank": s,
+                      "excluded": "attention, norms, modulation (M = 1), embedders"},
+           "w4a4g4_ms": round(t_w4, 3), "bf16_lora_ms": round(t_bf, 3), "speedup": round(t_bf / t_w4, 3),
+           "w4a4g4_tflops_4bit": round(flops_w4 / (t_w4 * 1e-3) / 1e12, 1),
+           "weights": dit_weight_bytes(args.double_blocks, args.single_blocks),
+           "device_bytes_allocated_w4_run": mem_w4,
+           "pages_for_context": {"dit_step_ms": {"fourtune": 612.4, "bf16_lora": 1541.0},
+                                 "weight_gb": {"fourtune": 7.71, "bf16_lora": 22.59}}}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------------------- CPU side
 def cpu_baseline(case, seconds):
     """The oracle as it stands, fwd+bwd on a row sample of the same layer."""
@@ -357,6 +535,8 @@ def main():
         return calibrate_copy()
     if args.ablation:
         return ablation(args)
+    if args.dit:
+        return dit(args)
     import torch
     from bit_quantized_lora_fp4_amd import abi
     from synth import workloads as wl

@@ -230,3 +230,22 @@ def test_mlp_full_size_sampled(key):
             GB1_all = _bf(_bf(dP_all) @ U1[:, j1])
             errs["dA1"] = rel_fro(host(g["dA1"])[j1][:, kcols], GB1_all.T @ _bf(X[:, kcols]))
     _errs_ok(errs)
+
+
+# ------------------------------------------------------------------ DiT text stream
+@pytest.mark.timeout(600)
+def test_dit_text_stream_linears_full():
+    """The whole-DiT step's smallest stream (the 512 text tokens of a double-stream
+    block) at its real shapes and ranks (LoRA 64, stabilizer 32): QKV, the output
+    projection and the MLP pair, every output against the full oracle."""
+    from tests.test_gpu_linear import _check_full, _run as run_linear
+    from tests.test_gpu_mlp import _check_all, _oracle as mlp_oracle, _run as run_mlp
+    for n, k in ((9216, 3072), (3072, 3072)):
+        log(f"DiT text stream linear m=512 n={n} k={k}")
+        d = wl.random_linear(512, n, k, 64, 32, seed=n + k)
+        _check_full(d, run_linear(d))
+    log("DiT text stream MLP m=512 d=3072 f=12288")
+    case = wl.random_mlp(512, 3072, 12288, 64, 32, seed=512)
+    got = run_mlp(case)
+    fwd, bwd = mlp_oracle(case)
+    _check_all(case, got, fwd, bwd)
