@@ -4,6 +4,7 @@
     python bench.py --calibrate-copy     (a plain 512 MiB device copy, for counter scaling)
     python bench.py --ablation           (fusion ablation; one JSON line of its own)
     python bench.py --dit                (every linear of a FLUX-shaped DiT; one JSON line)
+    python bench.py --granularity        (32x32 blocks vs 1x32 groups: error study; one JSON line)
 
 One step = the whole hot path once over one batch: the layer's forward (fused
 quantize + down-projection, 4-bit GEMM + up-projection) and backward (fused quantize +
@@ -53,6 +54,8 @@ def parse():
                     help="fusion ablation: bf16 LoRA, unfused and fused W4A4G4 at c2 (linear), c3 (MLP)")
     ap.add_argument("--dit", action="store_true",
                     help="all linears of a FLUX-shaped DiT (synthetic weights), W4A4G4 vs bf16 LoRA")
+    ap.add_argument("--granularity", action="store_true",
+                    help="32x32 blocks vs 1x32 groups for X and dY: quantization error study")
     ap.add_argument("--double-blocks", type=int, default=19)
     ap.add_argument("--single-blocks", type=int, default=38)
     return ap.parse_args()
@@ -317,6 +320,83 @@ def ablation(args):
     return 0
 
 
+# --------------------------------------------------------------------------- granularity
+def _deq_gpu(torch, q, groups):
+    """Values of GPU-produced MXFP4 codes, as fp32 on the device (measurement only: the
+    layer itself never dequantizes)."""
+    grid = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], device="cuda")
+    c = q.codes
+    codes = torch.stack([c & 0xF, c >> 4], dim=2).reshape(c.shape[0], c.shape[1] * 2)
+    mag = grid[(codes & 7).long()]
+    val = torch.where((codes & 8) != 0, -mag, mag)
+    s = q.scales.to(torch.int32)
+    if groups:
+        s = s.repeat_interleave(32, dim=1)
+    else:
+        s = s.repeat_interleave(32, dim=0)[: codes.shape[0]].repeat_interleave(32, dim=1)
+    out = val * torch.exp2((s - 127).to(torch.float32))
+    return torch.where(s == 0xFF, torch.full_like(out, float("nan")), out)
+
+
+def granularity(args):
+    """Synthetic stand-in for the pages' granularity comparison (FourTune §4 "Impact of
+    Quantization Granularity", Table 5: block-wise against group-wise scales, measured
+    there as image fidelity on a dataset that is not here): the relative Frobenius error
+    of the 4-bit backbone products against the unquantized ones, with X and dY quantized
+    in 32x32 blocks (what the layer uses: readable transposed) or in 1x32 groups, R in
+    32x32 blocks either way, on c4's heavy-tailed activations and c2's outlier channels.
+    Codes come from the library's quantizers; products are fp32 torch matmuls."""
+    import torch
+    from bit_quantized_lora_fp4_amd import abi
+    from synth import workloads as wl
+
+    abi.lib()
+    res = {}
+    for key, name in (("c4", "qkv"), ("c4", "o"), ("c2", None)):
+        log(f"[granularity] {key} {name or ''}")
+        case = wl.linear_case(key, name)
+        dt = {"fp32": torch.float32, "bf16": torch.bfloat16}
+        x = torch.from_numpy(np.ascontiguousarray(case["X"])).to("cuda").to(dt[case["x_dtype"]])
+        g = torch.from_numpy(np.ascontiguousarray(case["dY"])).to("cuda").to(dt[case["dy_dtype"]])
+        R = torch.from_numpy(np.ascontiguousarray(case["R"])).to("cuda").float()
+        m, k = x.shape
+        n = R.shape[0]
+        rq = abi.quantize(R)
+        Rd = _deq_gpu(torch, rq, False)
+        out = {"m": m, "n": n, "k": k}
+        for tname, T in (("x", x), ("dy", g)):
+            qb = abi.quantize(T)
+            qg = abi.Mx4.empty_groups(*T.shape)
+            abi.fourtune_quantize_groups(T, qg)
+            Tf = T.float()
+            e = {}
+            for lbl, q, grp in (("block_32x32", qb, False), ("group_1x32", qg, True)):
+                Td = _deq_gpu(torch, q, grp)
+                e[lbl] = {"tensor": float((Td - Tf).norm() / Tf.norm())}
+                if tname == "x":
+                    ref = Tf @ R.t()
+                    e[lbl]["Y"] = float((Td @ Rd.t() - ref).norm() / ref.norm())
+                else:
+                    ref = Tf @ R
+                    e[lbl]["dX"] = float((Td @ Rd - ref).norm() / ref.norm())
+                del Td, ref
+            t_b = time_graph(torch, lambda i: abi.fourtune_quantize(T, qb), 20)
+            t_g = time_graph(torch, lambda i: abi.fourtune_quantize_groups(T, qg), 20)
+            eb = T.element_size()
+            byt_b = T.numel() * (eb + 0.5) + qb.scales.numel()
+            byt_g = T.numel() * (eb + 0.5) + qg.scales.numel()
+            e["quantize_us"] = {"block_32x32": round(t_b * 1e6, 2), "group_1x32": round(t_g * 1e6, 2)}
+            e["quantize_gbps"] = {"block_32x32": round(byt_b / t_b / 1e9, 1), "group_1x32": round(byt_g / t_g / 1e9, 1)}
+            out[tname] = e
+        res[f"{key}_{name}" if name else key] = out
+        del x, g, R, Rd
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "relative Frobenius error of the 4-bit backbone products vs unquantized, "
+                                "32x32 blocks vs 1x32 groups for X and dY (FourTune Table 5 stand-in)",
+                      "unit": "relative error", "data": "synthetic", "n_gpus": 1, **res}), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------------------- whole DiT
 HIDDEN, MLP_DIM, QKV_DIM = 3072, 12288, 9216
 DIT_RANK, DIT_STAB = 64, 32
@@ -537,6 +617,8 @@ def main():
         return ablation(args)
     if args.dit:
         return dit(args)
+    if args.granularity:
+        return granularity(args)
     import torch
     from bit_quantized_lora_fp4_amd import abi
     from synth import workloads as wl

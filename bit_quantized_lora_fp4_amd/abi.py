@@ -51,6 +51,8 @@ _SIGS = {
     "ft_mx4_scales_bytes": (c_sz, [c_i64, c_i64]),
     "fourtune_quantize": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i64,
                                          ctypes.POINTER(FtMx4), c_vp]),
+    "fourtune_quantize_groups": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i64,
+                                                ctypes.POINTER(FtMx4), c_vp]),
     "fourtune_linear_workspace_bytes": (c_sz, [c_i64, ctypes.POINTER(FtLinear)]),
     "fourtune_linear_fwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), c_vp, ctypes.c_int, c_i64,
                                            c_vp, ctypes.c_int, c_vp, ctypes.POINTER(FtMx4),
@@ -153,6 +155,13 @@ class Mx4:
         scales = torch.empty(((rows + 31) // 32, cols // 32), dtype=torch.uint8, device=device)
         return Mx4(codes, scales, rows, cols)
 
+    @staticmethod
+    def empty_groups(rows: int, cols: int, device="cuda") -> "Mx4":
+        """Storage for the 1x32 group form: scales [rows x cols/32]."""
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
+        return Mx4(codes, scales, rows, cols)
+
     def struct(self) -> FtMx4:
         return FtMx4(_ptr(self.codes), _ptr(self.scales), self.rows, self.cols)
 
@@ -204,6 +213,17 @@ def fourtune_quantize(x: torch.Tensor, out: Mx4, stream=None, ld: Optional[int] 
     s = out.struct()
     _check(lib().fourtune_quantize(_ptr(x), _dt(x), rows, cols, ld, ctypes.byref(s),
                                    _stream(stream)))
+
+
+def fourtune_quantize_groups(x: torch.Tensor, out: Mx4, stream=None, ld: Optional[int] = None):
+    """1x32 groups: out.scales must be [rows x cols/32] (see Mx4.empty_groups)."""
+    rows, cols = x.shape
+    ld = x.stride(0) if ld is None else ld
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    s = out.struct()
+    _check(lib().fourtune_quantize_groups(_ptr(x), _dt(x), rows, cols, ld, ctypes.byref(s),
+                                          _stream(stream)))
 
 
 def fourtune_linear_workspace_bytes(m: int, L: Linear) -> int:

@@ -125,6 +125,25 @@ ft_status fourtune_quantize(const void* x, ft_dtype x_dt, int64_t rows, int64_t 
   return ok();
 }
 
+ft_status fourtune_quantize_groups(const void* x, ft_dtype x_dt, int64_t rows, int64_t cols, int64_t ld,
+                                   ft_mx4* out, void* stream) {
+  REQUIRE(dtype_ok(x_dt), FT_ERR_DTYPE, "quantize_groups: unknown dtype %d", (int)x_dt);
+  REQUIRE(rows >= 0 && cols >= 0, FT_ERR_SHAPE, "quantize_groups: negative size");
+  REQUIRE(cols % 32 == 0, FT_ERR_SHAPE, "quantize_groups: cols=%lld not a multiple of 32", (long long)cols);
+  REQUIRE(ld >= cols, FT_ERR_SHAPE, "quantize_groups: ld=%lld < cols=%lld", (long long)ld, (long long)cols);
+  REQUIRE((ld * (int64_t)elem_size(x_dt)) % 16 == 0, FT_ERR_ALIGN,
+          "quantize_groups: row stride of %lld bytes not a multiple of 16", (long long)(ld * elem_size(x_dt)));
+  REQUIRE(rows < (int64_t)65535 * 32, FT_ERR_UNSUPPORTED, "quantize_groups: rows=%lld too large", (long long)rows);
+  if (rows == 0 || cols == 0) return ok();
+  REQUIRE(x != nullptr, FT_ERR_NULL, "quantize_groups: NULL x");
+  REQUIRE(aligned16(x), FT_ERR_ALIGN, "quantize_groups: x not 16-byte aligned");
+  TRY(check_mx4(out, rows, cols, "quantize_groups: out"));
+  TRY(hip_check(ft::launch_quantize(x, x_dt == FT_BF16, rows, cols, ld, out->codes, out->scales,
+                                    static_cast<hipStream_t>(stream), true),
+                "quantize_groups launch"));
+  return ok();
+}
+
 }  // extern "C"
 
 namespace {

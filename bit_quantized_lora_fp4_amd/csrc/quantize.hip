@@ -11,6 +11,11 @@
 // (l%16)/4) combine their maxima with four butterfly steps (lane masks 1, 2, 16, 32).
 // Each lane then converts its 64 values with the hardware E2M1 conversion and writes
 // one 32-bit word (8 codes) per row: 16 lanes write 64 contiguous bytes of a row.
+//
+// GROUPS = true is the 1x32 form (one scale per row and 32 columns, the granularity
+// FourTune §4 "Impact of Quantization Granularity" compares the blocks against): the
+// same mapping, the maximum taken per row over the 4 lanes of a group (masks 1, 2),
+// scales stored [rows x cols/32].
 #include "common.h"
 
 namespace ft {
@@ -59,7 +64,7 @@ struct QuantIO<float> {
   }
 };
 
-template <typename T>
+template <typename T, bool GROUPS>
 __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ x, int64_t rows,
                                                   int64_t cols, int64_t ld,
                                                   uint8_t* __restrict__ codes,
@@ -78,6 +83,24 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ x, int64
   for (int i = 0; i < 8; ++i) {
     const int64_t row = r0 + 4 * i + rq;
     IO::load(x + row * ld + col, col_ok && row < rows, w[i]);
+  }
+  if constexpr (GROUPS) {
+    const int64_t cpitch = cols >> 1, spitch = cols >> 5;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t row = r0 + 4 * i + rq;
+      uint32_t m = IO::absmax(w[i]);
+      m = umax(m, shfl_xor_u32<1>(m));
+      m = umax(m, shfl_xor_u32<2>(m));
+      const uint32_t sb = scale_byte_from_amax(m);
+      uint32_t c = IO::codes(w[i], e8m0_to_f32_scale(sb));
+      if (sb == 0xFFu) c = 0;  // non-finite group: zero codes
+      if (col_ok && row < rows) {
+        *reinterpret_cast<uint32_t*>(codes + row * cpitch + (col >> 1)) = c;
+        if ((sub & 3) == 0) scales[row * spitch + (col >> 5)] = (uint8_t)sb;
+      }
+    }
+    return;
   }
   uint32_t amax = 0;
 #pragma unroll
@@ -102,14 +125,20 @@ __global__ __launch_bounds__(256) void k_quantize(const T* __restrict__ x, int64
 }
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld,
-                           uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+                           uint8_t* codes, uint8_t* scales, hipStream_t stream, bool groups) {
   if (rows == 0) return hipSuccess;
   dim3 grid((unsigned)((cols + 511) / 512), (unsigned)((rows + 31) / 32));
-  if (bf16)
-    hipLaunchKernelGGL(k_quantize<bf16_t>, grid, dim3(256), 0, stream,
+  if (bf16 && groups)
+    hipLaunchKernelGGL((k_quantize<bf16_t, true>), grid, dim3(256), 0, stream,
                        static_cast<const bf16_t*>(x), rows, cols, ld, codes, scales);
+  else if (bf16)
+    hipLaunchKernelGGL((k_quantize<bf16_t, false>), grid, dim3(256), 0, stream,
+                       static_cast<const bf16_t*>(x), rows, cols, ld, codes, scales);
+  else if (groups)
+    hipLaunchKernelGGL((k_quantize<float, true>), grid, dim3(256), 0, stream,
+                       static_cast<const float*>(x), rows, cols, ld, codes, scales);
   else
-    hipLaunchKernelGGL(k_quantize<float>, grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_quantize<float, false>), grid, dim3(256), 0, stream,
                        static_cast<const float*>(x), rows, cols, ld, codes, scales);
   return hipGetLastError();
 }

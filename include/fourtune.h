@@ -99,6 +99,15 @@ size_t ft_mx4_scales_bytes(int64_t rows, int64_t cols);
 ft_status fourtune_quantize(const void *x, ft_dtype x_dt, int64_t rows, int64_t cols,
                             int64_t ld, ft_mx4 *out, void *stream);
 
+/* fourtune_quantize_groups -- the 1x32 group form of the quantizer, for comparing
+ * granularities (FourTune §4, "Impact of Quantization Granularity": block-wise against
+ * group-wise scales). Each row's 32-column groups get a scale of their own, by the same
+ * rule as a block (E from the group's amax, E2M1 rounding, NaN/Inf group -> 0xFF and
+ * zero codes). Arguments as fourtune_quantize, except that out->scales holds
+ * [rows x cols/32] bytes, row-major. The layer's entry points use 32x32 blocks only. */
+ft_status fourtune_quantize_groups(const void *x, ft_dtype x_dt, int64_t rows, int64_t cols,
+                                   int64_t ld, ft_mx4 *out, void *stream);
+
 /* Workspace bytes needed by fourtune_linear_fwd and fourtune_linear_bwd for m rows.
  * The workspace is device scratch owned by the caller (16-byte aligned, contents
  * irrelevant, overwritten by every call; nothing in it outlives a call). Two calls

@@ -169,6 +169,40 @@ def quantize(T, rounder=e2m1_index_threshold):
     return codes.astype(np.uint8), scales
 
 
+def quantize_groups(T, rounder=e2m1_index_threshold):
+    """Quantize a 2-D tensor in 1x32 groups: each row's 32 consecutive columns share one
+    scale (the group-wise granularity FourTune §4 "Impact of Quantization Granularity"
+    compares the block-wise one against; the MX rule applies per group unchanged).
+
+    Returns (codes, scales): codes uint8 [rows, cols] as in ``quantize``; scales uint8
+    [rows, cols/32].
+    """
+    T = np.asarray(T, dtype=np.float64)
+    rows, cols = T.shape
+    if cols % BLOCK:
+        raise ValueError("cols must be a multiple of 32")
+    g = T.reshape(rows, cols // BLOCK, BLOCK)                 # [rows, ngroups, 32]
+    finite = np.isfinite(g).all(axis=2)                       # [rows, ngroups]
+    amax = np.where(finite, np.abs(np.where(np.isfinite(g), g, 0.0)).max(axis=2), 0.0)
+    E = shared_exponent(amax)
+    scales = np.where(finite, E + 127, NAN_SCALE).astype(np.uint8)
+    y = np.ldexp(np.where(np.isfinite(g), g, 0.0), -E[:, :, None])
+    idx = rounder(np.abs(y))
+    sign = np.signbit(y).astype(np.uint8) << 3
+    codes = (idx | sign) * finite[:, :, None].astype(np.uint8)
+    return codes.reshape(rows, cols).astype(np.uint8), scales
+
+
+def dequantize_groups(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Exact values of 1x32-group codes (scale byte 0xFF: NaN)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    mag = E2M1_GRID[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    sc = np.repeat(scales.astype(np.int64), BLOCK, axis=1)
+    out = np.ldexp(val, sc - 127)
+    return np.where(sc == NAN_SCALE, np.nan, out)
+
+
 def pack_codes(codes: np.ndarray) -> np.ndarray:
     """Two codes per byte: column 2j in the low nibble, column 2j+1 in the high one."""
     codes = np.asarray(codes, dtype=np.uint8)
