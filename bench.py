@@ -5,6 +5,7 @@
     python bench.py --ablation           (fusion ablation; one JSON line of its own)
     python bench.py --dit                (every linear of a FLUX-shaped DiT; one JSON line)
     python bench.py --granularity        (32x32 blocks vs 1x32 groups: error study; one JSON line)
+    python bench.py --precision          (the four precision configurations at c2; one JSON line)
 
 One step = the whole hot path once over one batch: the layer's forward (fused
 quantize + down-projection, 4-bit GEMM + up-projection) and backward (fused quantize +
@@ -56,6 +57,8 @@ def parse():
                     help="all linears of a FLUX-shaped DiT (synthetic weights), W4A4G4 vs bf16 LoRA")
     ap.add_argument("--granularity", action="store_true",
                     help="32x32 blocks vs 1x32 groups for X and dY: quantization error study")
+    ap.add_argument("--precision", action="store_true",
+                    help="W4A4G4 vs W4A16G4 / W4A4G16 / W4A16G16 at c2")
     ap.add_argument("--double-blocks", type=int, default=19)
     ap.add_argument("--single-blocks", type=int, default=38)
     return ap.parse_args()
@@ -397,6 +400,49 @@ def granularity(args):
     return 0
 
 
+# --------------------------------------------------------------------------- precision configurations
+def precision(args):
+    """The c2 linear's fwd+bwd in the four precision configurations of the pages'
+    ablation (FourTune §4 "Impact of Precision Configurations"; the pages measure
+    training quality there and note that only W4A4G4 uses 4-bit arithmetic throughout):
+    forward and backward times from graph replays, and the backbone product's rate."""
+    import torch
+    from bit_quantized_lora_fp4_amd import abi
+    from synth import workloads as wl
+
+    abi.lib()
+    case = wl.linear_case("c2")
+    m, k = case["X"].shape
+    n = case["R"].shape[0]
+    sets = build_sets(case, args.sets, torch, abi)
+    it = max(args.steps, 10)
+
+    def S(i):
+        return sets[i % len(sets)]
+
+    res = {}
+    for prec in ("W4A4G4", "W4A16G4", "W4A4G16", "W4A16G16"):
+        fwd = lambda i, p=prec: abi.fourtune_linear_fwd_prec(S(i)["L"], p, S(i)["x"], S(i)["y"], S(i)["xl"], S(i)["ws"])
+        bwd = lambda i, p=prec: abi.fourtune_linear_bwd_prec(S(i)["L"], p, S(i)["dy"], S(i)["x"], S(i)["xl"], S(i)["dx"],
+                                                             S(i)["da"], S(i)["db"], S(i)["ws"])
+        for i in range(args.warmup):
+            fwd(i)
+            bwd(i)
+        torch.cuda.synchronize()
+        tf, tb = time_graph(torch, fwd, it), time_graph(torch, bwd, it)
+        res[prec] = {"fwd_us": round(tf * 1e6, 2), "bwd_us": round(tb * 1e6, 2),
+                     "fwd_bwd_us": round((tf + tb) * 1e6, 2),
+                     "backbone_tflops": round(4.0 * m * n * k / (tf + tb) / 1e12, 1)}
+        log(f"[precision] {prec}: fwd {tf*1e6:.1f} us, bwd {tb*1e6:.1f} us")
+    base = res["W4A4G4"]["fwd_bwd_us"]
+    for p in res:
+        res[p]["slowdown_vs_w4a4g4"] = round(res[p]["fwd_bwd_us"] / base, 3)
+    print(json.dumps({"metric": "c2 linear fwd+bwd per precision configuration", "unit": "us",
+                      "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+                      "config": {"workload": "c2", "m": m, "n": n, "k": k}, **res}), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------------------- whole DiT
 HIDDEN, MLP_DIM, QKV_DIM = 3072, 12288, 9216
 DIT_RANK, DIT_STAB = 64, 32
@@ -619,6 +665,8 @@ def main():
         return dit(args)
     if args.granularity:
         return granularity(args)
+    if args.precision:
+        return precision(args)
     import torch
     from bit_quantized_lora_fp4_amd import abi
     from synth import workloads as wl

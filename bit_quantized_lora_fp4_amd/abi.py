@@ -90,6 +90,12 @@ _SIGS = {
                                                 ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_i64, c_vp,
                                                 ctypes.c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                                                 c_vp]),
+    "fourtune_linear_fwd_prec": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.c_int, c_vp,
+                                                ctypes.c_int, c_i64, c_vp, ctypes.c_int, c_vp, c_vp,
+                                                c_sz, c_vp]),
+    "fourtune_linear_bwd_prec": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.c_int, c_vp,
+                                                ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_i64, c_vp,
+                                                ctypes.c_int, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "fourtune_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fourtune_last_error": (ctypes.c_char_p, []),
 }
@@ -346,6 +352,28 @@ def fourtune_mlp_bwd_unfused(fc1: Linear, fc2: Linear, lora_fused: bool, dy: tor
                                           _ptr(pre_saved), _ptr(h_saved), _ptr(hl2_saved),
                                           x.shape[0], _ptr(dx), _dt(dx), _ptr(d_a1), _ptr(d_b1),
                                           _ptr(d_a2), _ptr(d_b2), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
+
+
+PREC = {"W4A4G4": 0, "W4A16G4": 1, "W4A4G16": 2, "W4A16G16": 3}
+
+
+def fourtune_linear_fwd_prec(L: Linear, prec: str, x: torch.Tensor, y: torch.Tensor,
+                             xl_saved: torch.Tensor, ws: torch.Tensor, stream=None):
+    s = L.struct()
+    _check(lib().fourtune_linear_fwd_prec(ctypes.byref(s), PREC[prec], _ptr(x), _dt(x), x.shape[0],
+                                          _ptr(y), _dt(y), _ptr(xl_saved), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
+
+
+def fourtune_linear_bwd_prec(L: Linear, prec: str, dy: torch.Tensor, x: torch.Tensor,
+                             xl_saved: torch.Tensor, dx: torch.Tensor,
+                             d_lora_a: Optional[torch.Tensor], d_lora_b: Optional[torch.Tensor],
+                             ws: torch.Tensor, stream=None):
+    s = L.struct()
+    _check(lib().fourtune_linear_bwd_prec(ctypes.byref(s), PREC[prec], _ptr(dy), _dt(dy), _ptr(x),
+                                          _dt(x), _ptr(xl_saved), x.shape[0], _ptr(dx), _dt(dx),
+                                          _ptr(d_lora_a), _ptr(d_lora_b), _ptr(ws), ws.numel(),
                                           _stream(stream)))
 
 

@@ -821,3 +821,101 @@ ft_status fourtune_mlp_bwd_unfused(const ft_linear* fc1, const ft_linear* fc2, i
 }
 
 }  // extern "C"
+
+// ================================================================ precision variants
+// FourTune §4 "Impact of Precision Configurations": the same layer with the activations
+// (A16) and/or the gradients (G16) kept in 16 bits (bf16) while the weight stays 4-bit.
+namespace {
+
+ft_status run_gemm_a16(const ft_linear* L, bool bwd, const void* act, ft_dtype act_dt, const void* low, int64_t m,
+                       void* out, ft_dtype out_dt, hipStream_t st, const char* what) {
+  ft::GemmA16Args g{};
+  g.act = act;
+  g.ld_act = bwd ? L->n : L->k;
+  g.b_codes = L->r.codes;
+  g.b_scales = L->r.scales;
+  g.M = m;
+  g.N = bwd ? L->k : L->n;
+  g.Kred = bwd ? L->n : L->k;
+  g.low = static_cast<const ft::bf16_t*>(low);
+  g.rt = (int)(L->rank + L->stab_rank);
+  g.up0 = static_cast<const ft::bf16_t*>(bwd ? L->lora_a : L->lora_b);
+  g.up1 = static_cast<const ft::bf16_t*>(bwd ? L->stab_down : L->stab_up);
+  g.up_split = (int)L->rank;
+  g.out = out;
+  g.ldo = g.N;
+  return hip_check(ft::launch_gemm_a16(g, act_dt == FT_BF16, bwd, out_dt == FT_BF16, st), what);
+}
+
+}  // namespace
+
+extern "C" {
+
+ft_status fourtune_linear_fwd_prec(const ft_linear* L, int prec, const void* x, ft_dtype x_dt, int64_t m, void* y,
+                                   ft_dtype y_dt, void* xl_saved, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "linear_fwd_prec";
+  REQUIRE(prec >= FT_PREC_W4A4G4 && prec <= FT_PREC_W4A16G16, FT_ERR_UNSUPPORTED, "%s: unknown precision %d", who,
+          prec);
+  if (prec == FT_PREC_W4A4G4 || prec == FT_PREC_W4A4G16)
+    return fourtune_linear_fwd(L, x, x_dt, m, y, y_dt, xl_saved, nullptr, ws, ws_bytes, stream);
+  TRY(check_linear(L, who));
+  REQUIRE(dtype_ok(x_dt) && dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m == 0) return ok();
+  TRY(check_m(m, L, who));
+  REQUIRE(m < (int64_t)65535 * 128, FT_ERR_UNSUPPORTED, "%s: m=%lld too large", who, (long long)m);
+  const int64_t rt = L->rank + L->stab_rank;
+  TRY(check_tensor(x, who, "x"));
+  TRY(check_tensor(y, who, "y"));
+  if (rt > 0) TRY(check_tensor(xl_saved, who, "xl_saved"));
+  const FwdLayout lay = fwd_layout(ws, m, L, false);
+  REQUIRE(lay.bytes == 0 || (ws != nullptr && ws_bytes >= lay.bytes), FT_ERR_WORKSPACE,
+          "%s: workspace of %zu bytes, %zu needed", who, ws_bytes, lay.bytes);
+  if (lay.bytes) REQUIRE(aligned16(ws), FT_ERR_ALIGN, "%s: workspace misaligned", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rt > 0)
+    TRY(run_quant_down(ft::QD_DOWN, L, true, x, x_dt == FT_BF16, m, L->k, nullptr, nullptr, xl_saved, lay.partials,
+                       st, "linear_fwd_prec down"));
+  TRY(run_gemm_a16(L, false, x, x_dt, xl_saved, m, y, y_dt, st, "linear_fwd_prec gemm_a16"));
+  return ok();
+}
+
+ft_status fourtune_linear_bwd_prec(const ft_linear* L, int prec, const void* dy, ft_dtype dy_dt, const void* x,
+                                   ft_dtype x_dt, const void* xl_saved, int64_t m, void* dx, ft_dtype dx_dt,
+                                   float* d_lora_a, float* d_lora_b, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "linear_bwd_prec";
+  REQUIRE(prec >= FT_PREC_W4A4G4 && prec <= FT_PREC_W4A16G16, FT_ERR_UNSUPPORTED, "%s: unknown precision %d", who,
+          prec);
+  if (prec == FT_PREC_W4A4G4 || prec == FT_PREC_W4A16G4)
+    return fourtune_linear_bwd(L, dy, dy_dt, x, x_dt, xl_saved, m, dx, dx_dt, d_lora_a, d_lora_b, nullptr, ws,
+                               ws_bytes, stream);
+  TRY(check_linear(L, who));
+  REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m == 0) return ok();
+  TRY(check_m(m, L, who));
+  REQUIRE(m < (int64_t)65535 * 128, FT_ERR_UNSUPPORTED, "%s: m=%lld too large", who, (long long)m);
+  const int64_t rt = L->rank + L->stab_rank;
+  TRY(check_tensor(dy, who, "dy"));
+  TRY(check_tensor(dx, who, "dx"));
+  if (L->rank > 0) {
+    TRY(check_tensor(x, who, "x"));
+    TRY(check_tensor(xl_saved, who, "xl_saved"));
+    TRY(check_tensor(d_lora_a, who, "d_lora_a"));
+    TRY(check_tensor(d_lora_b, who, "d_lora_b"));
+  }
+  const BwdLayout lay = bwd_layout(ws, m, L, false);
+  REQUIRE(ws != nullptr && ws_bytes >= lay.bytes, FT_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who,
+          ws_bytes, lay.bytes);
+  REQUIRE(aligned16(ws), FT_ERR_ALIGN, "%s: workspace misaligned", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rt > 0)
+    TRY(run_quant_down(ft::QD_DOWN, L, false, dy, dy_dt == FT_BF16, m, L->n, nullptr, nullptr, lay.GB, lay.partials,
+                       st, "linear_bwd_prec down"));
+  TRY(run_gemm_a16(L, true, dy, dy_dt, lay.GB, m, dx, dx_dt, st, "linear_bwd_prec gemm_a16"));
+  TRY(run_lora_grad(L, m, lay.GB, x, x_dt == FT_BF16, false, xl_saved, dy, dy_dt == FT_BF16, d_lora_a, d_lora_b,
+                    lay.partials, st, "linear_bwd_prec lora_grad"));
+  return ok();
+}
+
+}  // extern "C"

@@ -115,6 +115,27 @@ struct LoraGradArgs {
 
 hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream);
 
+// 16-bit activation x 4-bit weight GEMM (precision variants W4A16 / G16):
+//   forward : out[M x N] = bf16(act)[M x Kred] deq Q(R)^T + low[M x rt] U^T
+//   backward: out[M x N] = bf16(act)[M x Kred] deq Q(R)   + low[M x rt] D
+// with Q(R) the linear's weight ([N_lin x K_lin]: forward N = N_lin, Kred = K_lin;
+// backward N = K_lin, Kred = N_lin) and U / D split at up_split as in GemmArgs.
+struct GemmA16Args {
+  const void* act;          // [M x Kred] fp32 or bf16, row stride ld_act
+  int64_t ld_act;
+  const uint8_t* b_codes;   // Q(R) codes, contiguous rows
+  const uint8_t* b_scales;  // Q(R) block scales
+  int64_t M, N, Kred;
+  const bf16_t* low;        // [M x rt]
+  int rt;
+  const bf16_t* up0;
+  const bf16_t* up1;
+  int up_split;
+  void* out;                // [M x N] fp32 or bf16, row stride ldo
+  int64_t ldo;
+};
+hipError_t launch_gemm_a16(const GemmA16Args& g, bool act_bf16, bool trans_b, bool out_bf16, hipStream_t stream);
+
 // Unfused pieces for the fusion ablation (the fused path never uses them):
 //   out[M x C] = base[M x C] (bf16) + low[M x rt] * V, fp32 accumulation, one rounding
 //   forward : V = U^T, U row q = v0[q*r0 .. +r0] ++ v1[q*(rt-r0) .. +(rt-r0)] ([B | L2])

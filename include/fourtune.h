@@ -247,6 +247,29 @@ ft_status fourtune_mlp_bwd_unfused(const ft_linear *fc1, const ft_linear *fc2, i
                                    float *d_a2, float *d_b2, void *ws, size_t ws_bytes,
                                    void *stream);
 
+/* ---------------------------------------------------------------- precision variants
+ * FourTune §4 "Impact of Precision Configurations": W4A4G4 (the layer above), W4A16G4,
+ * W4A4G16 and W4A16G16. A16 keeps the activation X (as bf16(X)) instead of Q(X) in
+ * the forward's backbone product, G16 keeps bf16(dY) instead of Q(dY) in the
+ * backward's; the weight is Q(R) in every configuration. The 16-bit products run as
+ * bf16 MFMA on the weight dequantized exactly to bf16 as it is staged (only W4A4G4
+ * uses the 4-bit matrix cores); the low-rank branches, the LoRA gradients and the
+ * saved XL are as in fourtune_linear_fwd / _bwd, whose arguments and workspace
+ * (fourtune_linear_workspace_bytes) these take, plus `prec` (an ft_prec value). */
+typedef enum {
+  FT_PREC_W4A4G4 = 0,
+  FT_PREC_W4A16G4 = 1,
+  FT_PREC_W4A4G16 = 2,
+  FT_PREC_W4A16G16 = 3
+} ft_prec;
+ft_status fourtune_linear_fwd_prec(const ft_linear *L, int prec, const void *x, ft_dtype x_dt,
+                                   int64_t m, void *y, ft_dtype y_dt, void *xl_saved, void *ws,
+                                   size_t ws_bytes, void *stream);
+ft_status fourtune_linear_bwd_prec(const ft_linear *L, int prec, const void *dy, ft_dtype dy_dt,
+                                   const void *x, ft_dtype x_dt, const void *xl_saved, int64_t m,
+                                   void *dx, ft_dtype dx_dt, float *d_lora_a, float *d_lora_b,
+                                   void *ws, size_t ws_bytes, void *stream);
+
 /* Static text of a status code. */
 const char *fourtune_status_string(ft_status s);
 /* Detail of the last failing call on this thread ("" if none). */

@@ -238,3 +238,22 @@ def mlp_backward_unfused(dY, X, saved: dict, fc1: Linear, fc2: Linear, prec: Pre
     dP = _b(dH * gelu_tanh_grad(saved["P"]), prec)
     dX, dA1, dB1, _ = bwd(dP, X, saved["XL1"], fc1, prec)
     return dict(dX=dX, dA1=dA1, dB1=dB1, dA2=dA2, dB2=dB2, dH=dH, dP=dP)
+
+
+# ----------------------------------------------------------------------------------
+# Precision configurations (FourTune §4 "Impact of Precision Configurations")
+# ----------------------------------------------------------------------------------
+# W4A16 keeps the activation in 16 bits in the forward's backbone product, G16 the
+# gradient in the backward's; the weight is Q(R) throughout. The 16-bit type is bf16,
+# the pipeline's activation type (the pages name only the bit widths).
+def linear_forward_prec(X, lin: Linear, a16: bool, prec: Prec = EXACT):
+    """Returns (Y, XL): Y = A deq Q(R)^T + XL U^T with A = bf16(X) (a16) or deq Q(X)."""
+    X = np.asarray(X, dtype=np.float64)
+    return linear_forward(X, lin, prec, Xq=_b(X, prec) if a16 else None)
+
+
+def linear_backward_prec(G, X, XL, lin: Linear, g16: bool, prec: Prec = EXACT):
+    """Returns (dX, dA, dB, GB): dX = Gv deq Q(R) + GB D with Gv = bf16(G) (g16) or
+    deq Q(G); dA, dB, GB as in the W4A4G4 backward."""
+    G = np.asarray(G, dtype=np.float64)
+    return linear_backward(G, X, XL, lin, prec, Gq=_b(G, prec) if g16 else None)
