@@ -69,3 +69,60 @@ def test_quantize_validation_before_launch():
     assert _q(x, abi.FT_BF16, 64, 64, 64, bad) == 2            # out shape mismatch
     assert "rows" in abi.fourtune_last_error() or "expected" in abi.fourtune_last_error()
     assert _q(None, abi.FT_BF16, 0, 64, 64, None) == 0         # empty: no-op
+
+
+def _fake_linear(n=256, k=256, r=16, s=16, codes=4096):
+    rq = abi.FtMx4(ctypes.c_void_p(codes), ctypes.c_void_p(codes + (1 << 20)), n, k)
+    p = ctypes.c_void_p(1 << 24)
+    return abi.FtLinear(rq, p, p, p, p, n, k, r, s)
+
+
+def test_new_entry_points_validate_before_launch():
+    """The ablation, precision and group-quantizer entry points reject bad arguments
+    with FT_ERR_* codes before touching the GPU (fake device addresses are never used)."""
+    L = abi.lib()
+    lin = _fake_linear()
+    x, y, xl, ws = (ctypes.c_void_p(1 << 26), ctypes.c_void_p(1 << 27), ctypes.c_void_p(1 << 28),
+                    ctypes.c_void_p(1 << 29))
+    # precision variants: unknown configuration, NULL input, small workspace, bad dtype
+    assert L.fourtune_linear_fwd_prec(ctypes.byref(lin), 9, x, abi.FT_BF16, 64, y, abi.FT_BF16, xl, ws, 1 << 30,
+                                      None) == 6
+    assert L.fourtune_linear_fwd_prec(ctypes.byref(lin), 1, None, abi.FT_BF16, 64, y, abi.FT_BF16, xl, ws, 1 << 30,
+                                      None) == 1
+    assert L.fourtune_linear_bwd_prec(ctypes.byref(lin), 3, x, abi.FT_BF16, x, abi.FT_BF16, xl, 64, y, abi.FT_BF16,
+                                      y, y, ws, 16, None) == 5
+    assert L.fourtune_linear_fwd_prec(ctypes.byref(lin), 1, x, 5, 64, y, abi.FT_BF16, xl, ws, 1 << 30, None) == 3
+    # unfused linear: misaligned input, NULL saved XL, workspace too small
+    assert L.fourtune_linear_fwd_unfused(ctypes.byref(lin), ctypes.c_void_p((1 << 26) + 8), abi.FT_BF16, 64, y,
+                                         abi.FT_BF16, xl, ws, 1 << 30, None) == 4
+    assert L.fourtune_linear_fwd_unfused(ctypes.byref(lin), x, abi.FT_BF16, 64, y, abi.FT_BF16, None, ws, 1 << 30,
+                                         None) == 1
+    assert L.fourtune_linear_bwd_unfused(ctypes.byref(lin), x, abi.FT_BF16, x, abi.FT_BF16, xl, 64, y, abi.FT_BF16,
+                                         y, y, ws, 16, None) == 5
+    # unfused MLP: fc1's outputs must match fc2's inputs
+    fc2 = _fake_linear(n=256, k=512)
+    assert L.fourtune_mlp_fwd_unfused(ctypes.byref(lin), ctypes.byref(fc2), 0, x, abi.FT_BF16, 64, y, abi.FT_BF16,
+                                      xl, y, y, xl, ws, 1 << 30, None) == 2
+    # ranks that are not multiples of 16
+    odd = _fake_linear(r=8, s=24)
+    assert L.fourtune_linear_fwd_prec(ctypes.byref(odd), 1, x, abi.FT_BF16, 64, y, abi.FT_BF16, xl, ws, 1 << 30,
+                                      None) == 2
+    # group quantizer: as the block quantizer
+    out = abi.FtMx4(ctypes.c_void_p(4096), ctypes.c_void_p(8192), 64, 64)
+    assert L.fourtune_quantize_groups(x, abi.FT_BF16, 64, 48, 48, ctypes.byref(out), None) == 2
+    assert L.fourtune_quantize_groups(None, abi.FT_BF16, 64, 64, 64, ctypes.byref(out), None) == 1
+    assert L.fourtune_quantize_groups(None, abi.FT_BF16, 0, 64, 64, None, None) == 0
+    # workspace sizes are well defined without a GPU
+    assert abi.fourtune_ablation_workspace_bytes(4608, abi.Linear(
+        abi.Mx4(None, None, 3072, 3072), *[_FakeT((32, 3072))] * 4)) > 0
+
+
+class _FakeT:
+    """Stand-in for a tensor in the workspace-size query (only its shape is read)."""
+
+    def __init__(self, shape):
+        self.shape = shape
+        self.is_cuda = True
+
+    def data_ptr(self):
+        return 1 << 24
