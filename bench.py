@@ -6,6 +6,7 @@
     python bench.py --dit                (every linear of a FLUX-shaped DiT; one JSON line)
     python bench.py --granularity        (32x32 blocks vs 1x32 groups: error study; one JSON line)
     python bench.py --precision          (the four precision configurations at c2; one JSON line)
+    python bench.py --gemm-sweep         (both 4-bit GEMMs of every linear of c2..c5; one JSON line)
 
 One step = the whole hot path once over one batch: the layer's forward (fused
 quantize + down-projection, 4-bit GEMM + up-projection) and backward (fused quantize +
@@ -59,6 +60,8 @@ def parse():
                     help="32x32 blocks vs 1x32 groups for X and dY: quantization error study")
     ap.add_argument("--precision", action="store_true",
                     help="W4A4G4 vs W4A16G4 / W4A4G16 / W4A16G16 at c2")
+    ap.add_argument("--gemm-sweep", action="store_true",
+                    help="4-bit GEMM TFLOPS and MXFP4-peak fraction for every linear of c2..c5")
     ap.add_argument("--double-blocks", type=int, default=19)
     ap.add_argument("--single-blocks", type=int, default=38)
     return ap.parse_args()
@@ -400,6 +403,97 @@ def granularity(args):
     return 0
 
 
+# --------------------------------------------------------------------------- GEMM sweep
+def time_graph_stats(torch, fn, per_graph=10, replays=20):
+    """Per-launch time of fn(i) from `replays` replays of a graph of `per_graph`
+    back-to-back launches: (median, p10, p90) over the replays, in seconds."""
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / 1000.0 / per_graph)
+    ts = np.array(ts)
+    return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
+
+
+def gemm_sweep(args):
+    """Both 4-bit GEMM kernels (forward Q(X)Q(R)^T + XL U^T; backward Q(dY)Q(R) + GB D)
+    of every linear of c2..c5 at full size: TFLOP/s of the 2*M*N*K backbone flops and
+    the fraction of the dense MXFP4 peak, median / p10 / p90 over graph replays. Codes
+    and block scales are random bytes (every nibble is an E2M1 code; scale bytes kept
+    in 110..140), the low-rank operands random bf16: the kernels' time does not depend
+    on the values. Input sets rotate so that operands are not cache-resident."""
+    import torch
+    from bit_quantized_lora_fp4_amd import abi
+    from synth import workloads as wl
+
+    abi.lib()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+
+    def codes(rows, cols):
+        q = abi.Mx4.empty(rows, cols)
+        q.codes.copy_(torch.randint(0, 256, q.codes.shape, generator=gen, device="cuda", dtype=torch.int32).to(torch.uint8))
+        q.scales.copy_(torch.randint(110, 141, q.scales.shape, generator=gen, device="cuda", dtype=torch.int32).to(torch.uint8))
+        return q
+
+    def bf(shape):
+        return (torch.randn(shape, generator=gen, device="cuda") * 0.01).to(torch.bfloat16)
+
+    res = {}
+    for key in ("c2", "c3", "c4", "c5"):
+        spec = wl.WORKLOADS[key]
+        m = spec.m
+        lins = []
+        for ls in spec.layers:
+            if isinstance(ls, wl.LinearSpec):
+                lins.append((ls.name, ls.n, ls.k, ls.r, ls.s))
+            else:
+                lins += [(ls.name + ".fc1", ls.f, ls.d, ls.r, ls.s), (ls.name + ".fc2", ls.d, ls.f, ls.r, ls.s)]
+        for name, n, k, r, s in lins:
+            nsets = 2 if m * max(n, k) > 1 << 27 else 4
+            sets = []
+            for _ in range(nsets):
+                L = abi.Linear(codes(n, k), bf((r, k)), bf((n, r)), bf((s, k)), bf((n, s)))
+                sets.append(dict(L=L, xq=codes(m, k), gq=codes(m, n), xl=bf((m, r + s)), gb=bf((m, r + s)),
+                                 y=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+                                 dx=torch.empty((m, k), dtype=torch.bfloat16, device="cuda")))
+            torch.cuda.synchronize()
+            S = lambda i: sets[i % nsets]
+            f = time_graph_stats(torch, lambda i: abi.fourtune_gemm_fwd(S(i)["L"], S(i)["xq"], S(i)["xl"], S(i)["y"]))
+            b = time_graph_stats(torch, lambda i: abi.fourtune_gemm_bwd(S(i)["L"], S(i)["gq"], S(i)["gb"], S(i)["dx"]))
+            flops = 2.0 * m * n * k
+            row = {"m": m, "n": n, "k": k, "rt": r + s}
+            for tag, (med, p10, p90) in (("fwd", f), ("bwd", b)):
+                row[tag] = {"us_median": round(med * 1e6, 2), "us_p10": round(p10 * 1e6, 2), "us_p90": round(p90 * 1e6, 2),
+                            "tflops": round(flops / med / 1e12, 1), "frac": round(flops / med / 1e12 / PEAK_MXFP4_TFLOPS, 4)}
+            row["fwd_bwd_frac"] = round(2 * flops / (f[0] + b[0]) / 1e12 / PEAK_MXFP4_TFLOPS, 4)
+            res[f"{key}.{name}"] = row
+            log(f"[gemm-sweep] {key}.{name} m={m} n={n} k={k}: fwd {f[0]*1e6:.1f} us, bwd {b[0]*1e6:.1f} us, "
+                f"{row['fwd_bwd_frac']*100:.1f}% of peak")
+            del sets
+            torch.cuda.empty_cache()
+    print(json.dumps({"metric": "4-bit GEMM kernels: 2*M*N*K / time, fraction of dense MXFP4 peak",
+                      "unit": "TFLOP/s", "peak": PEAK_MXFP4_TFLOPS, "n_gpus": 1, "data": "synthetic codes",
+                      **res}), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------------------- precision configurations
 def precision(args):
     """The c2 linear's fwd+bwd in the four precision configurations of the pages'
@@ -644,7 +738,13 @@ def cpu_baseline(case, seconds):
     except Exception:  # noqa: BLE001 - report what is known
         pass
     flops = 4.0 * rows * n * k * reps
-    return dict(value=round(flops / el / 1e12, 5), unit="TFLOP/s",
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg.get("Build Dependencies", {}).get("blas", {}).get("name")
+    except Exception:  # noqa: BLE001 - report what is known
+        pass
+    return dict(value=round(flops / el / 1e12, 5), unit="TFLOP/s", blas=blas,
                 cores=threads or len(os.sched_getaffinity(0)), kind="oracle",
                 sample=f"fwd+bwd of the same linear on the first {rows} of {case['X'].shape[0]} "
                        f"token rows, {reps} repetitions in {el:.1f} s (numpy fp64)")
@@ -667,6 +767,8 @@ def main():
         return granularity(args)
     if args.precision:
         return precision(args)
+    if args.gemm_sweep:
+        return gemm_sweep(args)
     import torch
     from bit_quantized_lora_fp4_amd import abi
     from synth import workloads as wl
