@@ -48,7 +48,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c2")
-    ap.add_argument("--sets", type=int, default=4, help="rotated input/weight sets")
+    ap.add_argument("--sets", type=int, default=20,
+                    help="rotated input/weight sets (20 at c2: the per-kernel timings stream more "
+                         "than twice the 256 MB Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true")
