@@ -550,12 +550,9 @@ ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const voi
 
   TRY(run_quant_down(ft::QD_QUANT, fc1, true, x, x_dt == FT_BF16, m, d, lay.xq_codes, lay.xq_scales, xl1_saved,
                      lay.partials, st, "mlp_fwd quant_down(X)"));
-  Epi e;
-  e.kind = ft::GEMM_EPI_GELU_Q; e.q_codes = hq_codes; e.q_scales = hq_scales;
-  TRY(run_gemm_fwd(fc1, lay.xq_codes, lay.xq_scales, xl1_saved, m, pre_saved, FT_BF16, st, e));
-  if (fc2->rank + fc2->stab_rank > 0)
-    TRY(run_quant_down(ft::QD_GELU_DOWN, fc2, true, pre_saved, true, m, fdim, nullptr, nullptr, hl2_saved,
-                       lay.partials, st, "mlp_fwd down(GELU(P))"));
+  TRY(run_gemm_fwd(fc1, lay.xq_codes, lay.xq_scales, xl1_saved, m, pre_saved, FT_BF16, st));
+  TRY(run_quant_down(ft::QD_GELU_QUANT, fc2, true, pre_saved, true, m, fdim, hq_codes, hq_scales, hl2_saved,
+                     lay.partials, st, "mlp_fwd gelu_quant_down(P)"));
   TRY(run_gemm_fwd(fc2, hq_codes, hq_scales, hl2_saved, m, y, y_dt, st));
   return ok();
 }

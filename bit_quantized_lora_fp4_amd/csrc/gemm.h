@@ -32,17 +32,18 @@ struct GemmArgs {
   int up_split;
   void* out;                // [M x N] fp32 or bf16, row stride ldo
   int64_t ldo;
-  // MLP epilogues (bf16 output only; FourTune §3.3 "MLP Fusion"):
-  //   GEMM_EPI_GELU_Q : out = P^ = bf16(result); Q(GELU(P^)) -> q_codes/q_scales
+  // MLP backward epilogue (transposed GEMM, bf16 output; FourTune §3.3 "MLP Fusion"):
   //   GEMM_EPI_DGELU_Q: dP = result * GELU'(pre); out = bf16(dP); Q(dP) -> q_codes/q_scales
   //                     (pre = the saved P^ [M x N] bf16, row stride N)
+  // (The forward's GELU + Q(H) runs in the quantize + down-projection pass over P^,
+  // QD_GELU_QUANT.)
   int epi;
   const bf16_t* pre;
   uint8_t* q_codes;         // [M x N/2]
   uint8_t* q_scales;        // [ceil(M/32) x N/32]
 };
 
-enum { GEMM_EPI_NONE = 0, GEMM_EPI_GELU_Q = 1, GEMM_EPI_DGELU_Q = 2 };
+enum { GEMM_EPI_NONE = 0, GEMM_EPI_DGELU_Q = 2 };
 
 hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipStream_t stream);
 // Longest reduction the GEMM supports (its block scales are staged in LDS once).
@@ -57,9 +58,9 @@ constexpr int64_t GEMM_MAX_KRED = 16384;
 // The K range is split S = quant_down_splits(M, K, rt) ways; with S > 1 the launch
 // needs quant_down_partial_bytes(M, K, r0, rt) bytes of fp32 partials, which a second
 // kernel sums in a fixed order.
-// mode: QD_QUANT (as above); QD_GELU_DOWN: no quantization, the down-projection reads
-// bf16(GELU(x)) (x = the saved P^, bf16); QD_DOWN: no quantization.
-enum { QD_QUANT = 0, QD_GELU_DOWN = 1, QD_DOWN = 2 };
+// mode: QD_QUANT (as above); QD_DOWN: no quantization; QD_GELU_QUANT: x = the saved
+// FC1 output P^ (bf16), H = GELU(P^) in fp32 -> Q(H), low = bf16(bf16(H) D^T).
+enum { QD_QUANT = 0, QD_DOWN = 2, QD_GELU_QUANT = 3 };
 struct QuantDownArgs {
   int mode;
   const void* x;

@@ -701,8 +701,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 
   // ---------------------------------------------------------------- MLP epilogues
   // backward (FC2's dX GEMM): dP = dH * GELU'(P^) in place, Q(dP) from the fp32 values;
-  // the store below then writes bf16(dP). The forward epilogue (Q(GELU(P^))) runs after
-  // the store, from the bf16 P^ the store staged in LDS.
+  // the store below then writes bf16(dP). (dH exists only here, in fp32: moving this
+  // step out of the GEMM would mean storing dH.)
   if constexpr (EPI == GEMM_EPI_DGELU_Q) {
     const bufres rqc = make_buf(g.q_codes, (uint64_t)g.M * (g.N >> 1));
     const bufres rqs = make_buf(g.q_scales, (uint64_t)((g.M + 31) >> 5) * (g.N >> 5));
@@ -782,39 +782,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       if (row < g.M && col < g.N)  // streaming store: the output is not re-read here
         __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(reinterpret_cast<bf16_t*>(g.out) + row * g.ldo + col));
     }
-    if constexpr (EPI == GEMM_EPI_GELU_Q) {
-      // FC1 forward: H = GELU(P^) from the staged bf16 P^ (the stored values), then Q(H)
-      // per 32x32 block: lane l takes row l%32 of the block and its 16 columns
-      // 16*(l/32) .. +16, so its 8 code bytes are contiguous.
-      const bufres rqc = make_buf(g.q_codes, (uint64_t)g.M * (g.N >> 1));
-      const bufres rqs = make_buf(g.q_scales, (uint64_t)((g.M + 31) >> 5) * (g.N >> 5));
-#pragma unroll 1
-      for (int t = 0; t < TI * TJ; ++t) {
-        const int j = t >> 2, i = t & 3;
-        const int lr = 32 * j + (lane & 31), lc = 32 * i + 16 * half;
-        const v4i a = lds_read_b128(wbuf + wofs(lr, lc * 2));
-        const v4i b = lds_read_b128(wbuf + wofs(lr, lc * 2 + 16));
-        const uint32_t wd[8] = {(uint32_t)a.x, (uint32_t)a.y, (uint32_t)a.z, (uint32_t)a.w,
-                                (uint32_t)b.x, (uint32_t)b.y, (uint32_t)b.z, (uint32_t)b.w};
-        float h[16];
-        uint32_t m = 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          h[2 * q] = gelu_f(bf16_lo(wd[q]));
-          h[2 * q + 1] = gelu_f(bf16_hi(wd[q]));
-          m = umax(m, umax(__builtin_bit_cast(uint32_t, h[2 * q]) & 0x7FFFFFFFu,
-                           __builtin_bit_cast(uint32_t, h[2 * q + 1]) & 0x7FFFFFFFu));
-        }
-        const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
-        const float scale = e8m0_to_f32_scale(sb);
-        v2i cw = {(int)cvt8_f32(h, scale), (int)cvt8_f32(h + 8, scale)};
-        if (sb == 0xFFu) cw = v2i{0, 0};
-        const int64_t brow = orow0 + 32 * j, row = brow + (lane & 31), col0 = ocol0 + 32 * i;
-        const bool blk_ok = brow < g.M && col0 < g.N;
-        buf_store8(rqc, sel_off(blk_ok && row < g.M, (uint32_t)(row * (g.N >> 1) + ((col0 + 16 * half) >> 1))), cw);
-        buf_store1(rqs, sel_off(blk_ok && lane == 0, (uint32_t)((brow >> 5) * (g.N >> 5) + (col0 >> 5))), sb);
-      }
-    }
   } else {
     // fp32: two passes of 64 rows (64 x 512 bytes per wave)
 #pragma unroll
@@ -853,15 +820,12 @@ static_assert(GEMM_MAX_KRED == MAX_NKB * 32, "scale staging bound");
 hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipStream_t stream) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (g.Kred > GEMM_MAX_KRED) return hipErrorInvalidValue;
-  if (g.epi != GEMM_EPI_NONE && (!out_bf16 || g.q_codes == nullptr || g.q_scales == nullptr ||
-                                 (g.epi == GEMM_EPI_DGELU_Q && g.pre == nullptr) ||
-                                 (g.epi == GEMM_EPI_GELU_Q) == trans_b))
+  if (g.epi != GEMM_EPI_NONE && (g.epi != GEMM_EPI_DGELU_Q || !out_bf16 || !trans_b || g.q_codes == nullptr ||
+                                 g.q_scales == nullptr || g.pre == nullptr))
     return hipErrorInvalidValue;
   const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
   dim3 grid(tiles), block(256);
-  if (g.epi == GEMM_EPI_GELU_Q) {
-    hipLaunchKernelGGL((k_gemm_mx4<false, true, GEMM_EPI_GELU_Q>), grid, block, 0, stream, g);
-  } else if (g.epi == GEMM_EPI_DGELU_Q) {
+  if (g.epi == GEMM_EPI_DGELU_Q) {
     hipLaunchKernelGGL((k_gemm_mx4<true, true, GEMM_EPI_DGELU_Q>), grid, block, 0, stream, g);
   } else if (!trans_b) {
     if (out_bf16)

@@ -211,7 +211,7 @@ __device__ __forceinline__ void lds_tr_tiles(const lds_char* sd, int b, int lane
 template <typename T, int TP, bool UCOLS, int MODE>
 __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   static_assert(TP % 2 == 0, "rank + stab_rank is a multiple of 32");
-  constexpr int NS = MODE == QD_QUANT ? QD_STORES : 0;  // stores per chunk
+  constexpr int NS = (MODE == QD_QUANT || MODE == QD_GELU_QUANT) ? QD_STORES : 0;  // stores per chunk
   constexpr int RT = 16 * TP;
   constexpr int WAVE_LDS = UCOLS ? 2 * UStage<TP>::BYTES : 0;
   constexpr int RED = QD_WAVES * 4 * TP * 4 * 64 * 4;
@@ -256,6 +256,63 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   // ---- one chunk: down-projection MFMAs, then the quantization of its four blocks
   auto work = [&](const XChunk<T>& x, const DChunk<TP>& d, const lds_char* sd, int64_t ch) {
     const int64_t c0 = cstart(ch);
+    if constexpr (MODE == QD_GELU_QUANT) {
+      // x is the saved FC1 output P^ (bf16). H = GELU(P^) in fp32 for every element:
+      // Q(H) is decided on these fp32 values, bf16(H) is the down-projection operand
+      float hv[4][2][8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint32_t w[4] = {(uint32_t)x.v[g][b].x, (uint32_t)x.v[g][b].y, (uint32_t)x.v[g][b].z,
+                                 (uint32_t)x.v[g][b].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hv[g][b][2 * e] = gelu_f(bf16_lo(w[e]));
+            hv[g][b][2 * e + 1] = gelu_f(bf16_hi(w[e]));
+          }
+        }
+      if constexpr (TP > 0) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          v4i xop[4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            xop[g] = v4i{(int)pack_bf16x2(hv[g][b][0], hv[g][b][1]), (int)pack_bf16x2(hv[g][b][2], hv[g][b][3]),
+                         (int)pack_bf16x2(hv[g][b][4], hv[g][b][5]), (int)pack_bf16x2(hv[g][b][6], hv[g][b][7])};
+#pragma unroll
+          for (int t = 0; t < TP; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) acc[g][t] = mfma16(d.v[t][b], xop[g], acc[g][t]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int64_t bc = c0 + 32 * b;
+          const bool bok = bc < a.K;
+          uint32_t m = 0;
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = umax(m, __builtin_bit_cast(uint32_t, hv[2 * h + q][b][e]) & 0x7FFFFFFFu);
+          const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
+          const float scale = e8m0_to_f32_scale(sb);
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int g = 2 * h + q;
+            const int64_t row = r0 + 16 * g + lr;
+            uint32_t cw = cvt8_f32(hv[g][b], scale);
+            if (sb == 0xFFu) cw = 0;
+            buf_store4(rcodes, sel_off(bok && row_ok[g], (uint32_t)(row * cpitch + ((bc + 8 * lq) >> 1))), cw);
+          }
+          buf_store1(rscales,
+                     sel_off(bok && lane == 0 && r0 + 32 * h < a.M, (uint32_t)((r0 / 32 + h) * nkb + (bc >> 5))),
+                     sb);
+        }
+      return;
+    }
     if constexpr (TP > 0) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -263,9 +320,6 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           xop[g] = x.operand(g, b);
-          if constexpr (MODE == QD_GELU_DOWN)  // bf16(GELU(P^)), P^ the saved FC1 output
-            xop[g] = v4i{(int)gelu_bf16x2((uint32_t)xop[g].x), (int)gelu_bf16x2((uint32_t)xop[g].y),
-                         (int)gelu_bf16x2((uint32_t)xop[g].z), (int)gelu_bf16x2((uint32_t)xop[g].w)};
         }
         v4i dop[TP];
         if constexpr (UCOLS) {
@@ -472,9 +526,9 @@ hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t st
   const int S = quant_down_splits(a.M, a.K, a.rt);
   if (S > 1 && a.partials == nullptr) return hipErrorInvalidValue;
   hipError_t e;
-  if (a.mode == QD_GELU_DOWN) {  // the saved FC1 output P^: bf16, [A2; L1_2] rows
-    if (!x_bf16 || a.u_cols || tp == 0) return hipErrorInvalidValue;
-    e = launch_t<bf16_t, false, QD_GELU_DOWN>(a, tp, S, stream);
+  if (a.mode == QD_GELU_QUANT) {  // the saved P^: Q(GELU(P^)) and [A2; L1_2] down
+    if (!x_bf16 || a.u_cols) return hipErrorInvalidValue;
+    e = launch_t<bf16_t, false, QD_GELU_QUANT>(a, tp, S, stream);
   } else if (a.mode == QD_DOWN) {  // down-projection alone, either side
     if (tp == 0) return hipErrorInvalidValue;
     if (a.u_cols)

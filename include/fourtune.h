@@ -9,8 +9,7 @@
  * (A, B). Quantization is block-wise with block-local scales so that the backward
  * can read the same 4-bit weight transposed (§3.2). Quantization is fused with the
  * down-projections, and the 4-bit GEMM with the up-projections (§3.3 "LoRA Fusion");
- * in an MLP the FC1 GEMM is fused with GELU and the quantization of FC2's input
- * (§3.3 "MLP Fusion").
+ * in an MLP, GELU is fused with the quantization of FC2's input (§3.3 "MLP Fusion").
  *
  * Conventions for every entry point
  *   - Row-major storage everywhere; nn.Linear layout: W is [out x in], Y = X W^T.
@@ -170,10 +169,10 @@ size_t fourtune_mlp_workspace_bytes(int64_t m, const ft_linear *fc1, const ft_li
 /* fourtune_mlp_fwd -- FC1 -> GELU (tanh form) -> FC2 (FourTune §3.3 "MLP Fusion").
  * fc1: d -> f, fc2: f -> d (fc1->n == fc2->k). Kernels, in order:
  *   1. one pass over X: Q(X) and XL1 = bf16(X^ [A1;L1_1]^T)            (§3.3 "LoRA Fusion")
- *   2. FC1's 4-bit GEMM + up-projection; its epilogue stores P^ = bf16(FC1 output),
- *      forms H = GELU(P^) in fp32 and writes FC2's 4-bit operand Q(H); H itself is
- *      never written to memory                                          (§3.3 "MLP Fusion")
- *   3. HL2 = bf16(bf16(GELU(P^)) [A2;L1_2]^T) from the saved P^
+ *   2. FC1's 4-bit GEMM + up-projection, storing P^ = bf16(FC1 output)
+ *   3. one pass over P^: H = GELU(P^) in fp32, FC2's 4-bit operand Q(H) and
+ *      HL2 = bf16(bf16(H) [A2;L1_2]^T); H itself is never written to memory
+ *                                                                       (§3.3 "MLP Fusion")
  *   4. FC2's 4-bit GEMM + up-projection: y = Q(H) Q(R2)^T + HL2 [B2|L2_2]^T.
  *   x         [m x d] fp32 or bf16 (x_dt), contiguous
  *   y         [m x fc2->n] fp32 or bf16 (y_dt), overwritten
