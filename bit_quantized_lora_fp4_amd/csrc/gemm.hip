@@ -24,7 +24,9 @@
 // MFMAs; a 4-byte touch per line pulls the step after that into L2. The block scales
 // of the workgroup's rows and columns for the whole reduction are staged into LDS
 // once, before the main loop. Each stage is its own LDS object, so the compiler knows
-// which loads a fragment read can alias.
+// which loads a fragment read can alias. The up-projection's operands (its first 64
+// low-rank columns) arrive the same way: the last step loads them into the stage it
+// frees, and their bf16 MFMAs run after the loop.
 //
 // Operand order. The MFMA's first operand is the Q(R) side (output columns), the second
 // the activation side (output rows): a lane's accumulator registers 4g..4g+3 then hold
@@ -36,6 +38,7 @@
 // (first-operand index, second-operand index). The bf16 MFMA 32x32x16 has the same
 // accumulator layout, 8 bf16 per lane at reduction offset (l/32)*8.
 #include "common.h"
+#include <type_traits>
 #include <utility>
 
 #include "gemm.h"
@@ -244,18 +247,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     }
   }
   // segment i of the activation tile (part 0) or of the R tile (part 1)
+  // The stage loads' sources are loop-carried: before the last step they are switched
+  // to the up-projection's operands (switch_to_low below), which that step then loads
+  // into the stage it frees. Past the reduction's end the offsets go out of range, so
+  // no step needs a "live" test of its own.
+  bufres src_a = ra, src_r = rr;
+  int kred_eff = (int)Kred;
   auto issue_part = [&](lds_char* st, int kt, int i, int part) __attribute__((always_inline)) {
-    const bool live = kt < KT;
     const int q = wave * SEGS + i;
     if (part == 0) {
-      const bool ka = live && a_ok[i] && (int64_t)kt * BK + a_k[i] < Kred;
-      buf_load16_lds(ra, st + q * 1024, sel_off(ka, a_base[i] + (uint32_t)kt * (BK / 2)));
+      const bool ka = a_ok[i] && kt * BK + a_k[i] < kred_eff;
+      buf_load16_lds(src_a, st + q * 1024, sel_off(ka, a_base[i] + (uint32_t)kt * (BK / 2)));
     } else {
-      const bool kr = live && r_ok[i] && (int64_t)kt * BK + r_k[i] < Kred;
+      const bool kr = r_ok[i] && kt * BK + r_k[i] < kred_eff;
       uint32_t ro;
       if constexpr (!TRANS_B) ro = r_base[i] + (uint32_t)kt * (BK / 2);
       else ro = r_base[i] + (uint32_t)((int64_t)kt * BK * g.b_pitch);
-      buf_load16_lds(rr, st + TILE_BYTES + q * 1024, sel_off(kr, ro));
+      buf_load16_lds(src_r, st + TILE_BYTES + q * 1024, sel_off(kr, ro));
     }
   };
   auto issue_stage = [&](lds_char* st, int kt) {
@@ -465,6 +473,71 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     xs[0] = a.x, xs[1] = a.y, xs[2] = a.z, xs[3] = a.w;
     rs[0] = r.x, rs[1] = r.y, rs[2] = r.z, rs[3] = r.w;
   };
+  // ---- operands of the up-projection's first 64 low-rank columns. They are loaded by
+  // the last reduction step into the stage it frees, in place of a next step's codes,
+  // so their latency hides behind that step's MFMAs (loaded ahead of stage 0 instead,
+  // they delayed the first step by their own round trip). `low` = XL (forward) or GB
+  // (backward), [M x rt] bf16; the up side is [B | L2] rows (forward, row = output
+  // column; the first up_split values from up0, row stride up0_ld, the rest from up1)
+  // or [A; L1] rows (backward, row j = reduction index: up0 row j for j < up_split,
+  // else up1 row j - up_split). Stage layouts:
+  //   low side and forward up side: unit-major, the 16-byte unit c (low-rank columns
+  //   8c .. 8c+7) of tile row r at 4096c + 16r, one load instruction per 64 rows of a
+  //   unit; rank and stab_rank are multiples of 16, so a unit never straddles the two
+  //   sources and every instruction reads one tensor;
+  //   backward up side: rows j = 0..63 of the tile's 256 columns, row-major, 512 bytes
+  //   per row (read transposed with ds_read_b64_tr_b16).
+  const int rt = g.rt;
+  const int rt1 = rt < 64 ? rt : 64;
+  const bufres rl = make_buf(g.low, (uint64_t)g.M * rt * 2);
+  const bufres ru0 = TRANS_B ? make_buf(g.up0, (uint64_t)g.up_split * g.up0_ld * 2)
+                             : make_buf(g.up0, (uint64_t)g.N * g.up0_ld * 2);
+  const bufres ru1 = TRANS_B ? make_buf(g.up1, (uint64_t)(rt - g.up_split) * g.up1_ld * 2)
+                             : make_buf(g.up1, (uint64_t)g.N * g.up1_ld * 2);
+  constexpr int DP1 = BN * 2;  // row pitch of the backward up side (bytes)
+  // Per-lane parts of those loads' offsets; the rest of each offset is wave-uniform
+  // (segment q = 8 wave + i: unit c = 2 wave + i/4, rows 64 (i%4) .. +64).
+  const int lim_m = (int)min<int64_t>(g.M - m0, BM), lim_n = (int)min<int64_t>(g.N - n0, BN);
+  const uint32_t low_base = (uint32_t)(2 * (m0 + lane) * rt + 32 * wave);
+  uint32_t up_base0, up_base1;
+  if constexpr (!TRANS_B) {
+    up_base0 = (uint32_t)(2 * (n0 + lane) * g.up0_ld);
+    up_base1 = (uint32_t)(2 * (n0 + lane) * g.up1_ld);
+  } else {
+    up_base0 = (uint32_t)(2 * ((lane >> 5) * g.up0_ld + n0 + 8 * (lane & 31)));
+    up_base1 = (uint32_t)(2 * ((lane >> 5) * g.up1_ld + n0 + 8 * (lane & 31)));
+  }
+  // Point the stage loads at the up-projection's operands: issue_part(st, KT, i, part)
+  // then loads segment q = 8 wave + i of the low side (part 0) or the up side (part 1).
+  // Every segment of a wave draws from one source tensor: its up-side rows / units
+  // start at 16 wave, and up_split is a multiple of 16.
+  auto switch_to_low = [&]() {
+    const bool first = 16 * wave < g.up_split;
+    src_a = rl;
+    src_r = first ? ru0 : ru1;
+    kred_eff = 1 << 30;  // the reduction-range test passes; a_ok / r_ok decide
+    const uint32_t back_a = (uint32_t)KT * (BK / 2);
+    const uint32_t back_r = TRANS_B ? (uint32_t)((int64_t)KT * BK * g.b_pitch) : back_a;
+#pragma unroll
+    for (int i = 0; i < SEGS; ++i) {
+      const int q = wave * SEGS + i;
+      a_ok[i] = lane + 64 * (i & 3) < lim_m && 8 * (q >> 2) < rt1;
+      a_base[i] = low_base + (uint32_t)(128 * (i & 3) * rt + 16 * (i >> 2)) - back_a;
+      if constexpr (!TRANS_B) {
+        const int t = 8 * (q >> 2);
+        r_ok[i] = lane + 64 * (i & 3) < lim_n && t < rt1;
+        r_base[i] = (first ? up_base0 + (uint32_t)(128 * (i & 3) * g.up0_ld + 2 * t)
+                           : up_base1 + (uint32_t)(128 * (i & 3) * g.up1_ld + 2 * (t - g.up_split))) - back_r;
+      } else {
+        // lane halves take rows j = 2q and 2q+1; rt1 is even, so both rows are live
+        // exactly when 2q < rt1
+        r_ok[i] = 8 * (lane & 31) < lim_n && 2 * q < rt1;
+        r_base[i] = (first ? up_base0 + (uint32_t)(4 * q * g.up0_ld)
+                           : up_base1 + (uint32_t)(2 * (2 * q - g.up_split) * g.up1_ld)) - back_r;
+      }
+    }
+  };
+
   // One step in 16 scheduling regions of 4 MFMAs (one R fragment against the four
   // activation fragments). Region (s, q) also issues the LDS reads of fragments q of
   // substep s+1 and one 1 KB segment of step kt+1's stage (activation and R segments
@@ -503,16 +576,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   };
 
 
-  // ---------------------------------------------------------------- up-projection, part 1
-  // acc += up * low^T on bf16 MFMA 32x32x16 (first operand the output-column side),
-  // `low` = XL (forward) or GB (backward), [M x rt] bf16. Forward: up = [B | L2], row q
-  // (output column) = rt values read straight from memory, the first up_split from up0
-  // (row stride up0_ld), the rest from up1. The first 64 columns of the low-rank side
-  // run here, before the main loop: their loads are issued ahead of the first stage's
-  // (loads complete in order) and their MFMAs overlap that stage's latency.
-  const int rt = g.rt;
-  const bufres rl = make_buf(g.low, (uint64_t)g.M * rt * 2);
-  auto up_loads_fwd = [&](bufres rl_, bufres ru0, bufres ru1, int t0, v4i (&la)[4][TJ], v4i (&ub)[4][TI]) {
+  // ---------------------------------------------------------------- up-projection helpers
+  // acc += up * low^T on bf16 MFMA 32x32x16 (first operand the output-column side).
+  // Forward slices past the first 64 low-rank columns read their operands straight
+  // from memory.
+  auto up_loads_fwd = [&](int t0, v4i (&la)[4][TJ], v4i (&ub)[4][TI]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = t0 + 16 * u, j0 = t + 8 * half;
@@ -520,7 +588,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int64_t row = m0 + wm * 128 + 32 * j + (lane & 31);
-        la[u][j] = buf_load16(rl_, sel_off(live, (uint32_t)((row * rt + j0) * 2)));
+        la[u][j] = buf_load16(rl, sel_off(live, (uint32_t)((row * rt + j0) * 2)));
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
@@ -540,28 +608,45 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
         for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(ub[u][i], la[u][j], acc[i][j]);
     }
   };
-  v4i la0[4][TJ], ub0[4][TI];
-  // backward: the first 64 low-rank rows go through two 32-row slabs of [A; L1] staged
-  // in stage 1 (free until the main loop's first step refills it) by direct-to-LDS
-  // loads issued ahead of stage 0's; GB values in la0
-  constexpr int DP = BN * 2 + 32;  // slab row pitch (bytes) of the epilogue's slabs
-  constexpr int DP1 = BN * 2;      // prologue slab pitch: one load instruction fills 2 rows
-  const int rt1 = rt < 64 ? rt : 64;
-  auto slab_dma = [&](int jc, int i) __attribute__((always_inline)) {
-    const bufres ru0 = make_buf(g.up0, (uint64_t)g.up_split * g.up0_ld * 2);
-    const bufres ru1 = make_buf(g.up1, (uint64_t)(rt - g.up_split) * g.up1_ld * 2);
-    const int r0 = 2 * wave + 8 * i;              // this wave's two rows (uniform)
-    const bool first = jc + r0 < g.up_split;      // up_split is even: both rows agree
-    const int j = jc + r0 + (lane >> 5);
-    const int64_t col = n0 + 8 * (lane & 31);
-    const bool ok = col < g.N && j < rt;
-    const uint32_t off = first ? (uint32_t)(((int64_t)j * g.up0_ld + col) * 2)
-                               : (uint32_t)(((int64_t)(j - g.up_split) * g.up1_ld + col) * 2);
-    buf_load16_lds(first ? ru0 : ru1, st1 + (jc / 32) * 32 * DP1 + r0 * DP1, sel_off(ok, off));
+  // The first 64 low-rank columns from the stage `st` the last step filled (layouts at
+  // issue_low). Forward up operand: 8 consecutive columns of one row, a 16-byte read.
+  // Backward: 8 consecutive rows j of one output column, two transposed 16-bit reads
+  // (lds_tr16_pair's lane pattern, addresses one step from the stage object so the
+  // compiler sees which LDS object they read).
+  auto up_lds = [&](const lds_char* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (16 * u >= rt1) break;
+      v4i la[TJ], ub[TI];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) la[j] = lds_read_b128(st + (2 * u + half) * 4096 + (wm * 128 + 32 * j + (lane & 31)) * 16);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        if constexpr (!TRANS_B) {
+          ub[i] = lds_read_b128(st + TILE_BYTES + (2 * u + half) * 4096 + (wn * 128 + 32 * i + (lane & 31)) * 16);
+        } else {
+          const int gq = lane >> 4, sq = lane & 15;
+          const int col = wn * 128 + 32 * i + 16 * (gq & 1) + 4 * (sq & 3);
+          const int m = 16 * u + 8 * (gq >> 1) + (sq >> 2);
+          const int o = m * DP1 + col * 2;
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(st + (TILE_BYTES + o)));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(st + (TILE_BYTES + o + 4 * DP1)));
+          ub[i] = v4i{(int)(((uint32_t)(uint16_t)lo.x) | ((uint32_t)(uint16_t)lo.y << 16)),
+                      (int)(((uint32_t)(uint16_t)lo.z) | ((uint32_t)(uint16_t)lo.w << 16)),
+                      (int)(((uint32_t)(uint16_t)hi.x) | ((uint32_t)(uint16_t)hi.y << 16)),
+                      (int)(((uint32_t)(uint16_t)hi.z) | ((uint32_t)(uint16_t)hi.w << 16))};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(ub[i], la[j], acc[i][j]);
+    }
   };
+  constexpr int DP = BN * 2 + 32;  // slab row pitch (bytes) of the backward's later slabs
   auto slab_unit = [&](int jc, int i) __attribute__((always_inline)) -> v4i {
-    const bufres ru0 = make_buf(g.up0, (uint64_t)g.up_split * g.up0_ld * 2);
-    const bufres ru1 = make_buf(g.up1, (uint64_t)(rt - g.up_split) * g.up1_ld * 2);
     const int c = tid + 256 * i, row = c >> 5, c16 = c & 31;
     const int j = jc + row;
     const int64_t col = n0 + 8 * c16;
@@ -573,77 +658,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
            buf_load16(ru1, sel_off(ok && !first, (uint32_t)(((int64_t)(j - g.up_split) * g.up1_ld + col) * 2)));
   };
   // ---------------------------------------------------------------- main loop
-  // Branch-free: past the last step the loads go to out-of-range offsets (zeros into a
-  // stage nobody reads). Two stages: step kt+1's 64 KB land while step kt is multiplied.
-  // Prologue. Forward: the first 64 low-rank columns' operands go out ahead of stage 0
-  // and their MFMAs run while it lands. Backward: stage 0 first, then the operands
-  // (GB values and the [A; L1] slabs, which land with it), one wait for all, then the
-  // MFMAs. (Each order measured faster for its direction.)
-  if constexpr (!TRANS_B) {
-    if (rt > 0) {
-      const bufres ru0 = make_buf(g.up0, (uint64_t)g.N * g.up0_ld * 2);
-      const bufres ru1 = make_buf(g.up1, (uint64_t)g.N * g.up1_ld * 2);
-      up_loads_fwd(rl, ru0, ru1, 0, la0, ub0);
-    }
-  }
-  asm volatile("" ::: "memory");
+  // Two stages: step kt+1's 64 KB land while step kt is multiplied. Past the last step
+  // the touch loads go to out-of-range offsets.
   issue_stage(st0, 0);
   asm volatile("" ::: "memory");
-  if constexpr (!TRANS_B) {
-    if (rt > 0) up_mfma_fwd(0, la0, ub0);  // runs while stage 0 lands
-  } else {
-    if (rt > 0) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)  // low-rank columns 16u + 8*half .. +8 (u < rt1/16)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) {
-          const int64_t row = m0 + wm * 128 + 32 * j + (lane & 31);
-          la0[u][j] = buf_load16(rl, sel_off(16 * u < rt1, (uint32_t)((row * rt + 16 * u + 8 * half) * 2)));
-        }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        slab_dma(0, i);
-        slab_dma(32, i);  // rows past rt load zeros
-      }
-    }
-  }
   write_scales();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the staging stores are done
-  vm_barrier<0>();  // step 0, the low-rank operands and the slabs landed; scales in LDS
-  if constexpr (TRANS_B) {
-    if (rt > 0) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {  // branch-free: past rt the slab and la0 are zeros
-        v4i ub[TI];
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          // lds_tr16_pair's lane pattern, addresses one step from the stage object so
-          // the compiler sees which LDS object they read
-          const int gq = lane >> 4, sq = lane & 15;
-          const int col = wn * 128 + 32 * i + 16 * (gq & 1) + 4 * (sq & 3);
-          const int m = 32 * (u >> 1) + 16 * (u & 1) + 8 * (gq >> 1) + (sq >> 2);
-          const int o = m * DP1 + col * 2;
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(st1 + o));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(st1 + (o + 4 * DP1)));
-          ub[i] = v4i{(int)(((uint32_t)(uint16_t)lo.x) | ((uint32_t)(uint16_t)lo.y << 16)),
-                      (int)(((uint32_t)(uint16_t)lo.z) | ((uint32_t)(uint16_t)lo.w << 16)),
-                      (int)(((uint32_t)(uint16_t)hi.x) | ((uint32_t)(uint16_t)hi.y << 16)),
-                      (int)(((uint32_t)(uint16_t)hi.z) | ((uint32_t)(uint16_t)hi.w << 16))};
-        }
-#pragma unroll
-        for (int i = 0; i < TI; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma_bf16(ub[i], la0[u][j], acc[i][j]);
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // slab reads done before stage 1 is refilled
-    }
-  }
-  // (after the slab reads: the compiler would make them wait for this load)
+  vm_barrier<0>();  // step 0 landed; scales in LDS
   prefetch(1);
   // One step: step kt+1's loads go into the stage step kt-1 used (every wave left it at
   // the last barrier), then step kt's MFMAs run while they land. Unrolled by two so each
-  // step names its stage statically.
+  // step names its stage statically. The last step loads the up-projection's operands.
   auto step = [&](lds_char* cur, lds_char* nxt, int kt) __attribute__((always_inline)) {
     compute(cur, kt, nxt);  // also issues step kt+1's stage loads into nxt
     asm volatile("" ::: "memory");
@@ -652,26 +677,31 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     vm_barrier<TOUCHES>();
   };
   for (int kt = 0; kt < KT; kt += 2) {
+    if (kt + 1 == KT) switch_to_low();
     step(st0, st1, kt);
-    if (kt + 1 < KT) step(st1, st0, kt + 1);
+    if (kt + 1 < KT) {
+      if (kt + 2 == KT) switch_to_low();
+      step(st1, st0, kt + 1);
+    }
   }
+  if (rt > 0) up_lds((KT & 1) ? st1 : st0);
 
   // ---------------------------------------------------------------- up-projection, part 2
   if constexpr (!TRANS_B) {
-    // forward, rt > 64: the remaining 64-wide slices (the first was done in the prologue)
-    const bufres ru0 = make_buf(g.up0, (uint64_t)g.N * g.up0_ld * 2);
-    const bufres ru1 = make_buf(g.up1, (uint64_t)g.N * g.up1_ld * 2);
+    // forward, rt > 64: the remaining 64-wide slices (the first came with the last step)
     for (int t0 = 64; t0 < rt; t0 += 64) {
       v4i la[4][TJ], ub[4][TI];
-      up_loads_fwd(rl, ru0, ru1, t0, la, ub);
+      up_loads_fwd(t0, la, ub);
       up_mfma_fwd(t0, la, ub);
     }
   } else {
     // backward, rt > 64: the remaining 32-row slabs of up = [A; L1] [rt x N] (row j =
-    // up0 row j for j < up_split, else up1 row j - up_split; the first 64 were done in
-    // the prologue). The MFMA wants 8 consecutive j per output column, so each slab of
-    // the tile's 256 columns is staged in LDS (free after the main loop) and read
-    // transposed with ds_read_b64_tr_b16.
+    // up0 row j for j < up_split, else up1 row j - up_split; the first 64 came with the
+    // last step). The MFMA wants 8 consecutive j per output column, so each slab of
+    // the tile's 256 columns is staged in LDS (free after the main loop, once every
+    // wave has read the first 64 rows' stage) and read transposed with
+    // ds_read_b64_tr_b16.
+    if (rt > 64) __syncthreads();
     for (int jc = 64; jc < rt; jc += 32) {
       v4i la[2][TJ];
 #pragma unroll
@@ -819,7 +849,7 @@ static_assert(GEMM_MAX_KRED == MAX_NKB * 32, "scale staging bound");
 
 hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipStream_t stream) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
-  if (g.Kred > GEMM_MAX_KRED) return hipErrorInvalidValue;
+  if (g.Kred < 1 || g.Kred > GEMM_MAX_KRED) return hipErrorInvalidValue;  // the last step is peeled: KT >= 1
   if (g.epi != GEMM_EPI_NONE && (g.epi != GEMM_EPI_DGELU_Q || !out_bf16 || !trans_b || g.q_codes == nullptr ||
                                  g.q_scales == nullptr || g.pre == nullptr))
     return hipErrorInvalidValue;
