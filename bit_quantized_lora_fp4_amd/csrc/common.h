@@ -177,6 +177,9 @@ __device__ __forceinline__ void buf_store8(bufres r, uint32_t off, v2i v) {
 __device__ __forceinline__ void buf_store4(bufres r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buf_store16(bufres r, uint32_t off, v4i v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
 __device__ __forceinline__ void buf_store1(bufres r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, r, (int)off, 0, 0);
 }

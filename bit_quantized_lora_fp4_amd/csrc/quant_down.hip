@@ -208,11 +208,47 @@ __device__ __forceinline__ void lds_tr_tiles(const lds_char* sd, int b, int lane
   }
 }
 
+// Sum of the 4 waves' [64 x rt] partial products in LDS (wave order), then this column
+// range's result: fp32 partials when the range is one of S > 1, else bf16(low). Called
+// with every wave's LDS use finished (the area aliases the stages).
+template <int TP>
+__device__ __forceinline__ void reduce_waves(const v4f (&acc)[4][TP], float* red, const QuantDownArgs& a, int64_t r0,
+                                             int split, int S, int wave, int lane, int tid) {
+  constexpr int RT = 16 * TP;
+  // acc[g][t] register r of lane l: row 16g + l%16, column 16t + 4(l/16) + r
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int t = 0; t < TP; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[(((wave * 4 + g) * TP + t) * 4 + r) * 64 + lane] = acc[g][t][r];
+  __syncthreads();
+  constexpr int NI = 4 * TP * 64;
+  const bool partial = S > 1;
+  float* part = a.partials + ((int64_t)split * a.M) * RT;
+  for (int e = tid; e < NI; e += 256) {
+    const int l = e & 63, t = (e >> 6) % TP, g = e / (64 * TP);
+    v4f s = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < QD_WAVES; ++w) {
+      const float* src = red + ((((w * 4 + g) * TP + t) * 4) * 64 + l);
+      s += v4f{src[0], src[64], src[128], src[192]};
+    }
+    const int64_t orow = r0 + 16 * g + (l & 15);
+    const int col = 16 * t + 4 * (l >> 4);
+    if (orow < a.M) {
+      if (partial)
+        *reinterpret_cast<v4f*>(part + orow * RT + col) = s;
+      else
+        *reinterpret_cast<uint2*>(a.low + orow * RT + col) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+    }
+  }
+}
+
 template <typename T, int TP, bool UCOLS, int MODE>
 __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   static_assert(TP % 2 == 0, "rank + stab_rank is a multiple of 32");
   constexpr int NS = (MODE == QD_QUANT || MODE == QD_GELU_QUANT) ? QD_STORES : 0;  // stores per chunk
-  constexpr int RT = 16 * TP;
   constexpr int WAVE_LDS = UCOLS ? 2 * UStage<TP>::BYTES : 0;
   constexpr int RED = QD_WAVES * 4 * TP * 4 * 64 * 4;
   constexpr int SMEM = QD_WAVES * WAVE_LDS > RED ? QD_WAVES * WAVE_LDS : RED;
@@ -358,9 +394,10 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
         }
   };
 
-  // Two chunks per trip, each in its own register set (and LDS stage). The second may
-  // lie past the range: it then loads zeros and stores nothing, which keeps the trip
-  // branch-free and its memory-operation count fixed.
+  // Operand rows given (forward): a ring of three register sets, below. Operand staged
+  // in LDS (backward): two chunks per trip, each in its own register set and LDS stage;
+  // the second may lie past the range: it then loads zeros and stores nothing, which
+  // keeps the trip branch-free and its memory-operation count fixed.
   XChunk<T> x0, x1;
   DChunk<TP> d0, d1;
   int64_t ch = ch0 + wave;
@@ -381,27 +418,65 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
     }
   };
   if constexpr (!UCOLS) {
+    // Register sets in a ring: while one chunk is worked on, the next NBUF - 1 chunks'
+    // loads are in flight (one workgroup per CU, so a wave's own loads are all that
+    // covers the memory latency; with one chunk ahead the loop waited about twice as
+    // long per chunk). Three sets where the registers allow (bf16 input, rank + stab
+    // rank <= 64, no GELU values to hold), else two. The wait before each chunk is the
+    // compiler's, counted exactly: the chunks issued after it and one chunk's stores
+    // stay in flight.
+    constexpr int NBUF = (sizeof(T) == 2 && TP <= 4 && MODE != QD_GELU_QUANT) ? 3 : 2;
+    XChunk<T> x2;
+    DChunk<TP> d2;
     x0.load(rx, row_off, row_ok, cstart(ch), a.K, lq);
     d0.load(rd0, rd1, ta, cstart(ch), a.K, lr, lq);
     asm volatile("" ::: "memory");
-    dummy_stores();
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    for (; ch < ch1; ch += 2 * QD_WAVES) {
+    if constexpr (NBUF == 3) {
       x1.load(rx, row_off, row_ok, cstart(ch + QD_WAVES), a.K, lq);
       d1.load(rd0, rd1, ta, cstart(ch + QD_WAVES), a.K, lr, lq);
+    } else {
+      dummy_stores();
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    auto ring = [&](XChunk<T>& xw, DChunk<TP>& dw, XChunk<T>& xl, DChunk<TP>& dl) __attribute__((always_inline)) {
+      // load chunk ch + NBUF - 1 (in wave strides) into (xl, dl), then work on chunk ch
+      xl.load(rx, row_off, row_ok, cstart(ch + (NBUF - 1) * QD_WAVES), a.K, lq);
+      dl.load(rd0, rd1, ta, cstart(ch + (NBUF - 1) * QD_WAVES), a.K, lr, lq);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      work(x0, d0, nullptr, ch);
+      work(xw, dw, nullptr, ch);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      x0.load(rx, row_off, row_ok, cstart(ch + 2 * QD_WAVES), a.K, lq);
-      d0.load(rd0, rd1, ta, cstart(ch + 2 * QD_WAVES), a.K, lr, lq);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      work(x1, d1, nullptr, ch + QD_WAVES);
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
+      ch += QD_WAVES;
+    };
+    if constexpr (NBUF == 3) {
+      while (ch < ch1) {
+        ring(x0, d0, x2, d2);
+        if (ch >= ch1) break;
+        ring(x1, d1, x0, d0);
+        if (ch >= ch1) break;
+        ring(x2, d2, x1, d1);
+      }
+    } else {
+      // two sets: both chunks of a trip run; the second may lie past the range (then it
+      // loads zeros and stores nothing)
+      for (; ch < ch1; ch += 2 * QD_WAVES) {
+        x1.load(rx, row_off, row_ok, cstart(ch + QD_WAVES), a.K, lq);
+        d1.load(rd0, rd1, ta, cstart(ch + QD_WAVES), a.K, lr, lq);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        work(x0, d0, nullptr, ch);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        x0.load(rx, row_off, row_ok, cstart(ch + 2 * QD_WAVES), a.K, lq);
+        d0.load(rd0, rd1, ta, cstart(ch + 2 * QD_WAVES), a.K, lr, lq);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        work(x1, d1, nullptr, ch + QD_WAVES);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   } else {
     lds_char* sd0 = (lds_char*)smem_raw + wave * WAVE_LDS;
@@ -441,35 +516,329 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
     // backward's stages alias the reduction area: let every direct-to-LDS load land.
     if constexpr (UCOLS) wait_vmcnt<0>();
     __syncthreads();
-    float* red = (float*)smem_raw;
-    // acc[g][t] register r of lane l: row 16g + l%16, column 16t + 4(l/16) + r
+    reduce_waves<TP>(acc, (float*)smem_raw, a, r0, split, S, wave, lane, tid);
+  }
+}
+
+// ---------------------------------------------------------------- staged kernel
+// bf16 input with rank + stab_rank <= 64. The same work split as k_quant_down (64 rows
+// per workgroup, one of S column ranges, 64-column chunks, the same MFMA layouts), but
+// every operand reaches LDS by direct-to-LDS loads of whole rows of a chunk and the
+// codes leave through LDS, 64 contiguous bytes per row. Measured on k_quant_down at
+// 4608 x 3072 (rank + stab_rank = 64): without its code stores its loop ran 31% faster,
+// without its X loads or its operand loads about a third faster each, without its
+// quantization arithmetic or its MFMAs about 5%: the time went to the number of memory
+// requests (a load there spans 16 rows x 64 bytes, a code store 16 rows x 16 bytes),
+// not to arithmetic.
+//
+// Each wave works on its own LDS area, with no barrier until the final reduction: two
+// stages (one chunk of X and of the low-rank operand each) and a code buffer for two
+// chunks. A wave takes its chunks in adjacent pairs (chunks 2w, 2w+1 of every 8), so
+// the codes of a pair are 64 contiguous bytes of each row. Layouts:
+//   X, and D in the forward: chunk row r at 128 r, its 16-byte unit u at slot
+//     u ^ ((r >> 1) & 7) (the 16 rows an operand read touches meet 16 bank groups);
+//   backward: the chunk's 64 rows of each factor of [B | L2] contiguous as in memory
+//     (row pitch 2 r_f bytes; first factor, then second), read transposed;
+//   codes: row r at 64 r, unit u at slot u ^ ((r >> 2) & 3).
+// Loads are awaited with exact vmcnt counts (every load and store is issued, dead ones
+// at out-of-range offsets), and all LDS accesses inside the loop are written in asm
+// that waits for itself: the compiler, seeing direct-to-LDS loads into the same array,
+// would otherwise wait for all of them before every LDS access.
+constexpr int SQ_XB = QD_ROWS * 128;  // X per stage: 64 rows x 64 bf16
+constexpr int SQ_CB = QD_ROWS * 64;   // codes of two chunks: 64 rows x 64 bytes
+template <int TP>
+struct SqLds {
+  static constexpr int DB = 2048 * TP;  // low-rank operand per stage: 16 TP x 64 bf16
+  static constexpr int STAGE = SQ_XB + DB;
+  static constexpr int WAVE = 2 * STAGE + SQ_CB;
+  static constexpr int RED = QD_WAVES * 4 * TP * 4 * 64 * 4;
+  static constexpr int BYTES = QD_WAVES * WAVE > RED ? QD_WAVES * WAVE : RED;
+};
+__device__ __forceinline__ int sq_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
+
+// N 16-byte LDS reads (N = 4 or 8), awaited inside the block.
+__device__ __forceinline__ void lds_read16x8(const uint32_t (&ad)[8], v4i (&o)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+      : "memory");
+}
+__device__ __forceinline__ void lds_read16x4(const uint32_t (&ad)[4], v4i (&o)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
+}
+
+template <int TP, bool UCOLS, int MODE>
+__global__ __launch_bounds__(256) void k_quant_down_lds(const QuantDownArgs a) {
+  static_assert(TP == 0 || TP == 2 || TP == 4, "staged kernel: rank + stab_rank <= 64");
+  using L = SqLds<TP>;
+  constexpr bool QUANT = MODE == QD_QUANT || MODE == QD_GELU_QUANT;
+  constexpr int NL = SQ_XB / 1024 + L::DB / 1024;  // direct-to-LDS loads per stage
+  constexpr int NS = QUANT ? 5 : 0;                // stores per pair: 4 code blocks, 1 scale
+  __shared__ __align__(16) char smem_raw[L::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.x * QD_ROWS;
+  const int rows_left = (int)min<int64_t>(a.M - r0, QD_ROWS);
+  const int split = blockIdx.y, S = gridDim.y;
+  const int64_t nchunks = (a.K + CHUNK - 1) / CHUNK;
+  const int64_t per = (nchunks + S - 1) / S;
+  const int64_t ch0 = split * per, ch1 = min(nchunks, ch0 + per);
+  const int rounds = (int)((max<int64_t>(ch1 - ch0, 0) + 2 * QD_WAVES - 1) / (2 * QD_WAVES));
+  const int64_t cpitch = a.K >> 1, nkb = a.K >> 5;
+  const int ta = a.r0 / 16, r1 = a.rt - a.r0;
+
+  const bufres rx = make_buf(a.x, (uint64_t)a.M * a.ldx * 2);
+  const bufres rcodes = make_buf(a.codes, (uint64_t)a.M * cpitch);
+  const bufres rscales = make_buf(a.scales, (uint64_t)((a.M + 31) / 32) * nkb);
+  const bufres rd0 = make_buf(a.d0, (uint64_t)a.K * a.r0 * 2);
+  const bufres rd1 = make_buf(a.d1, (uint64_t)a.K * r1 * 2);
+
+  lds_char* const st0 = (lds_char*)smem_raw + wave * L::WAVE;
+  lds_char* const st1 = st0 + L::STAGE;
+  lds_char* const cbuf = st0 + 2 * L::STAGE;
+
+  v4f acc[4][TP > 0 ? TP : 1];
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
+  for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int t = 0; t < TP; ++t)
+    for (int t = 0; t < (TP > 0 ? TP : 1); ++t) acc[g][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // chunk i (0, 1) of this wave's pair in round k; live while below ch1
+  auto chunk_of = [&](int k, int i) -> int64_t { return ch0 + 2 * QD_WAVES * k + 2 * wave + i; };
+
+  // ---- one chunk's operands into a stage
+  auto dma = [&](lds_char* st, int64_t c) __attribute__((always_inline)) {
+    const bool live = c < ch1;
+    const int64_t c0 = c * CHUNK;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(((wave * 4 + g) * TP + t) * 4 + r) * 64 + lane] = acc[g][t][r];
-    __syncthreads();
-    constexpr int NI = 4 * TP * 64;
-    const bool partial = S > 1;
-    float* part = a.partials + ((int64_t)split * a.M) * RT;
-    for (int e = tid; e < NI; e += 256) {
-      const int l = e & 63, t = (e >> 6) % TP, g = e / (64 * TP);
-      v4f s = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i) {  // X rows 8i + l/8, slot l%8 holding unit (l%8) ^ swz(row)
+      const int row = 8 * i + (lane >> 3);
+      const int64_t col = c0 + 8 * ((lane & 7) ^ sq_swz(row));
+      buf_load16_lds(rx, st + i * 1024,
+                     sel_off(live && row < rows_left && col < a.K, (uint32_t)(((r0 + row) * a.ldx + col) * 2)));
+    }
+    if constexpr (TP > 0) {
+      lds_char* const sd = st + SQ_XB;
 #pragma unroll
-      for (int w = 0; w < QD_WAVES; ++w) {
-        const float* src = red + ((((w * 4 + g) * TP + t) * 4) * 64 + l);
-        s += v4f{src[0], src[64], src[128], src[192]};
-      }
-      const int64_t orow = r0 + 16 * g + (l & 15);
-      const int col = 16 * t + 4 * (l >> 4);
-      if (orow < a.M) {
-        if (partial)
-          *reinterpret_cast<v4f*>(part + orow * RT + col) = s;
-        else
-          *reinterpret_cast<uint2*>(a.low + orow * RT + col) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+      for (int i = 0; i < 2 * TP; ++i) {
+        const bool first = 8 * i < a.r0;  // uniform: r0 is a multiple of 16
+        if constexpr (!UCOLS) {
+          // D rows 8i + l/8 (first factor rows j < r0, K-contiguous), same swizzle as X
+          const int jj = 8 * i + (lane >> 3);
+          const int64_t j = first ? jj : jj - a.r0;
+          const int64_t col = c0 + 8 * ((lane & 7) ^ sq_swz(jj));
+          buf_load16_lds(first ? rd0 : rd1, sd + i * 1024, sel_off(live && col < a.K, (uint32_t)((j * a.K + col) * 2)));
+        } else {
+          // factor rows c0 .. c0+63 are 128 r_f contiguous bytes; r_f / 8 loads each
+          const int rf = first ? a.r0 : r1;
+          const int o = (first ? i : i - a.r0 / 8) * 1024 + 16 * lane;
+          const bool ok = live && (int64_t)o < (a.K - c0) * 2 * rf;
+          buf_load16_lds(first ? rd0 : rd1, sd + i * 1024, sel_off(ok, (uint32_t)(c0 * 2 * rf + o)));
+        }
       }
     }
+  };
+
+  // ---- one chunk: operand reads, MFMAs, quantization (codes into cbuf)
+  uint32_t sbs0 = 0, sbs1 = 0;  // the pair's scale bytes: block row h, byte 2i + b
+  auto work = [&](const lds_char* st, int i) __attribute__((always_inline)) {
+    v4i xv[8];  // [2g + b]: rows 16g + l%16, columns 32b + 8(l/16) .. +8 of the chunk
+    {
+      uint32_t ad[8];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int row = 16 * g + lr;
+          ad[2 * g + b] = lds_addr(st + row * 128 + (((4 * b + lq) ^ sq_swz(row)) << 4));
+        }
+      lds_read16x8(ad, xv);
+    }
+    float hv[4][2][8];  // GELU mode: H = GELU(P^) in fp32
+    if constexpr (MODE == QD_GELU_QUANT) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const v4i w = xv[2 * g + b];
+          const uint32_t ws[4] = {(uint32_t)w.x, (uint32_t)w.y, (uint32_t)w.z, (uint32_t)w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hv[g][b][2 * e] = gelu_f(bf16_lo(ws[e]));
+            hv[g][b][2 * e + 1] = gelu_f(bf16_hi(ws[e]));
+          }
+        }
+    }
+    if constexpr (TP > 0) {
+      v4i dv[TP][2];  // first MFMA operand: tile t (rank columns 16t .. +16), column block b
+      const lds_char* const sd = st + SQ_XB;
+      if constexpr (!UCOLS) {
+        uint32_t ad[2 * TP];
+#pragma unroll
+        for (int t = 0; t < TP; ++t)
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            const int jj = 16 * t + lr;
+            ad[2 * t + b] = lds_addr(sd + jj * 128 + (((4 * b + lq) ^ sq_swz(jj)) << 4));
+          }
+        v4i o[2 * TP];
+        if constexpr (TP == 4) lds_read16x8(ad, o);
+        else lds_read16x4(ad, o);
+#pragma unroll
+        for (int t = 0; t < TP; ++t) dv[t][0] = o[2 * t], dv[t][1] = o[2 * t + 1];
+      } else {
+        // lane l of 16-lane group g: rank column 16t + l%16 at rows 32b + 8g .. +8 of the
+        // chunk. Within the group, lane s addresses 4 consecutive rank columns
+        // (4(s%4) on) of row 32b + 8g + s/4; ds_read_b64_tr_b16 hands lane s column s of
+        // those 4 rows, and a second read 4 rows on covers the other 4.
+        const int gq = lane >> 4, s = lane & 15;
+#pragma unroll
+        for (int t = 0; t < TP; t += 2) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            uint32_t p[2], pitch[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const bool first = t + u < ta;
+              const int rf = first ? a.r0 : r1;
+              const int jl = 16 * (first ? t + u : t + u - ta) + 4 * (s & 3);
+              const int n = 32 * b + 8 * gq + (s >> 2);
+              pitch[u] = (uint32_t)(2 * rf);
+              p[u] = lds_addr(sd + (first ? 0 : 128 * a.r0)) + (uint32_t)(n * 2 * rf + 2 * jl);
+            }
+            v2i w, x, y, z;
+            asm volatile(
+                "ds_read_b64_tr_b16 %0, %4\n\t"
+                "ds_read_b64_tr_b16 %1, %5\n\t"
+                "ds_read_b64_tr_b16 %2, %6\n\t"
+                "ds_read_b64_tr_b16 %3, %7\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(w), "=&v"(x), "=&v"(y), "=&v"(z)
+                : "v"(p[0]), "v"(p[0] + 4 * pitch[0]), "v"(p[1]), "v"(p[1] + 4 * pitch[1])
+                : "memory");
+            dv[t][b] = v4i{w.x, w.y, x.x, x.y};
+            dv[t + 1][b] = v4i{y.x, y.y, z.x, z.y};
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        v4i xop[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          if constexpr (MODE == QD_GELU_QUANT)
+            xop[g] = v4i{(int)pack_bf16x2(hv[g][b][0], hv[g][b][1]), (int)pack_bf16x2(hv[g][b][2], hv[g][b][3]),
+                         (int)pack_bf16x2(hv[g][b][4], hv[g][b][5]), (int)pack_bf16x2(hv[g][b][6], hv[g][b][7])};
+          else
+            xop[g] = xv[2 * g + b];
+        }
+#pragma unroll
+        for (int t = 0; t < TP; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) acc[g][t] = mfma16(dv[t][b], xop[g], acc[g][t]);
+      }
+    }
+    if constexpr (QUANT) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          uint32_t m = 0;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int g = 2 * h + q;
+            if constexpr (MODE == QD_GELU_QUANT) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) m = umax(m, __builtin_bit_cast(uint32_t, hv[g][b][e]) & 0x7FFFFFFFu);
+            } else {
+              const v4i w = xv[2 * g + b];
+              m = umax(m, umax(umax(bf16x2_absmax_bits(w.x), bf16x2_absmax_bits(w.y)),
+                               umax(bf16x2_absmax_bits(w.z), bf16x2_absmax_bits(w.w))));
+            }
+          }
+          const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
+          const float scale = e8m0_to_f32_scale(sb);
+          if (h == 0) sbs0 |= sb << (8 * (2 * i + b));
+          else sbs1 |= sb << (8 * (2 * i + b));
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int g = 2 * h + q;
+            uint32_t cw;
+            if constexpr (MODE == QD_GELU_QUANT) {
+              cw = cvt8_f32(hv[g][b], scale);
+            } else {
+              const v4i w = xv[2 * g + b];
+              cw = cvt8_bf16(w.x, w.y, w.z, w.w, scale);
+            }
+            if (sb == 0xFFu) cw = 0;
+            const int row = 16 * g + lr;
+            const uint32_t ad = lds_addr(cbuf + row * 64 + (((2 * i + b) ^ ((row >> 2) & 3)) << 4) + 4 * lq);
+            asm volatile("ds_write_b32 %0, %1" ::"v"(ad), "v"(cw) : "memory");
+          }
+        }
+    }
+  };
+
+  // ---- the pair's codes (64 bytes of each row) and scale bytes, from cbuf
+  auto store_pair = [&](int k) __attribute__((always_inline)) {
+    const int64_t pc = chunk_of(k, 0) * CHUNK;  // first column of the pair
+    uint32_t ad[4];
+    v4i cv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // lane l: row 16q + l/4, unit l%4
+      const int row = 16 * q + (lane >> 2), u = lane & 3;
+      ad[q] = lds_addr(cbuf + row * 64 + ((u ^ ((row >> 2) & 3)) << 4));
+    }
+    lds_read16x4(ad, cv);
+    const int u = lane & 3;
+    const bool uok = chunk_of(k, u >> 1) < ch1 && pc + 32 * u < a.K;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 16 * q + (lane >> 2);
+      buf_store16(rcodes, sel_off(uok && row < rows_left, (uint32_t)((r0 + row) * cpitch + (pc >> 1) + 16 * u)), cv[q]);
+    }
+    // lanes 0..7: block row l/4, byte l%4 (column block pc/32 + l%4)
+    const int h = (lane >> 2) & 1, e = lane & 3;
+    const uint32_t v = ((h ? sbs1 : sbs0) >> (8 * e)) & 0xFFu;
+    const bool sok = lane < 8 && r0 + 32 * h < a.M && chunk_of(k, e >> 1) < ch1 && pc + 32 * e < a.K;
+    buf_store1(rscales, sel_off(sok, (uint32_t)((r0 / 32 + h) * nkb + (pc >> 5) + e)), v);
+  };
+
+  dma(st0, chunk_of(0, 0));
+  dma(st1, chunk_of(0, 1));
+  if constexpr (NS > 0) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {  // stand-ins for a previous pair's stores (see above)
+      uint32_t off = BUF_OOB + 16u * i;
+      asm volatile("" : "+v"(off));
+      buf_store4(rcodes, off, 0u);
+    }
+  }
+  for (int k = 0; k < rounds; ++k) {
+    sbs0 = sbs1 = 0;
+    wait_vmcnt<NL + NS>();  // stage 0 landed (stage 1 and the last pair's stores may not have)
+    work(st0, 0);
+    dma(st0, chunk_of(k + 1, 0));
+    wait_vmcnt<NS + NL>();  // stage 1 landed
+    work(st1, 1);
+    dma(st1, chunk_of(k + 1, 1));
+    if constexpr (NS > 0) store_pair(k);
+  }
+  if constexpr (TP > 0) {
+    wait_vmcnt<0>();  // the reduction area aliases the stages: every load has landed
+    __syncthreads();
+    reduce_waves<TP>(acc, (float*)smem_raw, a, r0, split, S, wave, lane, tid);
   }
 }
 
@@ -494,6 +863,18 @@ hipError_t launch_t(const QuantDownArgs& a, int tp, int splits, hipStream_t stre
     case 4: hipLaunchKernelGGL((k_quant_down<T, 4, UCOLS, MODE>), grid, block, 0, stream, a); break;
     case 6: hipLaunchKernelGGL((k_quant_down<T, 6, UCOLS, MODE>), grid, block, 0, stream, a); break;
     case 8: hipLaunchKernelGGL((k_quant_down<T, 8, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool UCOLS, int MODE>
+hipError_t launch_staged(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
+  dim3 grid((unsigned)((a.M + QD_ROWS - 1) / QD_ROWS), (unsigned)splits), block(256);
+  switch (tp) {
+    case 0: hipLaunchKernelGGL((k_quant_down_lds<0, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_quant_down_lds<2, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_quant_down_lds<4, UCOLS, MODE>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -526,8 +907,14 @@ hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t st
   const int S = quant_down_splits(a.M, a.K, a.rt);
   if (S > 1 && a.partials == nullptr) return hipErrorInvalidValue;
   hipError_t e;
-  if (a.mode == QD_GELU_QUANT) {  // the saved P^: Q(GELU(P^)) and [A2; L1_2] down
-    if (!x_bf16 || a.u_cols) return hipErrorInvalidValue;
+  if (a.mode == QD_GELU_QUANT && (!x_bf16 || a.u_cols)) return hipErrorInvalidValue;
+  if (a.mode == QD_DOWN && tp == 0) return hipErrorInvalidValue;
+  if (x_bf16 && tp <= 4) {  // the staged kernel (whole-row loads, LDS-staged code stores)
+    if (a.mode == QD_GELU_QUANT) e = launch_staged<false, QD_GELU_QUANT>(a, tp, S, stream);
+    else if (a.mode == QD_DOWN) e = a.u_cols ? launch_staged<true, QD_DOWN>(a, tp, S, stream)
+                                             : launch_staged<false, QD_DOWN>(a, tp, S, stream);
+    else e = a.u_cols ? launch_staged<true, QD_QUANT>(a, tp, S, stream) : launch_staged<false, QD_QUANT>(a, tp, S, stream);
+  } else if (a.mode == QD_GELU_QUANT) {  // the saved P^: Q(GELU(P^)) and [A2; L1_2] down
     e = launch_t<bf16_t, false, QD_GELU_QUANT>(a, tp, S, stream);
   } else if (a.mode == QD_DOWN) {  // down-projection alone, either side
     if (tp == 0) return hipErrorInvalidValue;

@@ -75,6 +75,10 @@ CASES = [
     (200, 320, 288, 32, 0, "fp32"),      # no stabilizer, fp32 input
     (96, 256, 512, 0, 0, "bf16"),        # plain 4-bit GEMM
     (520, 768, 640, 64, 64, "fp32"),
+    # two column ranges per row block in the fused quantize + down-projection, the first
+    # range's last chunk pair reaching into the second, the last chunk half past K
+    (640, 1056, 1056, 32, 32, "bf16"),
+    (600, 1120, 1088, 16, 16, "bf16"),
 ]
 
 
