@@ -211,7 +211,7 @@ __device__ __forceinline__ void lds_tr_tiles(const lds_char* sd, int b, int lane
 // Sum of the 4 waves' [64 x rt] partial products in LDS (wave order), then this column
 // range's result: fp32 partials when the range is one of S > 1, else bf16(low). Called
 // with every wave's LDS use finished (the area aliases the stages).
-template <int TP>
+template <int TP, int NW = QD_WAVES>
 __device__ __forceinline__ void reduce_waves(const v4f (&acc)[4][TP], float* red, const QuantDownArgs& a, int64_t r0,
                                              int split, int S, int wave, int lane, int tid) {
   constexpr int RT = 16 * TP;
@@ -226,11 +226,11 @@ __device__ __forceinline__ void reduce_waves(const v4f (&acc)[4][TP], float* red
   constexpr int NI = 4 * TP * 64;
   const bool partial = S > 1;
   float* part = a.partials + ((int64_t)split * a.M) * RT;
-  for (int e = tid; e < NI; e += 256) {
+  for (int e = tid; e < NI; e += 64 * NW) {
     const int l = e & 63, t = (e >> 6) % TP, g = e / (64 * TP);
     v4f s = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < QD_WAVES; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float* src = red + ((((w * 4 + g) * TP + t) * 4) * 64 + l);
       s += v4f{src[0], src[64], src[128], src[192]};
     }
@@ -531,10 +531,16 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
 // requests (a load there spans 16 rows x 64 bytes, a code store 16 rows x 16 bytes),
 // not to arithmetic.
 //
-// Each wave works on its own LDS area, with no barrier until the final reduction: two
-// stages (one chunk of X and of the low-rank operand each) and a code buffer for two
-// chunks. A wave takes its chunks in adjacent pairs (chunks 2w, 2w+1 of every 8), so
-// the codes of a pair are 64 contiguous bytes of each row. Layouts:
+// 8 waves, two per SIMD, each on its own LDS area with no barrier until the final
+// reduction: one stage (one chunk of X and of the low-rank operand) and a code buffer
+// for two chunks. While one wave of a SIMD waits for its chunk, the other converts and
+// quantizes (with one wave per SIMD and two stages each, those waits and the vector
+// arithmetic added up: at K = 12288 a chunk took 1.03 us without quantization, 1.66 us
+// with it and 3.1 us with GELU in front; two waves per SIMD took the GELU pass from 55
+// to 45 us). A wave takes its chunks in adjacent pairs (chunks 2w, 2w+1 of every 16), so
+// the codes of a pair are 64 contiguous bytes of each row, and works on a chunk in two
+// halves (column blocks b = 0, 1) so that it fits the 256 registers two waves per SIMD
+// leave it. Layouts:
 //   X, and D in the forward: chunk row r at 128 r, its 16-byte unit u at slot
 //     u ^ ((r >> 1) & 7) (the 16 rows an operand read touches meet 16 bank groups);
 //   backward: the chunk's 64 rows of each factor of [B | L2] contiguous as in memory
@@ -546,27 +552,10 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
 // would otherwise wait for all of them before every LDS access.
 constexpr int SQ_XB = QD_ROWS * 128;  // X per stage: 64 rows x 64 bf16
 constexpr int SQ_CB = QD_ROWS * 64;   // codes of two chunks: 64 rows x 64 bytes
-template <int TP>
-struct SqLds {
-  static constexpr int DB = 2048 * TP;  // low-rank operand per stage: 16 TP x 64 bf16
-  static constexpr int STAGE = SQ_XB + DB;
-  static constexpr int WAVE = 2 * STAGE + SQ_CB;
-  static constexpr int RED = QD_WAVES * 4 * TP * 4 * 64 * 4;
-  static constexpr int BYTES = QD_WAVES * WAVE > RED ? QD_WAVES * WAVE : RED;
-};
 __device__ __forceinline__ int sq_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ uint32_t lds_addr(const lds_char* p) { return (uint32_t)(uintptr_t)p; }
 
-// N 16-byte LDS reads (N = 4 or 8), awaited inside the block.
-__device__ __forceinline__ void lds_read16x8(const uint32_t (&ad)[8], v4i (&o)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
-      "ds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\tds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
-      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
-      : "memory");
-}
+// 16-byte LDS reads (four or two), awaited inside the block.
 __device__ __forceinline__ void lds_read16x4(const uint32_t (&ad)[4], v4i (&o)[4]) {
   asm volatile(
       "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
@@ -575,14 +564,32 @@ __device__ __forceinline__ void lds_read16x4(const uint32_t (&ad)[4], v4i (&o)[4
       : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
       : "memory");
 }
+__device__ __forceinline__ void lds_read16x2(const uint32_t (&ad)[2], v4i (&o)[2]) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(o[0]), "=&v"(o[1])
+               : "v"(ad[0]), "v"(ad[1])
+               : "memory");
+}
+
+constexpr int SQ_WAVES = 8;
+// LDS of the staged kernel: per wave one stage (X chunk, low-rank operand chunk) and the
+// code buffer; after the loop the same bytes hold the waves' partial products.
+template <int TP>
+struct SqLds {
+  static constexpr int DB = 2048 * TP;  // low-rank operand per stage: 16 TP x 64 bf16
+  static constexpr int STAGE = SQ_XB + DB;
+  static constexpr int WAVE = STAGE + SQ_CB;
+  static constexpr int RED = SQ_WAVES * 4 * TP * 4 * 64 * 4;
+  static constexpr int BYTES = SQ_WAVES * WAVE > RED ? SQ_WAVES * WAVE : RED;
+};
 
 template <int TP, bool UCOLS, int MODE>
-__global__ __launch_bounds__(256) void k_quant_down_lds(const QuantDownArgs a) {
+__global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDownArgs a) {
   static_assert(TP == 0 || TP == 2 || TP == 4, "staged kernel: rank + stab_rank <= 64");
+  constexpr int NW = SQ_WAVES;
   using L = SqLds<TP>;
   constexpr bool QUANT = MODE == QD_QUANT || MODE == QD_GELU_QUANT;
-  constexpr int NL = SQ_XB / 1024 + L::DB / 1024;  // direct-to-LDS loads per stage
-  constexpr int NS = QUANT ? 5 : 0;                // stores per pair: 4 code blocks, 1 scale
+  constexpr int NS = QUANT ? 5 : 0;  // stores per pair: 4 code blocks, 1 scale
   __shared__ __align__(16) char smem_raw[L::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -594,7 +601,7 @@ __global__ __launch_bounds__(256) void k_quant_down_lds(const QuantDownArgs a) {
   const int64_t nchunks = (a.K + CHUNK - 1) / CHUNK;
   const int64_t per = (nchunks + S - 1) / S;
   const int64_t ch0 = split * per, ch1 = min(nchunks, ch0 + per);
-  const int rounds = (int)((max<int64_t>(ch1 - ch0, 0) + 2 * QD_WAVES - 1) / (2 * QD_WAVES));
+  const int rounds = (int)((max<int64_t>(ch1 - ch0, 0) + 2 * NW - 1) / (2 * NW));
   const int64_t cpitch = a.K >> 1, nkb = a.K >> 5;
   const int ta = a.r0 / 16, r1 = a.rt - a.r0;
 
@@ -604,9 +611,8 @@ __global__ __launch_bounds__(256) void k_quant_down_lds(const QuantDownArgs a) {
   const bufres rd0 = make_buf(a.d0, (uint64_t)a.K * a.r0 * 2);
   const bufres rd1 = make_buf(a.d1, (uint64_t)a.K * r1 * 2);
 
-  lds_char* const st0 = (lds_char*)smem_raw + wave * L::WAVE;
-  lds_char* const st1 = st0 + L::STAGE;
-  lds_char* const cbuf = st0 + 2 * L::STAGE;
+  lds_char* const st = (lds_char*)smem_raw + wave * L::WAVE;
+  lds_char* const cbuf = st + L::STAGE;
 
   v4f acc[4][TP > 0 ? TP : 1];
 #pragma unroll
@@ -614,15 +620,13 @@ __global__ __launch_bounds__(256) void k_quant_down_lds(const QuantDownArgs a) {
 #pragma unroll
     for (int t = 0; t < (TP > 0 ? TP : 1); ++t) acc[g][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // chunk i (0, 1) of this wave's pair in round k; live while below ch1
-  auto chunk_of = [&](int k, int i) -> int64_t { return ch0 + 2 * QD_WAVES * k + 2 * wave + i; };
+  auto chunk_of = [&](int k, int i) -> int64_t { return ch0 + 2 * NW * k + 2 * wave + i; };
 
-  // ---- one chunk's operands into a stage
-  auto dma = [&](lds_char* st, int64_t c) __attribute__((always_inline)) {
+  auto dma = [&](int64_t c) __attribute__((always_inline)) {
     const bool live = c < ch1;
     const int64_t c0 = c * CHUNK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // X rows 8i + l/8, slot l%8 holding unit (l%8) ^ swz(row)
+    for (int i = 0; i < 8; ++i) {
       const int row = 8 * i + (lane >> 3);
       const int64_t col = c0 + 8 * ((lane & 7) ^ sq_swz(row));
       buf_load16_lds(rx, st + i * 1024,
@@ -632,15 +636,13 @@ __global__ __launch_bounds__(256) void k_quant_down_lds(const QuantDownArgs a) {
       lds_char* const sd = st + SQ_XB;
 #pragma unroll
       for (int i = 0; i < 2 * TP; ++i) {
-        const bool first = 8 * i < a.r0;  // uniform: r0 is a multiple of 16
+        const bool first = 8 * i < a.r0;
         if constexpr (!UCOLS) {
-          // D rows 8i + l/8 (first factor rows j < r0, K-contiguous), same swizzle as X
           const int jj = 8 * i + (lane >> 3);
           const int64_t j = first ? jj : jj - a.r0;
           const int64_t col = c0 + 8 * ((lane & 7) ^ sq_swz(jj));
           buf_load16_lds(first ? rd0 : rd1, sd + i * 1024, sel_off(live && col < a.K, (uint32_t)((j * a.K + col) * 2)));
         } else {
-          // factor rows c0 .. c0+63 are 128 r_f contiguous bytes; r_f / 8 loads each
           const int rf = first ? a.r0 : r1;
           const int o = (first ? i : i - a.r0 / 8) * 1024 + 16 * lane;
           const bool ok = live && (int64_t)o < (a.K - c0) * 2 * rf;
@@ -650,153 +652,132 @@ __global__ __launch_bounds__(256) void k_quant_down_lds(const QuantDownArgs a) {
     }
   };
 
-  // ---- one chunk: operand reads, MFMAs, quantization (codes into cbuf)
-  uint32_t sbs0 = 0, sbs1 = 0;  // the pair's scale bytes: block row h, byte 2i + b
-  auto work = [&](const lds_char* st, int i) __attribute__((always_inline)) {
-    v4i xv[8];  // [2g + b]: rows 16g + l%16, columns 32b + 8(l/16) .. +8 of the chunk
+  uint32_t sbs0 = 0, sbs1 = 0;
+  // column block b (32 columns) of chunk i (0, 1) of the pair
+  auto work_half = [&](int i, int b) __attribute__((always_inline)) {
+    v4i xv[4];  // rows 16g + l%16, columns 32b + 8(l/16) .. +8
     {
-      uint32_t ad[8];
+      uint32_t ad[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int row = 16 * g + lr;
-          ad[2 * g + b] = lds_addr(st + row * 128 + (((4 * b + lq) ^ sq_swz(row)) << 4));
-        }
-      lds_read16x8(ad, xv);
+      for (int g = 0; g < 4; ++g) {
+        const int row = 16 * g + lr;
+        ad[g] = lds_addr(st + row * 128 + (((4 * b + lq) ^ sq_swz(row)) << 4));
+      }
+      lds_read16x4(ad, xv);
     }
-    float hv[4][2][8];  // GELU mode: H = GELU(P^) in fp32
+    float hv[4][8];
     if constexpr (MODE == QD_GELU_QUANT) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t ws[4] = {(uint32_t)xv[g].x, (uint32_t)xv[g].y, (uint32_t)xv[g].z, (uint32_t)xv[g].w};
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const v4i w = xv[2 * g + b];
-          const uint32_t ws[4] = {(uint32_t)w.x, (uint32_t)w.y, (uint32_t)w.z, (uint32_t)w.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hv[g][b][2 * e] = gelu_f(bf16_lo(ws[e]));
-            hv[g][b][2 * e + 1] = gelu_f(bf16_hi(ws[e]));
-          }
+        for (int e = 0; e < 4; ++e) {
+          hv[g][2 * e] = gelu_f(bf16_lo(ws[e]));
+          hv[g][2 * e + 1] = gelu_f(bf16_hi(ws[e]));
         }
+      }
     }
     if constexpr (TP > 0) {
-      v4i dv[TP][2];  // first MFMA operand: tile t (rank columns 16t .. +16), column block b
+      v4i dv[TP];
       const lds_char* const sd = st + SQ_XB;
       if constexpr (!UCOLS) {
-        uint32_t ad[2 * TP];
+        uint32_t ad[TP];
 #pragma unroll
-        for (int t = 0; t < TP; ++t)
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const int jj = 16 * t + lr;
-            ad[2 * t + b] = lds_addr(sd + jj * 128 + (((4 * b + lq) ^ sq_swz(jj)) << 4));
-          }
-        v4i o[2 * TP];
-        if constexpr (TP == 4) lds_read16x8(ad, o);
-        else lds_read16x4(ad, o);
-#pragma unroll
-        for (int t = 0; t < TP; ++t) dv[t][0] = o[2 * t], dv[t][1] = o[2 * t + 1];
+        for (int t = 0; t < TP; ++t) {
+          const int jj = 16 * t + lr;
+          ad[t] = lds_addr(sd + jj * 128 + (((4 * b + lq) ^ sq_swz(jj)) << 4));
+        }
+        if constexpr (TP == 4) lds_read16x4(ad, dv);
+        else lds_read16x2(ad, dv);
       } else {
-        // lane l of 16-lane group g: rank column 16t + l%16 at rows 32b + 8g .. +8 of the
-        // chunk. Within the group, lane s addresses 4 consecutive rank columns
-        // (4(s%4) on) of row 32b + 8g + s/4; ds_read_b64_tr_b16 hands lane s column s of
-        // those 4 rows, and a second read 4 rows on covers the other 4.
         const int gq = lane >> 4, s = lane & 15;
 #pragma unroll
         for (int t = 0; t < TP; t += 2) {
+          uint32_t p[2], pitch[2];
 #pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            uint32_t p[2], pitch[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const bool first = t + u < ta;
-              const int rf = first ? a.r0 : r1;
-              const int jl = 16 * (first ? t + u : t + u - ta) + 4 * (s & 3);
-              const int n = 32 * b + 8 * gq + (s >> 2);
-              pitch[u] = (uint32_t)(2 * rf);
-              p[u] = lds_addr(sd + (first ? 0 : 128 * a.r0)) + (uint32_t)(n * 2 * rf + 2 * jl);
-            }
-            v2i w, x, y, z;
-            asm volatile(
-                "ds_read_b64_tr_b16 %0, %4\n\t"
-                "ds_read_b64_tr_b16 %1, %5\n\t"
-                "ds_read_b64_tr_b16 %2, %6\n\t"
-                "ds_read_b64_tr_b16 %3, %7\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(w), "=&v"(x), "=&v"(y), "=&v"(z)
-                : "v"(p[0]), "v"(p[0] + 4 * pitch[0]), "v"(p[1]), "v"(p[1] + 4 * pitch[1])
-                : "memory");
-            dv[t][b] = v4i{w.x, w.y, x.x, x.y};
-            dv[t + 1][b] = v4i{y.x, y.y, z.x, z.y};
+          for (int u = 0; u < 2; ++u) {
+            const bool first = t + u < ta;
+            const int rf = first ? a.r0 : r1;
+            const int jl = 16 * (first ? t + u : t + u - ta) + 4 * (s & 3);
+            const int n = 32 * b + 8 * gq + (s >> 2);
+            pitch[u] = (uint32_t)(2 * rf);
+            p[u] = lds_addr(sd + (first ? 0 : 128 * a.r0)) + (uint32_t)(n * 2 * rf + 2 * jl);
           }
+          v2i w, x, y, z;
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %4\n\t"
+              "ds_read_b64_tr_b16 %1, %5\n\t"
+              "ds_read_b64_tr_b16 %2, %6\n\t"
+              "ds_read_b64_tr_b16 %3, %7\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(w), "=&v"(x), "=&v"(y), "=&v"(z)
+              : "v"(p[0]), "v"(p[0] + 4 * pitch[0]), "v"(p[1]), "v"(p[1] + 4 * pitch[1])
+              : "memory");
+          dv[t] = v4i{w.x, w.y, x.x, x.y};
+          dv[t + 1] = v4i{y.x, y.y, z.x, z.y};
         }
       }
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        v4i xop[4];
+      for (int g = 0; g < 4; ++g) {
+        v4i xop;
+        if constexpr (MODE == QD_GELU_QUANT)
+          xop = v4i{(int)pack_bf16x2(hv[g][0], hv[g][1]), (int)pack_bf16x2(hv[g][2], hv[g][3]),
+                    (int)pack_bf16x2(hv[g][4], hv[g][5]), (int)pack_bf16x2(hv[g][6], hv[g][7])};
+        else
+          xop = xv[g];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          if constexpr (MODE == QD_GELU_QUANT)
-            xop[g] = v4i{(int)pack_bf16x2(hv[g][b][0], hv[g][b][1]), (int)pack_bf16x2(hv[g][b][2], hv[g][b][3]),
-                         (int)pack_bf16x2(hv[g][b][4], hv[g][b][5]), (int)pack_bf16x2(hv[g][b][6], hv[g][b][7])};
-          else
-            xop[g] = xv[2 * g + b];
-        }
-#pragma unroll
-        for (int t = 0; t < TP; ++t)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) acc[g][t] = mfma16(dv[t][b], xop[g], acc[g][t]);
+        for (int t = 0; t < TP; ++t) acc[g][t] = mfma16(dv[t], xop, acc[g][t]);
       }
     }
     if constexpr (QUANT) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h) {
+        uint32_t m = 0;
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          uint32_t m = 0;
+        for (int q = 0; q < 2; ++q) {
+          const int g = 2 * h + q;
+          if constexpr (MODE == QD_GELU_QUANT) {
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int g = 2 * h + q;
-            if constexpr (MODE == QD_GELU_QUANT) {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) m = umax(m, __builtin_bit_cast(uint32_t, hv[g][b][e]) & 0x7FFFFFFFu);
-            } else {
-              const v4i w = xv[2 * g + b];
-              m = umax(m, umax(umax(bf16x2_absmax_bits(w.x), bf16x2_absmax_bits(w.y)),
-                               umax(bf16x2_absmax_bits(w.z), bf16x2_absmax_bits(w.w))));
-            }
-          }
-          const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
-          const float scale = e8m0_to_f32_scale(sb);
-          if (h == 0) sbs0 |= sb << (8 * (2 * i + b));
-          else sbs1 |= sb << (8 * (2 * i + b));
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int g = 2 * h + q;
-            uint32_t cw;
-            if constexpr (MODE == QD_GELU_QUANT) {
-              cw = cvt8_f32(hv[g][b], scale);
-            } else {
-              const v4i w = xv[2 * g + b];
-              cw = cvt8_bf16(w.x, w.y, w.z, w.w, scale);
-            }
-            if (sb == 0xFFu) cw = 0;
-            const int row = 16 * g + lr;
-            const uint32_t ad = lds_addr(cbuf + row * 64 + (((2 * i + b) ^ ((row >> 2) & 3)) << 4) + 4 * lq);
-            asm volatile("ds_write_b32 %0, %1" ::"v"(ad), "v"(cw) : "memory");
+            for (int e = 0; e < 8; ++e) m = umax(m, __builtin_bit_cast(uint32_t, hv[g][e]) & 0x7FFFFFFFu);
+          } else {
+            const v4i w = xv[g];
+            m = umax(m, umax(umax(bf16x2_absmax_bits(w.x), bf16x2_absmax_bits(w.y)),
+                             umax(bf16x2_absmax_bits(w.z), bf16x2_absmax_bits(w.w))));
           }
         }
+        const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
+        const float scale = e8m0_to_f32_scale(sb);
+        if (h == 0) sbs0 |= sb << (8 * (2 * i + b));
+        else sbs1 |= sb << (8 * (2 * i + b));
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int g = 2 * h + q;
+          uint32_t cw;
+          if constexpr (MODE == QD_GELU_QUANT) {
+            cw = cvt8_f32(hv[g], scale);
+          } else {
+            const v4i w = xv[g];
+            cw = cvt8_bf16(w.x, w.y, w.z, w.w, scale);
+          }
+          if (sb == 0xFFu) cw = 0;
+          const int row = 16 * g + lr;
+          const uint32_t ad = lds_addr(cbuf + row * 64 + (((2 * i + b) ^ ((row >> 2) & 3)) << 4) + 4 * lq);
+          asm volatile("ds_write_b32 %0, %1" ::"v"(ad), "v"(cw) : "memory");
+        }
+      }
     }
   };
+  auto work = [&](int i) __attribute__((always_inline)) {
+    work_half(i, 0);
+    work_half(i, 1);
+  };
 
-  // ---- the pair's codes (64 bytes of each row) and scale bytes, from cbuf
   auto store_pair = [&](int k) __attribute__((always_inline)) {
-    const int64_t pc = chunk_of(k, 0) * CHUNK;  // first column of the pair
+    const int64_t pc = chunk_of(k, 0) * CHUNK;
     uint32_t ad[4];
     v4i cv[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {  // lane l: row 16q + l/4, unit l%4
+    for (int q = 0; q < 4; ++q) {
       const int row = 16 * q + (lane >> 2), u = lane & 3;
       ad[q] = lds_addr(cbuf + row * 64 + ((u ^ ((row >> 2) & 3)) << 4));
     }
@@ -808,18 +789,16 @@ __global__ __launch_bounds__(256) void k_quant_down_lds(const QuantDownArgs a) {
       const int row = 16 * q + (lane >> 2);
       buf_store16(rcodes, sel_off(uok && row < rows_left, (uint32_t)((r0 + row) * cpitch + (pc >> 1) + 16 * u)), cv[q]);
     }
-    // lanes 0..7: block row l/4, byte l%4 (column block pc/32 + l%4)
     const int h = (lane >> 2) & 1, e = lane & 3;
     const uint32_t v = ((h ? sbs1 : sbs0) >> (8 * e)) & 0xFFu;
     const bool sok = lane < 8 && r0 + 32 * h < a.M && chunk_of(k, e >> 1) < ch1 && pc + 32 * e < a.K;
     buf_store1(rscales, sel_off(sok, (uint32_t)((r0 / 32 + h) * nkb + (pc >> 5) + e)), v);
   };
 
-  dma(st0, chunk_of(0, 0));
-  dma(st1, chunk_of(0, 1));
+  dma(chunk_of(0, 0));
   if constexpr (NS > 0) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {  // stand-ins for a previous pair's stores (see above)
+    for (int i = 0; i < NS; ++i) {
       uint32_t off = BUF_OOB + 16u * i;
       asm volatile("" : "+v"(off));
       buf_store4(rcodes, off, 0u);
@@ -827,18 +806,18 @@ __global__ __launch_bounds__(256) void k_quant_down_lds(const QuantDownArgs a) {
   }
   for (int k = 0; k < rounds; ++k) {
     sbs0 = sbs1 = 0;
-    wait_vmcnt<NL + NS>();  // stage 0 landed (stage 1 and the last pair's stores may not have)
-    work(st0, 0);
-    dma(st0, chunk_of(k + 1, 0));
-    wait_vmcnt<NS + NL>();  // stage 1 landed
-    work(st1, 1);
-    dma(st1, chunk_of(k + 1, 1));
+    wait_vmcnt<NS>();  // chunk (k, 0) landed; the last pair's stores may still be in flight
+    work(0);
+    dma(chunk_of(k, 1));
+    wait_vmcnt<0>();
+    work(1);
+    dma(chunk_of(k + 1, 0));
     if constexpr (NS > 0) store_pair(k);
   }
   if constexpr (TP > 0) {
-    wait_vmcnt<0>();  // the reduction area aliases the stages: every load has landed
+    wait_vmcnt<0>();
     __syncthreads();
-    reduce_waves<TP>(acc, (float*)smem_raw, a, r0, split, S, wave, lane, tid);
+    reduce_waves<TP, NW>(acc, (float*)smem_raw, a, r0, split, S, wave, lane, tid);
   }
 }
 
@@ -870,7 +849,7 @@ hipError_t launch_t(const QuantDownArgs& a, int tp, int splits, hipStream_t stre
 
 template <bool UCOLS, int MODE>
 hipError_t launch_staged(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
-  dim3 grid((unsigned)((a.M + QD_ROWS - 1) / QD_ROWS), (unsigned)splits), block(256);
+  dim3 grid((unsigned)((a.M + QD_ROWS - 1) / QD_ROWS), (unsigned)splits), block(64 * SQ_WAVES);
   switch (tp) {
     case 0: hipLaunchKernelGGL((k_quant_down_lds<0, UCOLS, MODE>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((k_quant_down_lds<2, UCOLS, MODE>), grid, block, 0, stream, a); break;
