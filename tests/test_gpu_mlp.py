@@ -158,6 +158,9 @@ MLP_CASES = [
     (300, 384, 768, 16, 16, "bf16"),    # r % 32 == 16: padded low-rank tiles
     (96, 256, 512, 32, 0, "fp32"),
     (130, 320, 640, 0, 32, "bf16"),
+    # the pass over FC1's output in four column ranges, one range's last chunk pair
+    # reaching into the next, the last chunk half past F
+    (640, 512, 2080, 32, 32, "bf16"),
 ]
 
 
