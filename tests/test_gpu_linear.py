@@ -79,6 +79,9 @@ CASES = [
     # range's last chunk pair reaching into the second, the last chunk half past K
     (640, 1056, 1056, 32, 32, "bf16"),
     (600, 1120, 1088, 16, 16, "bf16"),
+    # tiny: a single reduction block (K = 32), a partial first row block, ragged tiles
+    (7, 96, 32, 16, 16, "bf16"),
+    (33, 64, 96, 0, 32, "bf16"),
 ]
 
 
