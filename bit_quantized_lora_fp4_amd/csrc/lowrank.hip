@@ -269,9 +269,15 @@ int lora_grad_tiles(int64_t K, int64_t N) {
   return (int)((K + LG_Q - 1) / LG_Q + (N + LG_Q - 1) / LG_Q);
 }
 
+// Row ranges per tile: enough for about 192 workgroups. Fewer ranges mean fewer fp32
+// partials (written here, read again by k_lora_reduce) and longer-lived waves; at
+// 4608 x 3072 (96 tiles) 2 ranges ran the fused linear ~1.5% faster than 6 (a 512
+// target), and 1 range (96 workgroups) was slower.
+constexpr int LG_TARGET_WGS = 192;
+
 int lora_grad_splits(int64_t M, int64_t K, int64_t N) {
   const int tiles = lora_grad_tiles(K, N);
-  int64_t s = (512 + tiles - 1) / tiles;
+  int64_t s = (LG_TARGET_WGS + tiles - 1) / tiles;
   const int64_t maxs = M / (2 * LG_WAVES * LG_SLAB);  // at least two slabs per wave
   if (s > maxs) s = maxs;
   if (s > 64) s = 64;
