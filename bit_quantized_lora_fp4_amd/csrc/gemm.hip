@@ -15,9 +15,10 @@
 // elements fall in (§3.2: a 4-bit block and its scale are fetched together in either
 // orientation, with no dequantize/requantize).
 //
-// Tiling. A workgroup of 4 waves computes a 256 x 256 output tile, each wave a
-// 128 x 128 quarter as 4 x 4 tiles of V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP4 x FP4,
-// one E8M0 scale per lane = per 32 reduction elements). The reduction advances 256
+// Tiling. A workgroup of 8 waves (two per SIMD) computes a 256 x 256 output tile, each
+// wave 128 rows x 64 columns as 2 x 4 tiles of V_MFMA_SCALE_F32_32X32X64_F8F6F4 (FP4 x
+// FP4, one E8M0 scale per lane = per 32 reduction elements); the layout is a template
+// parameter (Waves<NWN>), 4 waves of 128 x 128 being the other instance. The reduction advances 256
 // elements per step. A step's two code tiles (32 KB each, 128-byte rows: whole cache
 // lines) land in one of two LDS stages by direct-to-LDS buffer loads issued during the
 // step before, one 1 KB segment per scheduling region so the loads go out between
@@ -48,16 +49,30 @@ namespace ft {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 256;    // output tile (rows, cols), reduction step
-constexpr int TI = 4, TJ = 4;                  // 32x32 MFMA tiles per wave: R side, act side
+constexpr int TJ = 4;                          // 32x32 MFMA tiles per wave, activation side
 constexpr int SUBSTEPS = BK / 64;              // MFMA reduction substeps per step
 constexpr int TILE_BYTES = 256 * BK / 2;       // 32 KB of codes per operand tile per step
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // activation tile + R tile
-constexpr int SEGS = TILE_BYTES / 1024 / 4;    // 1 KB load segments per wave per tile (8)
 constexpr int SCALE_BYTES = 8192;              // LDS for the two operands' block scales
 constexpr int TOUCH_BYTES = 1024;              // landing slots of the L2 prefetch loads
-constexpr int TOUCHES = 2;                     // prefetch loads per wave per step
 constexpr int MAX_NKB = SCALE_BYTES / 2 / 8;   // 8 block rows per operand: Kred <= 16384
-constexpr int SW = 8 * MAX_NKB / 4 / 256;      // scale words staged per thread per operand (4)
+#ifndef GEMM_NWN
+#define GEMM_NWN 4
+#endif
+
+// Wave layout of the 256 x 256 tile: 2 waves along the rows (128 each) and NWN along
+// the columns. NWN = 4 (8 waves, two per SIMD, 128 x 64 each): while one wave of a
+// SIMD stalls issuing its direct-to-LDS loads the other keeps the matrix pipe busy.
+template <int NWN>
+struct Waves {
+  static constexpr int N = 2 * NWN;                  // waves per workgroup
+  static constexpr int NT = 64 * N;                  // threads
+  static constexpr int WCOLS = BN / NWN;             // output columns per wave
+  static constexpr int TI = WCOLS / 32;              // 32x32 MFMA tiles per wave, R side
+  static constexpr int SEGS = TILE_BYTES / 1024 / N; // 1 KB load segments per wave per tile
+  static constexpr int TOUCHES = 8 / N;              // L2 prefetch loads per wave per step
+  static constexpr int SW = 8 * MAX_NKB / 4 / NT;    // scale words staged per thread per operand
+};
 
 
 __device__ __forceinline__ v4i lds_read_b128(const lds_char* p) {
@@ -182,8 +197,11 @@ __device__ __forceinline__ void quant_tile_store(const float (&v)[16], int lane,
   buf_store1(rscales, sel_off(blk_ok && lane == 0, (uint32_t)(blk_row * nkb + (col0 >> 5))), sb);
 }
 
-template <bool TRANS_B, bool OUT_BF16, int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
+template <bool TRANS_B, bool OUT_BF16, int EPI, int NWN>
+__global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g) {
+  using W = Waves<NWN>;
+  constexpr int TI = W::TI, SEGS = W::SEGS, TOUCHES = W::TOUCHES, SW = W::SW, NT = W::NT;
+  constexpr int WCOLS = W::WCOLS;
   // Separate LDS objects per stage: the compiler then knows a transposed LDS read of one
   // stage cannot alias the direct-to-LDS loads still filling the other, and does not
   // drain those loads before the read.
@@ -196,7 +214,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // wave's half of the tile rows / columns
+  const int wm = wave / NWN, wn = wave % NWN;  // wave's half of the tile rows, its column slice
   const int half = lane >> 5;               // which 32-element half of a 64-step this lane holds
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
   int tm, tn;
@@ -275,11 +293,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   };
 
   // ---- L2 prefetch of a later step: one 4-byte load per 128-byte line of both operand
-  // tiles (lane l of wave w touches row 64w + l), landing in a dummy LDS slot. Issued
-  // after a step's stage loads and allowed to stay in flight across the step's wait,
-  // it turns the stage loads of the step after into L2 hits.
-  lds_char* touch = (lds_char*)touch_raw + wave * 256;
-  const int trow = wave * 64 + lane;
+  // tiles (lane l of wave w touches row 64(w%4) + l: of both tiles with 4 waves, of the
+  // activation tile for waves 0-3 and the R tile for waves 4-7 with 8), landing in a
+  // dummy LDS slot. Issued after a step's stage loads and allowed to stay in flight
+  // across the step's wait, it turns the stage loads of the step after into L2 hits.
+  lds_char* touch = (lds_char*)touch_raw + (wave & 3) * 256;
+  const int trow = (wave & 3) * 64 + lane;
   const bool ta_ok = m0 + trow < g.M;
   const uint32_t ta_base = (uint32_t)((m0 + trow) * a_pitch);
   uint32_t tr_base;
@@ -293,8 +312,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   }
   auto prefetch = [&](int kt) {
     const bool live = kt < KT;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)touch, 4,
-                                             (int)sel_off(live && ta_ok, ta_base + (uint32_t)kt * (BK / 2)), 0, 0, 0);
+    const bool ak = live && ta_ok;
+    const uint32_t ao = ta_base + (uint32_t)kt * (BK / 2);
     uint32_t ro;
     bool rk = live && tr_ok;
     if constexpr (!TRANS_B) ro = tr_base + (uint32_t)kt * (BK / 2);
@@ -302,8 +321,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       ro = tr_base + (uint32_t)((int64_t)kt * BK * g.b_pitch);
       rk = rk && (int64_t)kt * BK + trow < Kred;
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)touch, 4,
-                                             (int)sel_off(rk, ro), 0, 0, 0);
+    if constexpr (W::N == 4) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)touch, 4,
+                                               (int)sel_off(ak, ao), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)touch, 4,
+                                               (int)sel_off(rk, ro), 0, 0, 0);
+    } else {
+      const bool act = wave < 4;  // uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(act ? ra : rr, (__attribute__((address_space(3))) void*)touch, 4,
+                                               (int)sel_off(act ? ak : rk, act ? ao : ro), 0, 0, 0);
+    }
   };
 
   // ---- block scales for the whole reduction, staged once, step-major: for step kt,
@@ -318,7 +345,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   lds_char* sSA = (lds_char*)scale_raw;
   lds_char* sSR = sSA + SCALE_BYTES / 2;
   const int wpr = sp / 4;  // words per staged row
-  uint32_t sa_w[SW], sr_w[SW], st_lo[2], st_hi[2];
+  constexpr int SKB = MAX_NKB / NT > 0 ? MAX_NKB / NT : 1;  // backward scale rows per thread
+  uint32_t sa_w[SW], sr_w[SW], st_lo[SKB], st_hi[SKB];
   auto word = [&](bufres res, int64_t row, bool row_ok, int64_t pitch, int kw) -> uint32_t {
     // bytes 4kw .. 4kw+3 of a scale row, zero past the row end
     const int64_t o = row * pitch + 4 * kw;
@@ -331,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   };
 #pragma unroll
   for (int u = 0; u < SW; ++u) {
-    const int e = tid + 256 * u, blk = e / max(wpr, 1), kw = e % max(wpr, 1);
+    const int e = tid + NT * u, blk = e / max(wpr, 1), kw = e % max(wpr, 1);
     const bool live = e < 8 * wpr;
     const int64_t arb = (m0 >> 5) + blk;
     sa_w[u] = word(rsa, arb, live && arb < nrb_a, nkb, kw);
@@ -343,8 +371,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   if constexpr (TRANS_B) {
     // scale row kb (reduction block) holds output blocks cb0 .. cb0+7 in 8 bytes
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kb = tid + 256 * u;
+    for (int u = 0; u < SKB; ++u) {
+      const int kb = tid + NT * u;
       const bool live = kb < nkb;
       const int64_t o = (int64_t)kb * nkb_r + (n0 >> 5);
       if ((nkb_r & 3) == 0) {
@@ -375,7 +403,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   auto write_scales = [&]() {
 #pragma unroll
     for (int u = 0; u < SW; ++u) {
-      const int e = tid + 256 * u, blk = e / max(wpr, 1), kw = e % max(wpr, 1);
+      const int e = tid + NT * u, blk = e / max(wpr, 1), kw = e % max(wpr, 1);
       if (e < 8 * wpr) {
         put_word(sSA, blk, kw, sa_w[u]);
         if constexpr (!TRANS_B) put_word(sSR, blk, kw, sr_w[u]);
@@ -383,8 +411,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     }
     if constexpr (TRANS_B) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int kb = tid + 256 * u;
+      for (int u = 0; u < SKB; ++u) {
+        const int kb = tid + NT * u;
         if (kb < sp) {  // rows kb in [nkb, sp) are the zero padding
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
@@ -413,14 +441,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     v4i x[TJ], r[TI];
   };
   // backward: this lane's byte offset of fragment 0 within an R tile, for the
-  // transposed reads (row 32*half + (lane&15), unit 4wn, byte 8*(lane/16 % 2) of the
+  // transposed reads (row 32*half + (lane&15), unit TI*wn, byte 8*(lane/16 % 2) of the
   // unit). Kept opaque so each read's address stays one step from its stage: the
   // compiler then knows which LDS object it reads and that in-flight loads into the
   // other stage cannot alias it.
   uint32_t frag_tr = 0;
   if constexpr (TRANS_B) {
     const int rb = 32 * half + (lane & 15);
-    frag_tr = (uint32_t)(rb * 128 + (((4 * wn) ^ swz8(rb)) << 4) + ((lane >> 4) & 1) * 8);
+    frag_tr = (uint32_t)(rb * 128 + (((TI * wn) ^ swz8(rb)) << 4) + ((lane >> 4) & 1) * 8);
     asm("" : "+v"(frag_tr));
   }
   auto load_x = [&](const lds_char* st, int s, int j) __attribute__((always_inline)) -> v4i {
@@ -429,7 +457,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   };
   auto load_r = [&](const lds_char* st, int s, int i) __attribute__((always_inline)) -> v4i {
     if constexpr (!TRANS_B) {
-      const int row = wn * 128 + 32 * i + (lane & 31);
+      const int row = wn * WCOLS + 32 * i + (lane & 31);
       return lds_read_b128(st + TILE_BYTES + off128(row, 2 * s + half));
     } else {
       const uint32_t o = frag_tr ^ (uint32_t)(i << 4);
@@ -449,14 +477,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     if constexpr (!TRANS_B) {
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int row = wn * 128 + 32 * i + (lane & 31);
+        const int row = wn * WCOLS + 32 * i + (lane & 31);
         f.r[i] = lds_read_b128(sR + off128(row, 2 * s + half));
       }
     } else {
-      // output column c = wn*128 + 32i + (lane&31); reduction rows
+      // output column c = wn*WCOLS + 32i + (lane&31); reduction rows
       // 64s + 32*half + 16h + (lane&15): two 16x16 nibble transposes per fragment.
       // off128(64s + 16h + rb, unit) = off128(rb, unit) + 8192s + 2048h (swz8 ignores
-      // row bits 3 and up), and fragment i's unit is 4wn + i, so its offset is the
+      // row bits 3 and up), and fragment i's unit is TI*wn + i, so its offset is the
       // lane's base with i XORed into the unit field.
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
@@ -469,9 +497,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   };
   auto load_scales = [&](int kt, uint32_t (&xs)[TJ], uint32_t (&rs)[TI]) {
     const v4i a = lds_read_b128(sSA + 64 * kt + 32 * half + 16 * wm);
-    const v4i r = lds_read_b128(sSR + 64 * kt + 32 * half + 16 * wn);
     xs[0] = a.x, xs[1] = a.y, xs[2] = a.z, xs[3] = a.w;
-    rs[0] = r.x, rs[1] = r.y, rs[2] = r.z, rs[3] = r.w;
+    if constexpr (TI == 4) {
+      const v4i r = lds_read_b128(sSR + 64 * kt + 32 * half + 16 * wn);
+      rs[0] = r.x, rs[1] = r.y, rs[2] = r.z, rs[3] = r.w;
+    } else {
+      const v2i r = *reinterpret_cast<const __attribute__((address_space(3))) v2i*>(sSR + 64 * kt + 32 * half + 4 * TI * wn);
+      rs[0] = r.x, rs[1] = r.y;
+    }
   };
   // ---- operands of the up-projection's first 64 low-rank columns. They are loaded by
   // the last reduction step into the stage it frees, in place of a next step's codes,
@@ -496,9 +529,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
                              : make_buf(g.up1, (uint64_t)g.N * g.up1_ld * 2);
   constexpr int DP1 = BN * 2;  // row pitch of the backward up side (bytes)
   // Per-lane parts of those loads' offsets; the rest of each offset is wave-uniform
-  // (segment q = 8 wave + i: unit c = 2 wave + i/4, rows 64 (i%4) .. +64).
+  // (segment q = SEGS wave + i: unit c = q/4, rows 64 (q%4) .. +64; SEGS is a multiple
+  // of 4, so q%4 = i%4).
   const int lim_m = (int)min<int64_t>(g.M - m0, BM), lim_n = (int)min<int64_t>(g.N - n0, BN);
-  const uint32_t low_base = (uint32_t)(2 * (m0 + lane) * rt + 32 * wave);
+  const uint32_t low_base = (uint32_t)(2 * (m0 + lane) * rt);
   uint32_t up_base0, up_base1;
   if constexpr (!TRANS_B) {
     up_base0 = (uint32_t)(2 * (n0 + lane) * g.up0_ld);
@@ -508,11 +542,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     up_base1 = (uint32_t)(2 * ((lane >> 5) * g.up1_ld + n0 + 8 * (lane & 31)));
   }
   // Point the stage loads at the up-projection's operands: issue_part(st, KT, i, part)
-  // then loads segment q = 8 wave + i of the low side (part 0) or the up side (part 1).
-  // Every segment of a wave draws from one source tensor: its up-side rows / units
-  // start at 16 wave, and up_split is a multiple of 16.
+  // then loads segment q = SEGS wave + i of the low side (part 0) or the up side (part 1).
+  // Every segment of a wave draws from one source tensor: its up-side units (forward)
+  // or row pairs (backward) cover rank columns 2 SEGS wave .. +2 SEGS, and up_split is
+  // a multiple of 16 >= 2 SEGS.
   auto switch_to_low = [&]() {
-    const bool first = 16 * wave < g.up_split;
+    const bool first = 2 * SEGS * wave < g.up_split;
     src_a = rl;
     src_r = first ? ru0 : ru1;
     kred_eff = 1 << 30;  // the reduction-range test passes; a_ok / r_ok decide
@@ -522,7 +557,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     for (int i = 0; i < SEGS; ++i) {
       const int q = wave * SEGS + i;
       a_ok[i] = lane + 64 * (i & 3) < lim_m && 8 * (q >> 2) < rt1;
-      a_base[i] = low_base + (uint32_t)(128 * (i & 3) * rt + 16 * (i >> 2)) - back_a;
+      a_base[i] = low_base + (uint32_t)(128 * (i & 3) * rt + 16 * (q >> 2)) - back_a;
       if constexpr (!TRANS_B) {
         const int t = 8 * (q >> 2);
         r_ok[i] = lane + 64 * (i & 3) < lim_n && t < rt1;
@@ -562,7 +597,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
         // pin the MFMAs also fence the scheduler), then its four MFMAs
         issue_part(nxt, kt + 1, (TI * s + q) >> 1, q & 1);
         if (s + 1 < SUBSTEPS) {
-          nf.x[q] = load_x(st, s + 1, q);
+#pragma unroll
+          for (int jj = 0; jj < TJ / TI; ++jj) nf.x[q * (TJ / TI) + jj] = load_x(st, s + 1, q * (TJ / TI) + jj);
           nf.r[q] = load_r(st, s + 1, q);
         }
 #pragma unroll
@@ -592,7 +628,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int64_t q = n0 + wn * 128 + 32 * i + (lane & 31);
+        const int64_t q = n0 + wn * WCOLS + 32 * i + (lane & 31);
         ub[u][i] = (live && t < g.up_split) ? buf_load16(ru0, (uint32_t)((q * g.up0_ld + j0) * 2))
                                             : buf_load16(ru1, sel_off(live, (uint32_t)((q * g.up1_ld + j0 - g.up_split) * 2)));
       }
@@ -623,10 +659,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         if constexpr (!TRANS_B) {
-          ub[i] = lds_read_b128(st + TILE_BYTES + (2 * u + half) * 4096 + (wn * 128 + 32 * i + (lane & 31)) * 16);
+          ub[i] = lds_read_b128(st + TILE_BYTES + (2 * u + half) * 4096 + (wn * WCOLS + 32 * i + (lane & 31)) * 16);
         } else {
           const int gq = lane >> 4, sq = lane & 15;
-          const int col = wn * 128 + 32 * i + 16 * (gq & 1) + 4 * (sq & 3);
+          const int col = wn * WCOLS + 32 * i + 16 * (gq & 1) + 4 * (sq & 3);
           const int m = 16 * u + 8 * (gq >> 1) + (sq >> 2);
           const int o = m * DP1 + col * 2;
           const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -646,8 +682,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
     }
   };
   constexpr int DP = BN * 2 + 32;  // slab row pitch (bytes) of the backward's later slabs
-  auto slab_unit = [&](int jc, int i) __attribute__((always_inline)) -> v4i {
-    const int c = tid + 256 * i, row = c >> 5, c16 = c & 31;
+  auto slab_unit = [&](int jc, int c) __attribute__((always_inline)) -> v4i {
+    const int row = c >> 5, c16 = c & 31;
     const int j = jc + row;
     const int64_t col = n0 + 8 * c16;
     const bool ok = col < g.N && j < rt;
@@ -712,14 +748,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
           la[u][j] = buf_load16(rl, (uint32_t)((row * rt + jc + 16 * u + 8 * half) * 2));
         }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        lds_write_b128(st0 + (i * 8 + (tid >> 5)) * DP + (tid & 31) * 16, slab_unit(jc, i));
+      for (int i = 0; i < 1024 / NT; ++i) {
+        const int c = tid + NT * i;
+        lds_write_b128(st0 + (c >> 5) * DP + (c & 31) * 16, slab_unit(jc, c));
+      }
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         v4i ub[TI];
 #pragma unroll
-        for (int i = 0; i < TI; ++i) ub[i] = lds_tr16_pair(st0, DP, 16 * u, wn * 128 + 32 * i, lane);
+        for (int i = 0; i < TI; ++i) ub[i] = lds_tr16_pair(st0, DP, 16 * u, wn * WCOLS + 32 * i, lane);
 #pragma unroll
         for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -746,7 +784,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int64_t col = n0 + wn * 128 + 32 * i + 8 * gq + 4 * half;
+          const int64_t col = n0 + wn * WCOLS + 32 * i + 8 * gq + 4 * half;
           dst[i][gq] = buf_load8(rpre, sel_off(row < g.M && col < g.N, (uint32_t)((row * g.N + col) * 2)));
         }
     };
@@ -759,7 +797,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       const bool row_ok = row < g.M;
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        const int64_t col0 = n0 + wn * 128 + 32 * i;
+        const int64_t col0 = n0 + wn * WCOLS + 32 * i;
         float v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -777,18 +815,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
   }
 
   // ---------------------------------------------------------------- store
-  // Each wave stages its 128 x 128 result in 32 KB of LDS (half a stage; the stages
-  // are free now), then 16 consecutive lanes write 256 contiguous bytes of one output
-  // row per instruction. acc[i][j]: lane holds output row 32j + l%32 of the wave tile
-  // and, in registers 4g..4g+3, columns 32i + 8g + 4*half .. +4. Staged rows are
-  // 256 B (bf16) or 512 B (fp32, 64 rows per pass) with 16-byte units XOR-swizzled
-  // by the row, so column reads across rows and row reads across units both spread
-  // over the banks.
+  // Each wave stages its 128 x WCOLS result in LDS (the stages are free now: 32 KB per
+  // wave with 4 waves, 16 KB with 8), then consecutive lanes write whole rows of it,
+  // 16 bytes each. acc[i][j]: lane holds output row 32j + l%32 of the wave tile and, in
+  // registers 4g..4g+3, columns 32i + 8g + 4*half .. +4. Staged rows are 2 WCOLS bytes
+  // (bf16) or 4 WCOLS (fp32, 64 rows per pass) with 16-byte units XOR-swizzled by the
+  // row, so column reads across rows and row reads across units both spread over the
+  // banks.
   __syncthreads();
-  lds_char* wbuf = (wave < 2 ? st0 : st1) + (wave & 1) * 32768;
-  auto wofs = [](int r, int byte) { return r * 256 + ((((byte >> 4) ^ r) & 15) << 4) + (byte & 15); };
-  auto wofs_f = [](int r, int byte) { return r * 512 + ((((byte >> 4) ^ r) & 31) << 4) + (byte & 15); };
-  const int64_t orow0 = m0 + wm * 128, ocol0 = n0 + wn * 128;
+  constexpr int WB = 2 * STAGE_BYTES / W::N;
+  lds_char* wbuf = (wave < W::N / 2 ? st0 : st1) + (wave % (W::N / 2)) * WB;
+  constexpr int RB = 2 * WCOLS, UB = RB / 16;       // bf16 staged row
+  constexpr int RBF = 4 * WCOLS, UBF = RBF / 16;    // fp32 staged row
+  auto wofs = [](int r, int byte) { return r * RB + ((((byte >> 4) ^ r) & (UB - 1)) << 4) + (byte & 15); };
+  auto wofs_f = [](int r, int byte) { return r * RBF + ((((byte >> 4) ^ r) & (UBF - 1)) << 4) + (byte & 15); };
+  const int64_t orow0 = m0 + wm * 128, ocol0 = n0 + wn * WCOLS;
   if constexpr (OUT_BF16) {
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
@@ -804,16 +845,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
         }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave's LDS writes are done
+    constexpr int RPI = 64 / UB;  // rows per instruction
 #pragma unroll 4
-    for (int k = 0; k < 32; ++k) {  // 4 rows x 256 bytes per instruction
-      const int r = 4 * k + (lane >> 4), c = (lane & 15) * 8;
+    for (int k = 0; k < 128 / RPI; ++k) {
+      const int r = RPI * k + lane / UB, c = (lane % UB) * 8;
       const v4i v = lds_read_b128(wbuf + wofs(r, c * 2));
       const int64_t row = orow0 + r, col = ocol0 + c;
       if (row < g.M && col < g.N)  // streaming store: the output is not re-read here
         __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(reinterpret_cast<bf16_t*>(g.out) + row * g.ldo + col));
     }
   } else {
-    // fp32: two passes of 64 rows (64 x 512 bytes per wave)
+    // fp32: two passes of 64 rows
+    constexpr int RPI = 64 / UBF;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -831,8 +874,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_mx4(const GemmArgs g) {
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll 4
-      for (int k = 0; k < 32; ++k) {  // 2 rows x 512 bytes per instruction
-        const int r = 2 * k + (lane >> 5), c = (lane & 31) * 4;
+      for (int k = 0; k < 64 / RPI; ++k) {
+        const int r = RPI * k + lane / UBF, c = (lane % UBF) * 4;
         const v4i v = lds_read_b128(wbuf + wofs_f(r, c * 4));
         const int64_t row = orow0 + 64 * p + r, col = ocol0 + c;
         if (row < g.M && col < g.N)
@@ -854,19 +897,19 @@ hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipSt
                                  g.q_scales == nullptr || g.pre == nullptr))
     return hipErrorInvalidValue;
   const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
-  dim3 grid(tiles), block(256);
+  dim3 grid(tiles), block(Waves<GEMM_NWN>::NT);
   if (g.epi == GEMM_EPI_DGELU_Q) {
-    hipLaunchKernelGGL((k_gemm_mx4<true, true, GEMM_EPI_DGELU_Q>), grid, block, 0, stream, g);
+    hipLaunchKernelGGL((k_gemm_mx4<true, true, GEMM_EPI_DGELU_Q, GEMM_NWN>), grid, block, 0, stream, g);
   } else if (!trans_b) {
     if (out_bf16)
-      hipLaunchKernelGGL((k_gemm_mx4<false, true, GEMM_EPI_NONE>), grid, block, 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<false, true, GEMM_EPI_NONE, GEMM_NWN>), grid, block, 0, stream, g);
     else
-      hipLaunchKernelGGL((k_gemm_mx4<false, false, GEMM_EPI_NONE>), grid, block, 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<false, false, GEMM_EPI_NONE, GEMM_NWN>), grid, block, 0, stream, g);
   } else {
     if (out_bf16)
-      hipLaunchKernelGGL((k_gemm_mx4<true, true, GEMM_EPI_NONE>), grid, block, 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<true, true, GEMM_EPI_NONE, GEMM_NWN>), grid, block, 0, stream, g);
     else
-      hipLaunchKernelGGL((k_gemm_mx4<true, false, GEMM_EPI_NONE>), grid, block, 0, stream, g);
+      hipLaunchKernelGGL((k_gemm_mx4<true, false, GEMM_EPI_NONE, GEMM_NWN>), grid, block, 0, stream, g);
   }
   return hipGetLastError();
 }
