@@ -34,9 +34,10 @@
 // Reduction. The four waves' fp32 partial products are summed in LDS in wave order.
 // With S > 1 each range's sum goes to an fp32 partial buffer and a second kernel adds
 // the S partials in range order and rounds once to bf16, so the result does not
-// depend on timing. (A last-arriving-workgroup reduction inside this kernel would
-// need device-scope fences, which on this chip write back and invalidate the whole
-// L2 of the issuing XCD: far dearer than a kernel boundary.)
+// depend on timing. (A last-arriving-workgroup reduction inside this kernel needs
+// device-scope fences, which on this chip write back and invalidate the L2 of the
+// issuing XCD: measured at 4608 x 3072, the kernel went from 13 to 60 us, against
+// ~4.5 us for the second kernel.)
 #include "common.h"
 #include "gemm.h"
 

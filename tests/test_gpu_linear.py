@@ -117,6 +117,58 @@ def test_deterministic():
         assert np.array_equal(a[key], b[key]), key
 
 
+@pytest.mark.parametrize("xdt", ["bf16", "fp32"])  # staged / register quantize kernels
+def test_split_reductions_any_workspace_and_graph_replay(xdt):
+    """The split reductions (fused quantize + down-projection over column ranges, LoRA
+    gradients over row ranges) keep their fp32 partials in the workspace. Whatever the
+    workspace held before (all-ones bytes, random bytes, the previous call's state) the
+    bits come out the same, and so do replays of a captured graph with eager calls on
+    the same workspace between them."""
+    m, n, k = 1024, 3072, 3072  # 16 row stripes x 6 column ranges, 96 tiles x 2 row ranges
+    log(f"linear split reductions m={m} n={n} k={k} x={xdt}: workspace contents, graph replay")
+    d = wl.random_linear(m, n, k, 32, 32, seed=21, x_dtype=xdt, dy_dtype=xdt)
+    L = _gpu_linear(d)
+    x, dy = dev(d["X"], d["x_dtype"]), dev(d["dY"], d["dy_dtype"])
+    xq, gq = abi.Mx4.empty(m, k), abi.Mx4.empty(m, n)
+    ws = abi.workspace(abi.fourtune_linear_workspace_bytes(m, L))
+
+    def step():
+        y, xl = abi.linear_forward(L, x, y_dtype=torch.float32, ws=ws, xq_out=xq)
+        dx, da, db = abi.linear_backward(L, dy, x, xl, dx_dtype=torch.float32, ws=ws, gq_out=gq)
+        return dict(Y=y, XL=xl, dX=dx, dA=da, dB=db)
+
+    def fetch(o):
+        torch.cuda.synchronize()
+        got = {key: host(t) for key, t in o.items()}
+        got["xq"] = (host_u8(xq.codes), host_u8(xq.scales))
+        got["gq"] = (host_u8(gq.codes), host_u8(gq.scales))
+        return got
+
+    def same(a, b, what):
+        for key in ("Y", "XL", "dX", "dA", "dB"):
+            assert np.array_equal(a[key], b[key]), (what, key)
+
+    ws.fill_(0xFF)
+    ref = fetch(step())
+    _check_full(d, ref)
+    same(ref, fetch(step()), "second call, same workspace")
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda"))
+    same(ref, fetch(step()), "random workspace bytes")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step()
+    for rep in range(3):
+        g.replay()
+        same(ref, fetch(outs), f"graph replay {rep}")
+        same(ref, fetch(step()), f"eager call after replay {rep}")
+
+
 def test_workspace_and_argument_errors():
     d = wl.random_linear(64, 256, 256, 16, 16, seed=3)
     L = _gpu_linear(d)
