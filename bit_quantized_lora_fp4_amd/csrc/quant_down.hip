@@ -654,8 +654,10 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
   };
 
   uint32_t sbs0 = 0, sbs1 = 0;
-  // column block b (32 columns) of chunk i (0, 1) of the pair
-  auto work_half = [&](int i, int b) __attribute__((always_inline)) {
+  // column block b (32 columns) of chunk i (0, 1) of the pair. The second block's last
+  // read of the stage is followed by the loads of chunk `pf` into it, which then land
+  // while that block's arithmetic runs.
+  auto work_half = [&](int i, int b, int64_t pf) __attribute__((always_inline)) {
     v4i xv[4];  // rows 16g + l%16, columns 32b + 8(l/16) .. +8
     {
       uint32_t ad[4];
@@ -665,6 +667,9 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
         ad[g] = lds_addr(st + row * 128 + (((4 * b + lq) ^ sq_swz(row)) << 4));
       }
       lds_read16x4(ad, xv);
+    }
+    if constexpr (TP == 0) {
+      if (b == 1) dma(pf);
     }
     float hv[4][8];
     if constexpr (MODE == QD_GELU_QUANT) {
@@ -718,6 +723,7 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
           dv[t + 1] = v4i{y.x, y.y, z.x, z.y};
         }
       }
+      if (b == 1) dma(pf);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         v4i xop;
@@ -768,9 +774,9 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
       }
     }
   };
-  auto work = [&](int i) __attribute__((always_inline)) {
-    work_half(i, 0);
-    work_half(i, 1);
+  auto work = [&](int i, int64_t pf) __attribute__((always_inline)) {
+    work_half(i, 0, pf);
+    work_half(i, 1, pf);
   };
 
   auto store_pair = [&](int k) __attribute__((always_inline)) {
@@ -808,11 +814,9 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
   for (int k = 0; k < rounds; ++k) {
     sbs0 = sbs1 = 0;
     wait_vmcnt<NS>();  // chunk (k, 0) landed; the last pair's stores may still be in flight
-    work(0);
-    dma(chunk_of(k, 1));
+    work(0, chunk_of(k, 1));
     wait_vmcnt<0>();
-    work(1);
-    dma(chunk_of(k + 1, 0));
+    work(1, chunk_of(k + 1, 0));
     if constexpr (NS > 0) store_pair(k);
   }
   if constexpr (TP > 0) {
