@@ -186,6 +186,59 @@ def test_mlp_bf16_outputs_deterministic():
     assert rel_fro(a["dX"], mx4.bf16_round(bwd["dX"])) <= TOL
 
 
+def test_mlp_split_reductions_any_workspace_and_graph_replay():
+    """The MLP pair's split reductions keep their fp32 partials in the workspace: any
+    prior contents (all-ones bytes, random bytes, the previous call's state) give the
+    same bits, and so do replays of a captured forward + backward with eager calls on
+    the same workspace between them."""
+    m, d, f = 640, 512, 2080
+    log(f"mlp split reductions m={m} d={d} f={f}: workspace contents, graph replay")
+    case = wl.random_mlp(m, d, f, 32, 32, seed=31)
+    fc1, fc2 = _gpu_lin(case["fc1"]), _gpu_lin(case["fc2"])
+    x, dy = dev(case["X"], case["x_dtype"]), dev(case["dY"], case["dy_dtype"])
+    hq, dpq = abi.Mx4.empty(m, f), abi.Mx4.empty(m, f)
+    ws = abi.workspace(abi.fourtune_mlp_workspace_bytes(m, fc1, fc2))
+
+    def step():
+        y, saved = abi.mlp_forward(fc1, fc2, x, y_dtype=torch.float32, ws=ws, hq_out=hq)
+        g = abi.mlp_backward(fc1, fc2, dy, x, saved, dx_dtype=torch.float32, ws=ws, dpq_out=dpq)
+        return dict(Y=y, XL1=saved["xl1"], P=saved["pre"], HL2=saved["hl2"], **g)
+
+    def fetch(o):
+        torch.cuda.synchronize()
+        got = {k: host(v) for k, v in o.items()}
+        got["hq"] = (host_u8(hq.codes), host_u8(hq.scales))
+        got["dpq"] = (host_u8(dpq.codes), host_u8(dpq.scales))
+        return got
+
+    def same(a, b, what):
+        for k in ("Y", "XL1", "P", "HL2", "dX", "dA1", "dB1", "dA2", "dB2"):
+            assert np.array_equal(a[k], b[k]), (what, k)
+        for k in ("hq", "dpq"):
+            assert np.array_equal(a[k][0], b[k][0]) and np.array_equal(a[k][1], b[k][1]), (what, k)
+
+    ws.fill_(0xFF)
+    ref = fetch(step())
+    fwd, bwd = _oracle(case)
+    _check_all(case, ref, fwd, bwd)
+    same(ref, fetch(step()), "second call, same workspace")
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda"))
+    same(ref, fetch(step()), "random workspace bytes")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    for rep in range(3):
+        graph.replay()
+        same(ref, fetch(outs), f"graph replay {rep}")
+        same(ref, fetch(step()), f"eager call after replay {rep}")
+
+
 def _on_grid(rng, rows, cols, e_lo, e_hi):
     """A tensor each of whose 32x32 blocks holds E2M1 grid values times one power of
     two 2^e (e uniform in [e_lo, e_hi]) with a +-6 element, so that quantizing it is
