@@ -45,8 +45,8 @@ GEMM_SRC = os.path.join(ROOT, "bit_quantized_lora_fp4_amd", "csrc", "gemm.hip")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2")
     ap.add_argument("--sets", type=int, default=20,
                     help="rotated input/weight sets (20 at c2: the per-kernel timings stream more "
