@@ -7,7 +7,12 @@
   linear with the merged weight R + L2 L1 + B A (FourTune §3.1);
 - finite differences: the backward (dX, dA, dB; and through GELU for the MLP) is the
   derivative of <Y, G> (FourTune §3.2);
-- GELU identities.
+- GELU identities;
+- hand-computed cases with quantization and bf16 rounding on: the MLP pair on on-grid
+  operands whose FC1 output lands on an E2M1 tie (the fp32 decision precision of Q(H)
+  and Q(dP), the rounding of P^, GELU' in dP), and an fp32-input linear whose bf16
+  roundings (X^, G^, XL, GB) survive cancellation, so each rounding point changes an
+  output value.
 """
 from fractions import Fraction
 
@@ -214,6 +219,106 @@ def test_mlp_epilogue_decision_in_fp32():
     assert H[5, 7] < 7.0 and layer.fp32(H)[5, 7] == 7.0
     assert mx4.fake_quant(layer.fp32(H))[5, 7] == 8.0
     assert mx4.fake_quant(H)[5, 7] == 6.0
-    # the MLP's 4-bit operand is taken from the fp32 values
-    fwd_h32 = layer.fp32(H)
-    assert np.array_equal(mx4.fake_quant(fwd_h32), mx4.fake_quant(layer.fp32(layer.gelu_tanh(P))))
+
+
+# ---------------------------------------------------------------- quantized MLP, by hand
+# On-grid operands, no low-rank branches: every product below is exact, so the expected
+# outputs are written down by hand (FourTune §3.3 "MLP Fusion": FC2's 4-bit operand is
+# the quantized GELU of FC1's output; §3.2: FC1's backward takes the quantized gradient
+# dP = dH * GELU'(P^)). Shapes: M = 32, d = 64, f = 32.
+#   R1 [f x d]: R1[j, j] = R1[j, (j+16) % 32] = R1[j, 32+j] = 1, so
+#               P[i, j] = X[i, j] + X[i, (j+16) % 32] + X[i, 32+j];
+#   R2 [d x f] = [I; I], so Y[i, c] = Hq[i, c % 32] and dH[i, j] = G[i, j] + G[i, 32+j].
+# Every block of X, R1, R2 and G holds its amax exactly on a power-of-two multiple of 4
+# or 6 or is otherwise representable, so Q() leaves them unchanged.
+def _mlp_hand_case():
+    M, d, f = 32, 64, 32
+    R1 = np.zeros((f, d))
+    for j in range(f):
+        R1[j, j] = R1[j, (j + 16) % 32] = R1[j, 32 + j] = 1.0
+    R2 = np.vstack([np.eye(f), np.eye(f)])
+    X = np.zeros((M, d))
+    X[0, 0] = X[0, 16] = 6.0                         # P[0, 0] = P[0, 16] = 12
+    X[5, 7], X[5, 23] = 4.0, 3.0                     # P[5, 7] = P[5, 23] = 7: a tie after GELU
+    X[9, 3], X[9, 19], X[9, 35] = 4.0, 3.0, -2.0 ** -8   # P[9, 3] = 7 - 2^-8, P^ = bf16 -> 7
+    G = np.zeros((M, d))
+    G[0, 0] = G[0, 32] = 3.0                         # dH[0, 0] = 6, GELU'(12) = 1
+    G[5, 7], G[5, 39] = 1.0, 0.25                    # dH[5, 7] = 1.25, GELU'(7) = 1 + 3e-14
+    G[9, 10] = 3.0                                   # dH[9, 10] = 3, GELU'(0) = 1/2
+    empty = dict(A=np.zeros((0, d)), B=np.zeros((f, 0)), L1=np.zeros((0, d)), L2=np.zeros((f, 0)))
+    fc1 = Linear(R=R1, **empty)
+    fc2 = Linear(R=R2, A=np.zeros((0, f)), B=np.zeros((d, 0)), L1=np.zeros((0, f)), L2=np.zeros((d, 0)))
+    return X, G, fc1, fc2
+
+
+def test_mlp_quantized_forward_by_hand():
+    """P^ = bf16(FC1 out) holds 12 (block max: scale 2) and 7 = 3.5 * 2, a tie that the
+    fp32 value of GELU(7) sits on (rounds to the even code: 4 * 2 = 8) and fp64's
+    GELU(7) = 7 - 3e-15 misses (3 * 2 = 6); P[9, 3] = 7 - 2^-8 rounds to P^ = 7 first.
+    A wrong decision precision, a skipped rounding of P or a missing Q(H) each change Y."""
+    X, G, fc1, fc2 = _mlp_hand_case()
+    assert np.array_equal(mx4.fake_quant(X), X) and np.array_equal(mx4.fake_quant(fc1.R), fc1.R)
+    out = layer.mlp_forward(X, fc1, fc2)
+    P = np.zeros((32, 32))
+    P[0, 0] = P[0, 16] = 12.0
+    P[5, 7] = P[5, 23] = P[9, 3] = P[9, 19] = 7.0
+    assert np.array_equal(out["P"], P)
+    Hq = np.zeros((32, 32))
+    Hq[0, 0] = Hq[0, 16] = 12.0
+    Hq[5, 7] = Hq[5, 23] = Hq[9, 3] = Hq[9, 19] = 8.0
+    assert np.array_equal(out["Y"], np.hstack([Hq, Hq]))
+
+
+def test_mlp_quantized_backward_by_hand():
+    """dP = dH * GELU'(P^): dP[5, 7] = 1.25 (1 + 3e-14) in fp64, exactly 1.25 in fp32, the
+    1 | 1.5 tie in a block of maximum 6 (scale 1): the fp32 decision rounds to the even
+    code (1); dP[9, 10] = 3 * GELU'(0) = 1.5. dX = Q(dP) Q(R1) spreads each code to its
+    three input columns."""
+    X, G, fc1, fc2 = _mlp_hand_case()
+    saved = layer.mlp_forward(X, fc1, fc2)
+    g = layer.mlp_backward(G, X, saved, fc1, fc2)
+    dPq = np.zeros((32, 32))
+    dPq[0, 0], dPq[5, 7], dPq[9, 10] = 6.0, 1.0, 1.5
+    dX = np.zeros((32, 64))
+    for i, j in ((0, 0), (5, 7), (9, 10)):
+        dX[i, j] = dX[i, (j + 16) % 32] = dX[i, 32 + j] = dPq[i, j]
+    assert np.array_equal(g["dX"], dX)
+    assert g["dP32"][5, 7] == 1.25 and g["dP"][5, 7] > 1.25
+
+
+# ---------------------------------------------------------------- bf16 rounding points
+def test_bf16_rounding_points_by_hand():
+    """fp32 input and gradient whose bf16 roundings survive cancellation (the c1 input is
+    fp32): X^ = bf16(X) before the down-projection and in dA, G^ = bf16(G) in GB and dB,
+    and the single roundings of XL and GB. x = 1 + 3 * 2^-9 rounds to 1 + 2^-7 and
+    1 + 2^-8 (a tie) rounds to 1. Rank 1, no stabilizer, R = 0."""
+    K = N = 32
+    X = np.zeros((2, K))
+    X[0, 0], X[0, 1] = 1.0 + 3 * 2.0 ** -9, -1.0     # X^ A^T = 2^-7 (exact: 3 * 2^-9)
+    X[1, 0], X[1, 1] = 1.0, 2.0 ** -8                # X^ A^T = 1 + 2^-8 -> bf16 1
+    G = np.zeros((2, N))
+    G[0, 0], G[0, 1] = 1.0 + 3 * 2.0 ** -9, -1.0     # G^ B = 2^-7
+    G[1, 0], G[1, 1] = 1.0, 2.0 ** -8                # G^ B = 1 + 2^-8 -> bf16 1
+    A = np.zeros((1, K))
+    A[0, 0] = A[0, 1] = 1.0
+    B = np.zeros((N, 1))
+    B[0, 0] = B[1, 0] = 1.0
+    lin = Linear(R=np.zeros((N, K)), A=A, B=B, L1=np.zeros((0, K)), L2=np.zeros((N, 0)))
+    Y, XL = layer.linear_forward(X, lin)
+    e7, e8, e14 = 2.0 ** -7, 2.0 ** -8, 2.0 ** -14
+    assert np.array_equal(XL, np.array([[e7], [1.0]]))
+    Yw = np.zeros((2, N))
+    Yw[0, :2], Yw[1, :2] = e7, 1.0
+    assert np.array_equal(Y, Yw)
+    dX, dA, dB, GB = layer.linear_backward(G, X, XL, lin)
+    assert np.array_equal(GB, np.array([[e7], [1.0]]))
+    dXw = np.zeros((2, K))
+    dXw[0, :2], dXw[1, :2] = e7, 1.0
+    assert np.array_equal(dX, dXw)
+    dAw = np.zeros((1, K))
+    dAw[0, 0], dAw[0, 1] = e7 * (1 + e7) + 1.0, -e7 + e8   # GB^T X^
+    assert np.array_equal(dA, dAw)
+    dBw = np.zeros((N, 1))
+    dBw[0, 0], dBw[1, 0] = (1 + e7) * e7 + 1.0, -e7 + e8   # G^^T XL
+    assert np.array_equal(dB, dBw)
+    assert dA[0, 0] == 1.0 + e7 + e14
