@@ -68,11 +68,11 @@ _SIGS = {
                                             ctypes.POINTER(FtLinear)]),
     "fourtune_mlp_fwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear), c_vp,
                                         ctypes.c_int, c_i64, c_vp, ctypes.c_int, c_vp, c_vp, c_vp,
-                                        ctypes.POINTER(FtMx4), c_vp, c_sz, c_vp]),
+                                        ctypes.POINTER(FtMx4), c_vp, c_vp, c_sz, c_vp]),
     "fourtune_mlp_bwd": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear), c_vp,
                                         ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_i64,
                                         c_vp, ctypes.c_int, c_vp, c_vp, c_vp, c_vp,
-                                        ctypes.POINTER(FtMx4), c_vp, c_sz, c_vp]),
+                                        ctypes.POINTER(FtMx4), c_vp, c_vp, c_sz, c_vp]),
     "fourtune_ablation_workspace_bytes": (c_sz, [c_i64, ctypes.POINTER(FtLinear),
                                                  ctypes.POINTER(FtLinear)]),
     "fourtune_linear_fwd_unfused": (ctypes.c_int, [ctypes.POINTER(FtLinear), c_vp, ctypes.c_int,
@@ -139,6 +139,116 @@ def _dt(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return FT_BF16
     raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------- argument checks
+# The C side sees raw pointers and sizes only, so the shape, dtype and layout of every
+# tensor argument are checked here, before any pointer is taken.
+_F32_BF16 = (torch.float32, torch.bfloat16)
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+_U8 = (torch.uint8,)
+
+
+def _need(t, name: str, shape, dtypes, optional: bool = False):
+    """t must be a contiguous tensor of `shape` and one of `dtypes` (or None when
+    `optional`)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(v) for v in shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {list(dtypes)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_mx4(q, name: str, rows: int, cols: int, optional: bool = False, groups: bool = False):
+    if q is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(q, Mx4):
+        raise TypeError(f"{name} must be an Mx4")
+    if (q.rows, q.cols) != (rows, cols):
+        raise ValueError(f"{name} is [{q.rows} x {q.cols}], expected [{rows} x {cols}]")
+    _need(q.codes, f"{name}.codes", (rows, cols // 2), _U8)
+    _need(q.scales, f"{name}.scales", (rows if groups else (rows + 31) // 32, cols // 32), _U8)
+
+
+def _need_linear(L, name: str = "L"):
+    if not isinstance(L, Linear):
+        raise TypeError(f"{name} must be a Linear")
+    n, k = L.rq.rows, L.rq.cols
+    _need_mx4(L.rq, f"{name}.rq", n, k)
+    for t, nm in ((L.A, "A"), (L.B, "B"), (L.L1, "L1"), (L.L2, "L2")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 2:
+            raise ValueError(f"{name}.{nm} must be a 2-D tensor")
+    r, s = L.A.shape[0], L.L1.shape[0]
+    _need(L.A, f"{name}.A", (r, k), _BF16)
+    _need(L.B, f"{name}.B", (n, r), _BF16)
+    _need(L.L1, f"{name}.L1", (s, k), _BF16)
+    _need(L.L2, f"{name}.L2", (n, s), _BF16)
+
+
+def _rt(L) -> int:
+    return L.A.shape[0] + L.L1.shape[0]
+
+
+def _need_low(t, name: str, m: int, rt: int):
+    """A saved [m x rt] bf16 low-rank activation (may be omitted when rt is 0)."""
+    _need(t, name, (m, rt), _BF16, optional=rt == 0)
+
+
+def _need_ws(ws):
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous 1-D uint8 tensor")
+
+
+def _need_linear_fwd(L, x, y, xl_saved, ws):
+    _need_linear(L)
+    m = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+    _need(x, "x", (m, L.k), _F32_BF16)
+    _need(y, "y", (m, L.n), _F32_BF16)
+    _need_low(xl_saved, "xl_saved", m, _rt(L))
+    _need_ws(ws)
+
+
+def _need_linear_bwd(L, dy, x, xl_saved, dx, d_lora_a, d_lora_b, ws):
+    _need_linear(L)
+    m = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+    _need(x, "x", (m, L.k), _F32_BF16)
+    _need(dy, "dy", (m, L.n), _F32_BF16)
+    _need_low(xl_saved, "xl_saved", m, _rt(L))
+    _need(dx, "dx", (m, L.k), _F32_BF16)
+    _need(d_lora_a, "d_lora_a", (L.rank, L.k), _F32, optional=L.rank == 0)
+    _need(d_lora_b, "d_lora_b", (L.n, L.rank), _F32, optional=L.rank == 0)
+    _need_ws(ws)
+
+
+def _need_mlp(fc1, fc2):
+    _need_linear(fc1, "fc1")
+    _need_linear(fc2, "fc2")
+    if fc1.n != fc2.k:
+        raise ValueError(f"fc1 has {fc1.n} outputs, fc2 {fc2.k} inputs")
+
+
+def _need_mlp_bwd(fc1, fc2, m, dy, x, xl1_saved, pre_saved, hl2_saved, dx, d_a1, d_b1, d_a2, d_b2):
+    _need(x, "x", (m, fc1.k), _F32_BF16)
+    _need(dy, "dy", (m, fc2.n), _F32_BF16)
+    _need_low(xl1_saved, "xl1_saved", m, _rt(fc1))
+    _need(pre_saved, "pre_saved", (m, fc1.n), _BF16)
+    _need_low(hl2_saved, "hl2_saved", m, _rt(fc2))
+    _need(dx, "dx", (m, fc1.k), _F32_BF16)
+    _need(d_a1, "d_a1", (fc1.rank, fc1.k), _F32, optional=fc1.rank == 0)
+    _need(d_b1, "d_b1", (fc1.n, fc1.rank), _F32, optional=fc1.rank == 0)
+    _need(d_a2, "d_a2", (fc2.rank, fc2.k), _F32, optional=fc2.rank == 0)
+    _need(d_b2, "d_b2", (fc2.n, fc2.rank), _F32, optional=fc2.rank == 0)
 
 
 def _stream(stream):
@@ -211,11 +321,20 @@ def ft_mx4_scales_bytes(rows: int, cols: int) -> int:
     return lib().ft_mx4_scales_bytes(rows, cols)
 
 
+def _need_rows(x, name="x"):
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor")
+    if x.dtype not in _F32_BF16:
+        raise ValueError(f"{name} has dtype {x.dtype}, expected one of {list(_F32_BF16)}")
+    if x.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+
+
 def fourtune_quantize(x: torch.Tensor, out: Mx4, stream=None, ld: Optional[int] = None):
+    _need_rows(x)
     rows, cols = x.shape
     ld = x.stride(0) if ld is None else ld
-    if x.stride(1) != 1:
-        raise ValueError("x must have unit column stride")
+    _need_mx4(out, "out", rows, cols)
     s = out.struct()
     _check(lib().fourtune_quantize(_ptr(x), _dt(x), rows, cols, ld, ctypes.byref(s),
                                    _stream(stream)))
@@ -223,10 +342,10 @@ def fourtune_quantize(x: torch.Tensor, out: Mx4, stream=None, ld: Optional[int] 
 
 def fourtune_quantize_groups(x: torch.Tensor, out: Mx4, stream=None, ld: Optional[int] = None):
     """1x32 groups: out.scales must be [rows x cols/32] (see Mx4.empty_groups)."""
+    _need_rows(x)
     rows, cols = x.shape
     ld = x.stride(0) if ld is None else ld
-    if x.stride(1) != 1:
-        raise ValueError("x must have unit column stride")
+    _need_mx4(out, "out", rows, cols, groups=True)
     s = out.struct()
     _check(lib().fourtune_quantize_groups(_ptr(x), _dt(x), rows, cols, ld, ctypes.byref(s),
                                           _stream(stream)))
@@ -239,6 +358,13 @@ def fourtune_linear_workspace_bytes(m: int, L: Linear) -> int:
 
 def fourtune_linear_fwd(L: Linear, x: torch.Tensor, y: torch.Tensor, xl_saved: torch.Tensor,
                         ws: torch.Tensor, xq_out: Optional[Mx4] = None, stream=None):
+    _need_linear(L)
+    m = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+    _need(x, "x", (m, L.k), _F32_BF16)
+    _need(y, "y", (m, L.n), _F32_BF16)
+    _need_low(xl_saved, "xl_saved", m, _rt(L))
+    _need_mx4(xq_out, "xq_out", m, L.k, optional=True)
+    _need_ws(ws)
     s = L.struct()
     xq = xq_out.struct() if xq_out is not None else None
     _check(lib().fourtune_linear_fwd(ctypes.byref(s), _ptr(x), _dt(x), x.shape[0], _ptr(y),
@@ -252,6 +378,16 @@ def fourtune_linear_bwd(L: Linear, dy: torch.Tensor, x: torch.Tensor, xl_saved: 
                         dx: torch.Tensor, d_lora_a: Optional[torch.Tensor],
                         d_lora_b: Optional[torch.Tensor], ws: torch.Tensor,
                         gq_out: Optional[Mx4] = None, stream=None):
+    _need_linear(L)
+    m = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+    _need(x, "x", (m, L.k), _F32_BF16)
+    _need(dy, "dy", (m, L.n), _F32_BF16)
+    _need_low(xl_saved, "xl_saved", m, _rt(L))
+    _need(dx, "dx", (m, L.k), _F32_BF16)
+    _need(d_lora_a, "d_lora_a", (L.rank, L.k), _F32, optional=L.rank == 0)
+    _need(d_lora_b, "d_lora_b", (L.n, L.rank), _F32, optional=L.rank == 0)
+    _need_mx4(gq_out, "gq_out", m, L.n, optional=True)
+    _need_ws(ws)
     s = L.struct()
     gq = gq_out.struct() if gq_out is not None else None
     _check(lib().fourtune_linear_bwd(ctypes.byref(s), _ptr(dy), _dt(dy), _ptr(x), _dt(x),
@@ -264,6 +400,12 @@ def fourtune_linear_bwd(L: Linear, dy: torch.Tensor, x: torch.Tensor, xl_saved: 
 
 def fourtune_gemm_fwd(L: Linear, xq: Mx4, xl: Optional[torch.Tensor], y: torch.Tensor,
                       stream=None):
+    _need_linear(L)
+    if not isinstance(xq, Mx4):
+        raise TypeError("xq must be an Mx4")
+    _need_mx4(xq, "xq", xq.rows, L.k)
+    _need_low(xl, "xl", xq.rows, _rt(L))
+    _need(y, "y", (xq.rows, L.n), _F32_BF16)
     s, q = L.struct(), xq.struct()
     _check(lib().fourtune_gemm_fwd(ctypes.byref(s), ctypes.byref(q), _ptr(xl), xq.rows, _ptr(y),
                                    _dt(y), _stream(stream)))
@@ -271,6 +413,12 @@ def fourtune_gemm_fwd(L: Linear, xq: Mx4, xl: Optional[torch.Tensor], y: torch.T
 
 def fourtune_gemm_bwd(L: Linear, gq: Mx4, gb: Optional[torch.Tensor], dx: torch.Tensor,
                       stream=None):
+    _need_linear(L)
+    if not isinstance(gq, Mx4):
+        raise TypeError("gq must be an Mx4")
+    _need_mx4(gq, "gq", gq.rows, L.n)
+    _need_low(gb, "gb", gq.rows, _rt(L))
+    _need(dx, "dx", (gq.rows, L.k), _F32_BF16)
     s, q = L.struct(), gq.struct()
     _check(lib().fourtune_gemm_bwd(ctypes.byref(s), ctypes.byref(q), _ptr(gb), gq.rows, _ptr(dx),
                                    _dt(dx), _stream(stream)))
@@ -283,26 +431,46 @@ def fourtune_mlp_workspace_bytes(m: int, fc1: Linear, fc2: Linear) -> int:
 
 def fourtune_mlp_fwd(fc1: Linear, fc2: Linear, x: torch.Tensor, y: torch.Tensor,
                      xl1_saved: torch.Tensor, pre_saved: torch.Tensor, hl2_saved: torch.Tensor,
-                     ws: torch.Tensor, hq_out: Optional[Mx4] = None, stream=None):
+                     ws: torch.Tensor, hq_out: Optional[Mx4] = None,
+                     h_debug: Optional[torch.Tensor] = None, stream=None):
+    _need_mlp(fc1, fc2)
+    m = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+    _need(x, "x", (m, fc1.k), _F32_BF16)
+    _need(y, "y", (m, fc2.n), _F32_BF16)
+    _need_low(xl1_saved, "xl1_saved", m, _rt(fc1))
+    _need(pre_saved, "pre_saved", (m, fc1.n), _BF16)
+    _need_low(hl2_saved, "hl2_saved", m, _rt(fc2))
+    _need_mx4(hq_out, "hq_out", m, fc1.n, optional=True)
+    _need(h_debug, "h_debug", (m, fc1.n), _F32, optional=True)
+    _need_ws(ws)
     s1, s2 = fc1.struct(), fc2.struct()
     hq = hq_out.struct() if hq_out is not None else None
     _check(lib().fourtune_mlp_fwd(ctypes.byref(s1), ctypes.byref(s2), _ptr(x), _dt(x),
                                   x.shape[0], _ptr(y), _dt(y), _ptr(xl1_saved), _ptr(pre_saved),
                                   _ptr(hl2_saved), ctypes.byref(hq) if hq is not None else None,
-                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+                                  _ptr(h_debug), _ptr(ws), ws.numel() if ws is not None else 0,
+                                  _stream(stream)))
 
 
 def fourtune_mlp_bwd(fc1: Linear, fc2: Linear, dy: torch.Tensor, x: torch.Tensor,
                      xl1_saved: torch.Tensor, pre_saved: torch.Tensor, hl2_saved: torch.Tensor,
                      dx: torch.Tensor, d_a1, d_b1, d_a2, d_b2, ws: torch.Tensor,
-                     dpq_out: Optional[Mx4] = None, stream=None):
+                     dpq_out: Optional[Mx4] = None, dp_debug: Optional[torch.Tensor] = None,
+                     stream=None):
+    _need_mlp(fc1, fc2)
+    m = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+    _need_mlp_bwd(fc1, fc2, m, dy, x, xl1_saved, pre_saved, hl2_saved, dx, d_a1, d_b1, d_a2, d_b2)
+    _need_mx4(dpq_out, "dpq_out", m, fc1.n, optional=True)
+    _need(dp_debug, "dp_debug", (m, fc1.n), _F32, optional=True)
+    _need_ws(ws)
     s1, s2 = fc1.struct(), fc2.struct()
     dq = dpq_out.struct() if dpq_out is not None else None
     _check(lib().fourtune_mlp_bwd(ctypes.byref(s1), ctypes.byref(s2), _ptr(dy), _dt(dy), _ptr(x),
                                   _dt(x), _ptr(xl1_saved), _ptr(pre_saved), _ptr(hl2_saved),
                                   x.shape[0], _ptr(dx), _dt(dx), _ptr(d_a1), _ptr(d_b1),
                                   _ptr(d_a2), _ptr(d_b2), ctypes.byref(dq) if dq is not None else None,
-                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream)))
+                                  _ptr(dp_debug), _ptr(ws), ws.numel() if ws is not None else 0,
+                                  _stream(stream)))
 
 
 def fourtune_ablation_workspace_bytes(m: int, fc1: Linear, fc2: Optional[Linear] = None) -> int:
@@ -314,6 +482,7 @@ def fourtune_ablation_workspace_bytes(m: int, fc1: Linear, fc2: Optional[Linear]
 
 def fourtune_linear_fwd_unfused(L: Linear, x: torch.Tensor, y: torch.Tensor,
                                 xl_saved: torch.Tensor, ws: torch.Tensor, stream=None):
+    _need_linear_fwd(L, x, y, xl_saved, ws)
     s = L.struct()
     _check(lib().fourtune_linear_fwd_unfused(ctypes.byref(s), _ptr(x), _dt(x), x.shape[0], _ptr(y),
                                              _dt(y), _ptr(xl_saved), _ptr(ws), ws.numel(),
@@ -324,6 +493,7 @@ def fourtune_linear_bwd_unfused(L: Linear, dy: torch.Tensor, x: torch.Tensor,
                                 xl_saved: torch.Tensor, dx: torch.Tensor,
                                 d_lora_a: Optional[torch.Tensor], d_lora_b: Optional[torch.Tensor],
                                 ws: torch.Tensor, stream=None):
+    _need_linear_bwd(L, dy, x, xl_saved, dx, d_lora_a, d_lora_b, ws)
     s = L.struct()
     _check(lib().fourtune_linear_bwd_unfused(ctypes.byref(s), _ptr(dy), _dt(dy), _ptr(x), _dt(x),
                                              _ptr(xl_saved), x.shape[0], _ptr(dx), _dt(dx),
@@ -335,6 +505,15 @@ def fourtune_mlp_fwd_unfused(fc1: Linear, fc2: Linear, lora_fused: bool, x: torc
                              y: torch.Tensor, xl1_saved: torch.Tensor, pre_saved: torch.Tensor,
                              h_saved: torch.Tensor, hl2_saved: torch.Tensor, ws: torch.Tensor,
                              stream=None):
+    _need_mlp(fc1, fc2)
+    m = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+    _need(x, "x", (m, fc1.k), _F32_BF16)
+    _need(y, "y", (m, fc2.n), _F32_BF16)
+    _need_low(xl1_saved, "xl1_saved", m, _rt(fc1))
+    _need(pre_saved, "pre_saved", (m, fc1.n), _BF16)
+    _need(h_saved, "h_saved", (m, fc1.n), _BF16)
+    _need_low(hl2_saved, "hl2_saved", m, _rt(fc2))
+    _need_ws(ws)
     s1, s2 = fc1.struct(), fc2.struct()
     _check(lib().fourtune_mlp_fwd_unfused(ctypes.byref(s1), ctypes.byref(s2), int(bool(lora_fused)),
                                           _ptr(x), _dt(x), x.shape[0], _ptr(y), _dt(y),
@@ -346,6 +525,11 @@ def fourtune_mlp_bwd_unfused(fc1: Linear, fc2: Linear, lora_fused: bool, dy: tor
                              x: torch.Tensor, xl1_saved: torch.Tensor, pre_saved: torch.Tensor,
                              h_saved: torch.Tensor, hl2_saved: torch.Tensor, dx: torch.Tensor,
                              d_a1, d_b1, d_a2, d_b2, ws: torch.Tensor, stream=None):
+    _need_mlp(fc1, fc2)
+    m = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+    _need_mlp_bwd(fc1, fc2, m, dy, x, xl1_saved, pre_saved, hl2_saved, dx, d_a1, d_b1, d_a2, d_b2)
+    _need(h_saved, "h_saved", (m, fc1.n), _BF16)
+    _need_ws(ws)
     s1, s2 = fc1.struct(), fc2.struct()
     _check(lib().fourtune_mlp_bwd_unfused(ctypes.byref(s1), ctypes.byref(s2), int(bool(lora_fused)),
                                           _ptr(dy), _dt(dy), _ptr(x), _dt(x), _ptr(xl1_saved),
@@ -360,6 +544,7 @@ PREC = {"W4A4G4": 0, "W4A16G4": 1, "W4A4G16": 2, "W4A16G16": 3}
 
 def fourtune_linear_fwd_prec(L: Linear, prec: str, x: torch.Tensor, y: torch.Tensor,
                              xl_saved: torch.Tensor, ws: torch.Tensor, stream=None):
+    _need_linear_fwd(L, x, y, xl_saved, ws)
     s = L.struct()
     _check(lib().fourtune_linear_fwd_prec(ctypes.byref(s), PREC[prec], _ptr(x), _dt(x), x.shape[0],
                                           _ptr(y), _dt(y), _ptr(xl_saved), _ptr(ws), ws.numel(),
@@ -370,6 +555,7 @@ def fourtune_linear_bwd_prec(L: Linear, prec: str, dy: torch.Tensor, x: torch.Te
                              xl_saved: torch.Tensor, dx: torch.Tensor,
                              d_lora_a: Optional[torch.Tensor], d_lora_b: Optional[torch.Tensor],
                              ws: torch.Tensor, stream=None):
+    _need_linear_bwd(L, dy, x, xl_saved, dx, d_lora_a, d_lora_b, ws)
     s = L.struct()
     _check(lib().fourtune_linear_bwd_prec(ctypes.byref(s), PREC[prec], _ptr(dy), _dt(dy), _ptr(x),
                                           _dt(x), _ptr(xl_saved), x.shape[0], _ptr(dx), _dt(dx),
@@ -424,7 +610,7 @@ def linear_backward(L: Linear, dy: torch.Tensor, x: torch.Tensor, xl: torch.Tens
 
 
 def mlp_forward(fc1: Linear, fc2: Linear, x: torch.Tensor, y_dtype=torch.bfloat16, ws=None,
-                hq_out=None, stream=None):
+                hq_out=None, h_debug=None, stream=None):
     """Allocating helper: returns (y, saved) with saved = dict(xl1, pre, hl2)."""
     m, dev = x.shape[0], x.device
     y = torch.empty((m, fc2.n), dtype=y_dtype, device=dev)
@@ -433,12 +619,12 @@ def mlp_forward(fc1: Linear, fc2: Linear, x: torch.Tensor, y_dtype=torch.bfloat1
                  hl2=torch.empty((m, fc2.rank + fc2.stab_rank), dtype=torch.bfloat16, device=dev))
     ws = workspace(fourtune_mlp_workspace_bytes(m, fc1, fc2), dev) if ws is None else ws
     fourtune_mlp_fwd(fc1, fc2, x, y, saved["xl1"], saved["pre"], saved["hl2"], ws, hq_out=hq_out,
-                     stream=stream)
+                     h_debug=h_debug, stream=stream)
     return y, saved
 
 
 def mlp_backward(fc1: Linear, fc2: Linear, dy: torch.Tensor, x: torch.Tensor, saved: dict,
-                 dx_dtype=torch.bfloat16, ws=None, dpq_out=None, stream=None):
+                 dx_dtype=torch.bfloat16, ws=None, dpq_out=None, dp_debug=None, stream=None):
     """Allocating helper: returns dict(dX, dA1, dB1, dA2, dB2)."""
     m, dev = x.shape[0], x.device
     dx = torch.empty((m, fc1.k), dtype=dx_dtype, device=dev)
@@ -448,6 +634,6 @@ def mlp_backward(fc1: Linear, fc2: Linear, dy: torch.Tensor, x: torch.Tensor, sa
              dB2=torch.empty((fc2.n, fc2.rank), dtype=torch.float32, device=dev))
     ws = workspace(fourtune_mlp_workspace_bytes(m, fc1, fc2), dev) if ws is None else ws
     fourtune_mlp_bwd(fc1, fc2, dy, x, saved["xl1"], saved["pre"], saved["hl2"], dx, g["dA1"], g["dB1"],
-                     g["dA2"], g["dB2"], ws, dpq_out=dpq_out, stream=stream)
+                     g["dA2"], g["dB2"], ws, dpq_out=dpq_out, dp_debug=dp_debug, stream=stream)
     g["dX"] = dx
     return g

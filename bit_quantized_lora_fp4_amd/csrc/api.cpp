@@ -157,7 +157,10 @@ ft_status check_linear(const ft_linear* L, const char* who) {
           FT_ERR_SHAPE, "%s: rank=%lld, stab_rank=%lld must be multiples of 16", who,
           (long long)L->rank, (long long)L->stab_rank);
   const int64_t rt = L->rank + L->stab_rank;
-  REQUIRE(rt % 32 == 0, FT_ERR_SHAPE, "%s: rank + stab_rank = %lld must be a multiple of 32", who, (long long)rt);
+  // The fused quantize + down-projection kernels work the low-rank width in pairs of
+  // 16-wide tiles; a width of 16 (mod 32) is a valid layer this build does not handle.
+  REQUIRE(rt % 32 == 0, FT_ERR_UNSUPPORTED, "%s: rank + stab_rank = %lld is not a multiple of 32", who,
+          (long long)rt);
   REQUIRE(rt <= 128, FT_ERR_UNSUPPORTED, "%s: rank + stab_rank = %lld > 128", who, (long long)rt);
   REQUIRE(ft::quant_down_tiles((int)L->rank, (int)rt) <= ft::QD_MAX_TILES, FT_ERR_UNSUPPORTED,
           "%s: ceil(rank/32) + ceil(stab_rank/32) > %d", who, ft::QD_MAX_TILES);
@@ -237,12 +240,13 @@ ft_status check_m(int64_t m, const ft_linear* L, const char* who) {
   return FT_OK;
 }
 
-// Epilogue options of the 4-bit GEMMs (the MLP's FC1 forward and FC2 backward).
+// Epilogue options of the 4-bit GEMMs (the MLP's FC2 backward).
 struct Epi {
   int kind = ft::GEMM_EPI_NONE;
   const void* pre = nullptr;
   uint8_t* q_codes = nullptr;
   uint8_t* q_scales = nullptr;
+  float* dbg = nullptr;
 };
 
 ft_status run_gemm_fwd(const ft_linear* L, const uint8_t* xq_codes, const uint8_t* xq_scales,
@@ -274,6 +278,7 @@ ft_status run_gemm_bwd(const ft_linear* L, const uint8_t* gq_codes, const uint8_
   g.up_split = (int)L->rank;
   g.out = dx; g.ldo = L->k;
   g.epi = e.kind; g.pre = static_cast<const ft::bf16_t*>(e.pre); g.q_codes = e.q_codes; g.q_scales = e.q_scales;
+  g.dbg = e.dbg;
   return hip_check(ft::launch_gemm_mx4(g, true, dx_dt == FT_BF16, st), "gemm_bwd");
 }
 
@@ -282,7 +287,7 @@ ft_status run_gemm_bwd(const ft_linear* L, const uint8_t* gq_codes, const uint8_
 // [B | L2] (output side).
 ft_status run_quant_down(int mode, const ft_linear* L, bool down, const void* x, bool x_bf16, int64_t m,
                          int64_t cols, uint8_t* codes, uint8_t* scales, void* low, float* partials,
-                         hipStream_t st, const char* what) {
+                         hipStream_t st, const char* what, float* hdbg = nullptr) {
   ft::QuantDownArgs qd{};
   qd.mode = mode;
   qd.x = x; qd.M = m; qd.K = cols; qd.ldx = cols;
@@ -292,6 +297,7 @@ ft_status run_quant_down(int mode, const ft_linear* L, bool down, const void* x,
   qd.r0 = (int)L->rank; qd.rt = (int)(L->rank + L->stab_rank); qd.u_cols = !down;
   qd.low = static_cast<ft::bf16_t*>(low);
   qd.partials = partials;
+  qd.hdbg = hdbg;
   return hip_check(ft::launch_quant_down(qd, x_bf16, st), what);
 }
 
@@ -528,7 +534,7 @@ size_t fourtune_mlp_workspace_bytes(int64_t m, const ft_linear* fc1, const ft_li
 
 ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const void* x, ft_dtype x_dt, int64_t m,
                            void* y, ft_dtype y_dt, void* xl1_saved, void* pre_saved, void* hl2_saved,
-                           ft_mx4* hq_out, void* ws, size_t ws_bytes, void* stream) {
+                           ft_mx4* hq_out, float* h_debug, void* ws, size_t ws_bytes, void* stream) {
   const char* who = "mlp_fwd";
   TRY(check_mlp(fc1, fc2, m, who));
   REQUIRE(dtype_ok(x_dt) && dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
@@ -539,6 +545,7 @@ ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const voi
   if (fc1->rank + fc1->stab_rank > 0) TRY(check_tensor(xl1_saved, who, "xl1_saved"));
   if (fc2->rank + fc2->stab_rank > 0) TRY(check_tensor(hl2_saved, who, "hl2_saved"));
   if (hq_out) TRY(check_mx4(hq_out, m, fc1->n, "mlp_fwd: hq_out"));
+  if (h_debug) REQUIRE(aligned16(h_debug), FT_ERR_ALIGN, "%s: h_debug not 16-byte aligned", who);
   const MlpFwdLayout lay = mlp_fwd_layout(ws, m, fc1, fc2, hq_out == nullptr);
   REQUIRE(ws != nullptr && ws_bytes >= lay.bytes, FT_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed",
           who, ws_bytes, lay.bytes);
@@ -552,7 +559,7 @@ ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const voi
                      lay.partials, st, "mlp_fwd quant_down(X)"));
   TRY(run_gemm_fwd(fc1, lay.xq_codes, lay.xq_scales, xl1_saved, m, pre_saved, FT_BF16, st));
   TRY(run_quant_down(ft::QD_GELU_QUANT, fc2, true, pre_saved, true, m, fdim, hq_codes, hq_scales, hl2_saved,
-                     lay.partials, st, "mlp_fwd gelu_quant_down(P)"));
+                     lay.partials, st, "mlp_fwd gelu_quant_down(P)", h_debug));
   TRY(run_gemm_fwd(fc2, hq_codes, hq_scales, hl2_saved, m, y, y_dt, st));
   return ok();
 }
@@ -560,7 +567,8 @@ ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const voi
 ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const void* dy, ft_dtype dy_dt,
                            const void* x, ft_dtype x_dt, const void* xl1_saved, const void* pre_saved,
                            const void* hl2_saved, int64_t m, void* dx, ft_dtype dx_dt, float* d_a1, float* d_b1,
-                           float* d_a2, float* d_b2, ft_mx4* dpq_out, void* ws, size_t ws_bytes, void* stream) {
+                           float* d_a2, float* d_b2, ft_mx4* dpq_out, float* dp_debug, void* ws, size_t ws_bytes,
+                           void* stream) {
   const char* who = "mlp_bwd";
   TRY(check_mlp(fc1, fc2, m, who));
   REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
@@ -580,6 +588,7 @@ ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const voi
     TRY(check_tensor(d_b2, who, "d_b2"));
   }
   if (dpq_out) TRY(check_mx4(dpq_out, m, fc1->n, "mlp_bwd: dpq_out"));
+  if (dp_debug) REQUIRE(aligned16(dp_debug), FT_ERR_ALIGN, "%s: dp_debug not 16-byte aligned", who);
   const MlpBwdLayout lay = mlp_bwd_layout(ws, m, fc1, fc2, dpq_out == nullptr);
   REQUIRE(ws != nullptr && ws_bytes >= lay.bytes, FT_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed",
           who, ws_bytes, lay.bytes);
@@ -593,6 +602,7 @@ ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const voi
                      lay.gb2, lay.partials, st, "mlp_bwd quant_down(dY)"));
   Epi e;
   e.kind = ft::GEMM_EPI_DGELU_Q; e.pre = pre_saved; e.q_codes = dpq_codes; e.q_scales = dpq_scales;
+  e.dbg = dp_debug;
   TRY(run_gemm_bwd(fc2, lay.gq_codes, lay.gq_scales, lay.gb2, m, lay.dp, FT_BF16, st, e));
   TRY(run_lora_grad(fc2, m, lay.gb2, pre_saved, true, true, hl2_saved, dy, dy_dt == FT_BF16, d_a2, d_b2,
                     lay.partials, st, "mlp_bwd lora_grad(fc2)"));

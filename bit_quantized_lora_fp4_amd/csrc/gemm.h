@@ -41,6 +41,7 @@ struct GemmArgs {
   const bf16_t* pre;
   uint8_t* q_codes;         // [M x N/2]
   uint8_t* q_scales;        // [ceil(M/32) x N/32]
+  float* dbg;               // optional: the fp32 dP that Q(dP) quantized, [M x N]
 };
 
 enum { GEMM_EPI_NONE = 0, GEMM_EPI_DGELU_Q = 2 };
@@ -59,7 +60,8 @@ constexpr int64_t GEMM_MAX_KRED = 16384;
 // needs quant_down_partial_bytes(M, K, r0, rt) bytes of fp32 partials, which a second
 // kernel sums in a fixed order.
 // mode: QD_QUANT (as above); QD_DOWN: no quantization; QD_GELU_QUANT: x = the saved
-// FC1 output P^ (bf16), H = GELU(P^) in fp32 -> Q(H), low = bf16(bf16(H) D^T).
+// FC1 output P^ (bf16), H = GELU(P^) in fp32 -> Q(H), low = bf16(bf16(H) D^T); when
+// hdbg is not NULL the fp32 H that Q(H) quantized is also stored there ([M x K]).
 enum { QD_QUANT = 0, QD_DOWN = 2, QD_GELU_QUANT = 3 };
 struct QuantDownArgs {
   int mode;
@@ -74,6 +76,7 @@ struct QuantDownArgs {
   bool u_cols;
   bf16_t* low;
   float* partials;
+  float* hdbg;  // QD_GELU_QUANT only, optional
 };
 
 hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t stream);

@@ -790,6 +790,8 @@ __global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g
     };
     load_pre(0, pw[0]);
     load_pre(1, pw[1]);
+    const bool dbg = g.dbg != nullptr;  // uniform
+    const bufres rdbg = make_buf(g.dbg, dbg ? (uint64_t)g.M * g.N * 4 : 0);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int64_t brow = m0 + wm * 128 + 32 * j;  // first row of this block row
@@ -805,6 +807,14 @@ __global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g
           const float p = (r & 1) ? bf16_hi(pwd) : bf16_lo(pwd);
           acc[i][j][r] = acc[i][j][r] * gelu_grad_f(p);  // dP = dH * GELU'(P^)
           v[r] = acc[i][j][r];
+        }
+        if (dbg) {  // optional export of the fp32 dP that Q(dP) quantizes
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int64_t col = col0 + 8 * gq + 4 * half;
+            buf_store16(rdbg, sel_off(row_ok && col < g.N, (uint32_t)((row * g.N + col) * 4)),
+                        __builtin_bit_cast(v4i, v4f{v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]}));
+          }
         }
         quant_tile_store(v, lane, row, row_ok, brow < g.M && col0 < g.N, brow >> 5, col0, rqc, rqs, g.N >> 1,
                          g.N >> 5);

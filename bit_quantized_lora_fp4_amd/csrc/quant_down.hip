@@ -246,6 +246,23 @@ __device__ __forceinline__ void reduce_waves(const v4f (&acc)[4][TP], float* red
   }
 }
 
+// The fp32 H = GELU(P^) of a chunk's two column blocks (hv[g][b]: row 16g + lr, columns
+// c0 + 32b + 8lq .. +8), stored to a.hdbg [M x K] for inspection. Chunks past the range
+// have c0 = K: every store is then out of range.
+__device__ __forceinline__ void store_h(const QuantDownArgs& a, const float (&hv)[4][2][8], int64_t r0, int64_t c0,
+                                        int lr, int lq) {
+  const bufres rh = make_buf(a.hdbg, (uint64_t)a.M * a.K * 4);
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t row = r0 + 16 * g + lr, col = c0 + 32 * b + 8 * lq;
+      const uint32_t off = sel_off(row < a.M && col < a.K, (uint32_t)((row * a.K + col) * 4));
+      buf_store16(rh, off, __builtin_bit_cast(v4i, v4f{hv[g][b][0], hv[g][b][1], hv[g][b][2], hv[g][b][3]}));
+      buf_store16(rh, off + 16, __builtin_bit_cast(v4i, v4f{hv[g][b][4], hv[g][b][5], hv[g][b][6], hv[g][b][7]}));
+    }
+}
+
 template <typename T, int TP, bool UCOLS, int MODE>
 __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   static_assert(TP % 2 == 0, "rank + stab_rank is a multiple of 32");
@@ -309,6 +326,7 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
             hv[g][b][2 * e + 1] = gelu_f(bf16_hi(w[e]));
           }
         }
+      if (a.hdbg != nullptr) store_h(a, hv, r0, c0, lr, lq);
       if constexpr (TP > 0) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
@@ -657,7 +675,7 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
   // column block b (32 columns) of chunk i (0, 1) of the pair. The second block's last
   // read of the stage is followed by the loads of chunk `pf` into it, which then land
   // while that block's arithmetic runs.
-  auto work_half = [&](int i, int b, int64_t pf) __attribute__((always_inline)) {
+  auto work_half = [&](int i, int b, int64_t cc, int64_t pf) __attribute__((always_inline)) {
     v4i xv[4];  // rows 16g + l%16, columns 32b + 8(l/16) .. +8
     {
       uint32_t ad[4];
@@ -680,6 +698,21 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
         for (int e = 0; e < 4; ++e) {
           hv[g][2 * e] = gelu_f(bf16_lo(ws[e]));
           hv[g][2 * e + 1] = gelu_f(bf16_hi(ws[e]));
+        }
+      }
+      // optional export of the fp32 H that Q(H) quantizes. These stores precede the
+      // pair's code stores, so the exact vmcnt waits below stay correct (operations
+      // complete in issue order; extra ones ahead of the last NS only make a wait
+      // stricter).
+      if (a.hdbg != nullptr) {
+        const bufres rh = make_buf(a.hdbg, (uint64_t)a.M * a.K * 4);
+        const int64_t col = cc * CHUNK + 32 * b + 8 * lq;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t row = r0 + 16 * g + lr;
+          const uint32_t off = sel_off(cc < ch1 && row < a.M && col < a.K, (uint32_t)((row * a.K + col) * 4));
+          buf_store16(rh, off, __builtin_bit_cast(v4i, v4f{hv[g][0], hv[g][1], hv[g][2], hv[g][3]}));
+          buf_store16(rh, off + 16, __builtin_bit_cast(v4i, v4f{hv[g][4], hv[g][5], hv[g][6], hv[g][7]}));
         }
       }
     }
@@ -774,9 +807,9 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
       }
     }
   };
-  auto work = [&](int i, int64_t pf) __attribute__((always_inline)) {
-    work_half(i, 0, pf);
-    work_half(i, 1, pf);
+  auto work = [&](int i, int64_t cc, int64_t pf) __attribute__((always_inline)) {
+    work_half(i, 0, cc, pf);
+    work_half(i, 1, cc, pf);
   };
 
   auto store_pair = [&](int k) __attribute__((always_inline)) {
@@ -814,9 +847,9 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
   for (int k = 0; k < rounds; ++k) {
     sbs0 = sbs1 = 0;
     wait_vmcnt<NS>();  // chunk (k, 0) landed; the last pair's stores may still be in flight
-    work(0, chunk_of(k, 1));
+    work(0, chunk_of(k, 0), chunk_of(k, 1));
     wait_vmcnt<0>();
-    work(1, chunk_of(k + 1, 0));
+    work(1, chunk_of(k, 1), chunk_of(k + 1, 0));
     if constexpr (NS > 0) store_pair(k);
   }
   if constexpr (TP > 0) {

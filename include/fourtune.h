@@ -70,10 +70,11 @@ typedef struct {
 
 /* One W4A4G4 linear: Y = Q(X) Q(R)^T + X^ L1^T L2^T + X^ A^T B^T (FourTune §3.1).
  * n = out features, k = in features (multiples of 32). rank = r (LoRA), stab_rank = s;
- * each a multiple of 16, r + s a multiple of 32; either may be 0 (branch absent).
- * Limits of this build (FT_ERR_UNSUPPORTED beyond them): n, k <= 16384;
- * r + s <= 128 and ceil(r/32) + ceil(s/32) <= 4; (m + 64) * max(n, k) * 4 bytes
- * below 4 GiB (32-bit buffer addressing). */
+ * each a multiple of 16 (FT_ERR_SHAPE otherwise); either may be 0 (branch absent).
+ * Limits of this build (FT_ERR_UNSUPPORTED beyond them): r + s a multiple of 32 (so
+ * r = 16, s = 32 is refused); n, k <= 16384; r + s <= 128 and
+ * ceil(r/32) + ceil(s/32) <= 4; (m + 64) * max(n, k) * 4 bytes below 4 GiB (32-bit
+ * buffer addressing). */
 typedef struct {
   ft_mx4 r;               /* Q(R), rows = n, cols = k (frozen; from fourtune_quantize) */
   const void *lora_a;     /* A  [rank x k]      bf16, trainable down-projection     */
@@ -180,11 +181,13 @@ size_t fourtune_mlp_workspace_bytes(int64_t m, const ft_linear *fc1, const ft_li
  *             overwritten; pass them to the backward.
  *   hq_out    optional (may be NULL): receives Q(H) ([m x f] MXFP4) instead of the
  *             workspace holding it.
+ *   h_debug   optional (may be NULL): [m x f] fp32, receives the fp32 H that step 3
+ *             quantized (for checking Q(H) bit for bit); costs 4 bytes per element.
  * f must be at most 16384 (it is FC2's reduction length). */
 ft_status fourtune_mlp_fwd(const ft_linear *fc1, const ft_linear *fc2, const void *x,
                            ft_dtype x_dt, int64_t m, void *y, ft_dtype y_dt, void *xl1_saved,
-                           void *pre_saved, void *hl2_saved, ft_mx4 *hq_out, void *ws,
-                           size_t ws_bytes, void *stream);
+                           void *pre_saved, void *hl2_saved, ft_mx4 *hq_out, float *h_debug,
+                           void *ws, size_t ws_bytes, void *stream);
 
 /* fourtune_mlp_bwd -- backward of the MLP pair (FourTune §3.2 for each linear, §3.3
  * "MLP Fusion" for the GELU). Kernels, in order:
@@ -199,12 +202,15 @@ ft_status fourtune_mlp_fwd(const ft_linear *fc1, const ft_linear *fc2, const voi
  *   dy [m x fc2->n] (dy_dt); x, xl1_saved, pre_saved, hl2_saved from the forward;
  *   dx [m x d] (dx_dt), overwritten; d_a1 [r1 x d], d_b1 [f x r1], d_a2 [r2 x f],
  *   d_b2 [fc2->n x r2] fp32, overwritten (may be NULL when that rank is 0).
- *   dpq_out optional (may be NULL): receives Q(dP) ([m x f] MXFP4). */
+ *   dpq_out optional (may be NULL): receives Q(dP) ([m x f] MXFP4).
+ *   dp_debug optional (may be NULL): [m x f] fp32, receives the fp32 dP that step 2
+ *            quantized (for checking Q(dP) bit for bit). */
 ft_status fourtune_mlp_bwd(const ft_linear *fc1, const ft_linear *fc2, const void *dy,
                            ft_dtype dy_dt, const void *x, ft_dtype x_dt, const void *xl1_saved,
                            const void *pre_saved, const void *hl2_saved, int64_t m, void *dx,
                            ft_dtype dx_dt, float *d_a1, float *d_b1, float *d_a2, float *d_b2,
-                           ft_mx4 *dpq_out, void *ws, size_t ws_bytes, void *stream);
+                           ft_mx4 *dpq_out, float *dp_debug, void *ws, size_t ws_bytes,
+                           void *stream);
 
 /* ---------------------------------------------------------------- fusion ablation
  * The same layer with the fusions taken apart, for measuring what they save (FourTune

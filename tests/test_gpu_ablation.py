@@ -20,7 +20,7 @@ from bit_quantized_lora_fp4_amd import abi
 from oracle import layer, mx4
 from synth import workloads as wl
 from tests.gpu_util import dev, host, log, rel_fro
-from tests.test_gpu_fullsize import (_bf, _block_rows, _chunked, _col_blocks, _errs_ok, _f64, _gpu_lin,
+from tests.sampling import (_bf, _block_rows, _chunked, _col_blocks, _errs_ok, _f64, _gpu_lin,
                                      _lin64, _rows)
 
 pytestmark = pytest.mark.gpu

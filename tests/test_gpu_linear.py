@@ -1,10 +1,13 @@
 """GPU parity of fourtune_linear_fwd / fourtune_linear_bwd against the oracle.
 
-Bar: Q(X), Q(dY) codes and scales bit-exact; Y, dX, dA, dB (fp32 outputs) within a
-relative Frobenius error of 1e-3 of the fp64 oracle; bf16 outputs against the oracle
-rounded to bf16 within the same bar. The oracle computes everything from the same
-seeded inputs; nothing it uses comes from the GPU.
+Bar: Q(X), Q(dY) codes and scales bit-exact; XL, Y, dX, dA, dB element by element
+within the bounds derived in tests/parity.py (fp32 accumulation plus one bf16 ulp per
+rounded intermediate), each stage on the operands it consumes; and, end to end, the
+oracle's own chain from the same seeded inputs within a relative Frobenius error of
+1e-3 (bf16 outputs against the oracle rounded to bf16).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -12,7 +15,8 @@ import torch
 from bit_quantized_lora_fp4_amd import abi
 from oracle import layer, mx4
 from synth import workloads as wl
-from tests.gpu_util import dev, host, host_u8, log, oracle_packed, rel_fro
+from tests import parity
+from tests.gpu_util import dev, host, host_u8, log, rel_fro
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -48,19 +52,24 @@ def _run(d, out_dtype=torch.float32):
 
 def _check_full(d, got, out_bf16=False):
     lin = _oracle_linear(d)
-    X = d["X"].astype(np.float64)
-    G = d["dY"].astype(np.float64)
-    Y, XL = layer.linear_forward(X, lin)
-    dX, dA, dB, _ = layer.linear_backward(G, X, XL, lin)
-    wc, ws_ = oracle_packed(X)
-    assert np.array_equal(got["xq"][1], ws_) and np.array_equal(got["xq"][0], wc), "Q(X)"
-    gc, gs = oracle_packed(G)
-    assert np.array_equal(got["gq"][1], gs) and np.array_equal(got["gq"][0], gc), "Q(dY)"
+    X, G = d["X"], d["dY"]
+    parity.quant_exact("Q(X)", *got["xq"], X)
+    parity.quant_exact("Q(dY)", *got["gq"], G)
+    ex = parity.linear_expect(lin, X, G, got)
+    parity.check_values("XL", got["XL"], *ex["XL"], out_bf16=True)
+    for k_ in ("Y", "dX"):
+        parity.check_values(k_, got[k_], *ex[k_], out_bf16=out_bf16)
+    for k_ in ("dA", "dB"):
+        if k_ in ex:
+            parity.check_values(k_, got[k_], *ex[k_])
+    # end to end: the oracle's own chain
+    X64, G64 = X.astype(np.float64), G.astype(np.float64)
+    Y, XL = layer.linear_forward(X64, lin)
+    dX, dA, dB, _ = layer.linear_backward(G64, X64, XL, lin)
     rnd = mx4.bf16_round if out_bf16 else (lambda a: a)
-    errs = dict(XL=rel_fro(got["XL"], XL), Y=rel_fro(got["Y"], rnd(Y)), dX=rel_fro(got["dX"], rnd(dX)),
-                dA=rel_fro(got["dA"], dA) if dA.size else 0.0,
-                dB=rel_fro(got["dB"], dB) if dB.size else 0.0)
-    log(f"  rel errors {errs}")
+    errs = dict(Y=rel_fro(got["Y"], rnd(Y)), dX=rel_fro(got["dX"], rnd(dX)),
+                dA=rel_fro(got["dA"], dA) if dA.size else 0.0, dB=rel_fro(got["dB"], dB) if dB.size else 0.0)
+    log(f"  end to end rel errors {errs}")
     for k_, e in errs.items():
         assert e <= TOL, (k_, e)
     return errs
@@ -105,9 +114,17 @@ def test_c1_tiny_layer():
 
 
 def test_c2_attention_projection():
-    log("linear c2 (full size, full oracle)")
+    log("linear c2 (full size, full oracle), fp32 outputs")
     d = wl.linear_case("c2")
     _check_full(d, _run(d))
+
+
+def test_c2_attention_projection_bf16_outputs():
+    """c2 in the launch configuration the benchmark times (bf16 Y and dX), against the
+    full oracle."""
+    log("linear c2 (full size, full oracle), bf16 outputs")
+    d = wl.linear_case("c2")
+    _check_full(d, _run(d, out_dtype=torch.bfloat16), out_bf16=True)
 
 
 def test_deterministic():
@@ -180,12 +197,19 @@ def test_workspace_and_argument_errors():
         abi.fourtune_linear_fwd(L, x, y, xl, small)
     assert e.value.name == "FT_ERR_WORKSPACE"
     ws = abi.workspace(abi.fourtune_linear_workspace_bytes(64, L))
-    with pytest.raises(abi.FourTuneError) as e:
+    with pytest.raises(ValueError):  # the binding checks every tensor before the call
         abi.fourtune_linear_fwd(L, x, y, None, ws)
-    assert e.value.name == "FT_ERR_NULL"
-    with pytest.raises(abi.FourTuneError) as e:
-        abi.fourtune_linear_fwd(L, x[:, 1:], y, xl, ws)  # misaligned
-    assert e.value.name == "FT_ERR_ALIGN"
+    with pytest.raises(ValueError):
+        abi.fourtune_linear_fwd(L, x[:, 1:], y, xl, ws)
+    # the library's own checks, reached with raw pointers
+    s = L.struct()
+    lib = abi.lib()
+    st = lib.fourtune_linear_fwd(ctypes.byref(s), abi._ptr(x), abi.FT_BF16, 64, abi._ptr(y), abi.FT_F32, None,
+                                 None, abi._ptr(ws), ws.numel(), None)
+    assert abi.STATUS[st] == "FT_ERR_NULL"
+    st = lib.fourtune_linear_fwd(ctypes.byref(s), ctypes.c_void_p(x.data_ptr() + 2), abi.FT_BF16, 64, abi._ptr(y),
+                                 abi.FT_F32, abi._ptr(xl), None, abi._ptr(ws), ws.numel(), None)
+    assert abi.STATUS[st] == "FT_ERR_ALIGN"
 
 
 def test_gemm_entry_points():

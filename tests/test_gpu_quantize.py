@@ -102,3 +102,74 @@ def test_empty_is_noop():
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     q = abi.Mx4.empty(0, 64)
     abi.fourtune_quantize(x, q)
+
+
+# ------------------------------------------------------------------ exhaustive table
+def _exhaustive_blocks(fp32: bool, seed: int = 0):
+    """Every finite bf16 bit pattern under every scale byte it can carry.
+
+    A block's scale byte s comes from its amax: for an amax with fp32 exponent field
+    e >= 3, s = e - 2; smaller (and zero or subnormal) amax give s = 0. So a block whose
+    largest magnitude is the anchor with exponent field s + 2 (field 2 for s = 0) and
+    all-ones mantissa has scale byte s, and any pattern of magnitude up to the anchor
+    can sit in it. For each s in 0..252 (253 and 254 need an exponent field of 255, i.e.
+    a non-finite amax: unreachable from finite input) every bf16 magnitude up to the
+    anchor, with both signs, fills blocks of 1023 behind that anchor; 256 more blocks
+    each hold one of the 256 non-finite patterns (scale byte 0xFF, codes zero). With
+    fp32 input the lower 16 bits of every value carry random bits (the anchor keeps an
+    all-ones mantissa, so it stays the block maximum). Returns fp32 bit patterns [rows x
+    4096] holding 8.6M values."""
+    rng = np.random.default_rng(seed)
+    blocks = []
+    for s in range(253):
+        e = s + 2 if s > 0 else 2
+        anchor = (e << 7) | 0x7F
+        mags = np.arange(anchor + 1, dtype=np.uint32)
+        vals = np.concatenate([mags, mags | 0x8000])
+        n_blk = -(-vals.size // 1023)
+        pad = np.zeros(n_blk * 1023, dtype=np.uint32)
+        pad[: vals.size] = vals
+        b = np.empty((n_blk, 1024), dtype=np.uint32)
+        b[:, 0] = anchor
+        b[:, 1:] = pad.reshape(n_blk, 1023)
+        blocks.append(b)
+    special = np.arange(0x7F80, 0x8000, dtype=np.uint32)
+    special = np.concatenate([special, special | 0x8000])
+    sb = rng.integers(0, 0x7F80, (special.size, 1024), dtype=np.uint32) | (
+        rng.integers(0, 2, (special.size, 1024), dtype=np.uint32) << 15)
+    sb[np.arange(special.size), rng.integers(0, 1024, special.size)] = special
+    blocks.append(sb)
+    allb = np.concatenate(blocks)                          # [nblocks x 1024] bf16 bits
+    nbc = 128
+    nbr = -(-allb.shape[0] // nbc)
+    full = np.zeros((nbr * nbc, 1024), dtype=np.uint32)
+    full[: allb.shape[0]] = allb
+    bits = full << 16
+    if fp32:
+        low = rng.integers(0, 1 << 16, bits.shape, dtype=np.uint32)
+        finite = (full & 0x7F80) != 0x7F80
+        low[:, 0] = np.where(allb.shape[0] > np.arange(full.shape[0]), 0xFFFF, 0)  # anchors: all-ones mantissa
+        bits = bits | np.where(finite, low, 0)
+    # block (br, bc) element (i, j) -> row 32 br + i, column 32 bc + j
+    t = bits.reshape(nbr, nbc, 32, 32).transpose(0, 2, 1, 3).reshape(nbr * 32, nbc * 32)
+    return np.ascontiguousarray(t)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_exhaustive_bf16_patterns_every_scale(dtype):
+    """The quantizer against the oracle on every bf16 pattern under every reachable
+    scale byte (0..252) plus the non-finite patterns: codes and scales bit for bit."""
+    bits = _exhaustive_blocks(dtype == "fp32")
+    log(f"quantize exhaustive table {bits.shape} {dtype}: {bits.size} values")
+    T = bits.view(np.float32)
+    if dtype == "bf16":
+        x = torch.from_numpy((bits >> 16).astype(np.uint16).view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        x = torch.from_numpy(bits.view(np.int32)).view(torch.float32).cuda()
+    q = abi.quantize(x)
+    torch.cuda.synchronize()
+    want_c, want_s = oracle_packed(T.astype(np.float64))
+    got_c, got_s = host_u8(q.codes), host_u8(q.scales)
+    assert set(np.unique(want_s).tolist()) == set(range(253)) | {255}
+    assert np.array_equal(got_s, want_s), f"scales differ at {np.argwhere(got_s != want_s)[:5]}"
+    assert np.array_equal(got_c, want_c), f"codes differ at {np.argwhere(got_c != want_c)[:5]}"
