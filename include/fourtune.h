@@ -47,7 +47,11 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status and dtype codes are plain 32-bit integers with named values, so any integer a
+ * caller passes is a defined value that validation can reject (an out-of-range value
+ * held in an enum type would not be). */
+typedef int32_t ft_status;
+enum {
   FT_OK = 0,
   FT_ERR_NULL = 1,         /* a required pointer is NULL                           */
   FT_ERR_SHAPE = 2,        /* a size is negative, inconsistent or not a multiple   */
@@ -56,9 +60,10 @@ typedef enum {
   FT_ERR_WORKSPACE = 5,    /* workspace missing or smaller than required           */
   FT_ERR_UNSUPPORTED = 6,  /* valid request this build does not handle             */
   FT_ERR_HIP = 7           /* the HIP runtime reported an error                    */
-} ft_status;
+};
 
-typedef enum { FT_F32 = 0, FT_BF16 = 1 } ft_dtype;
+typedef int32_t ft_dtype;
+enum { FT_F32 = 0, FT_BF16 = 1 };
 
 /* One MXFP4 tensor (see the format above). */
 typedef struct {
