@@ -96,6 +96,8 @@ _SIGS = {
     "fourtune_linear_bwd_prec": (ctypes.c_int, [ctypes.POINTER(FtLinear), ctypes.c_int, c_vp,
                                                 ctypes.c_int, c_vp, ctypes.c_int, c_vp, c_i64, c_vp,
                                                 ctypes.c_int, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "fourtune_linear_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(FtLinear), c_vp, ctypes.c_int, c_i64, c_vp,
+                                                   ctypes.c_int, c_vp, ctypes.POINTER(FtMx4), c_vp]),
     "fourtune_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "fourtune_last_error": (ctypes.c_char_p, []),
 }
@@ -396,6 +398,21 @@ def fourtune_linear_bwd(L: Linear, dy: torch.Tensor, x: torch.Tensor, xl_saved: 
                                      ctypes.byref(gq) if gq is not None else None,
                                      _ptr(ws), ws.numel() if ws is not None else 0,
                                      _stream(stream)))
+
+
+def fourtune_linear_fwd_noalloc(L: Linear, x: torch.Tensor, y: torch.Tensor, xl_saved: torch.Tensor,
+                                xq_out: Mx4, stream=None):
+    """The forward without a workspace (the library allocates nothing; Q(X) goes to
+    xq_out, the split reduction's partial sums to the library's own device array)."""
+    _need_linear(L)
+    m = x.shape[0] if isinstance(x, torch.Tensor) and x.dim() == 2 else -1
+    _need(x, "x", (m, L.k), _F32_BF16)
+    _need(y, "y", (m, L.n), _F32_BF16)
+    _need_low(xl_saved, "xl_saved", m, _rt(L))
+    _need_mx4(xq_out, "xq_out", m, L.k)
+    s, q = L.struct(), xq_out.struct()
+    _check(lib().fourtune_linear_fwd_noalloc(ctypes.byref(s), _ptr(x), _dt(x), m, _ptr(y), _dt(y), _ptr(xl_saved),
+                                             ctypes.byref(q), _stream(stream)))
 
 
 def fourtune_gemm_fwd(L: Linear, xq: Mx4, xl: Optional[torch.Tensor], y: torch.Tensor,

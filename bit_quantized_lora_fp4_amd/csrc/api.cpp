@@ -323,7 +323,61 @@ ft_status run_lora_grad(const ft_linear* L, int64_t m, const void* gb, const voi
   return hip_check(ft::launch_lora_grad(lg, st), what);
 }
 
+// Argument checks of the linear forward (shared by the workspace and scratch forms).
+ft_status check_linear_fwd_args(const ft_linear* L, const void* x, ft_dtype x_dt, int64_t m, const void* y,
+                                ft_dtype y_dt, const void* xl_saved, const ft_mx4* xq_out, const char* who) {
+  TRY(check_linear(L, who));
+  REQUIRE(dtype_ok(x_dt) && dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
+  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  if (m == 0) return FT_OK;
+  TRY(check_m(m, L, who));
+  TRY(check_tensor(x, who, "x"));
+  TRY(check_tensor(y, who, "y"));
+  if (L->rank + L->stab_rank > 0) TRY(check_tensor(xl_saved, who, "xl_saved"));
+  if (xq_out) TRY(check_mx4(xq_out, m, L->k, "linear_fwd: xq_out"));
+  return FT_OK;
+}
+
+// The forward's two launches: one pass over X (Q(X), XL; fp32 partial sums in
+// `partials` when the reduction is split), then the 4-bit GEMM with the up-projection.
+ft_status launch_linear_fwd(const ft_linear* L, const void* x, ft_dtype x_dt, int64_t m, void* y, ft_dtype y_dt,
+                            void* xl_saved, uint8_t* xq_codes, uint8_t* xq_scales, float* partials, hipStream_t st) {
+  const int64_t rt = L->rank + L->stab_rank;
+  ft::QuantDownArgs qd{};
+  qd.mode = ft::QD_QUANT;
+  qd.x = x; qd.M = m; qd.K = L->k; qd.ldx = L->k;
+  qd.codes = xq_codes; qd.scales = xq_scales;
+  qd.d0 = static_cast<const ft::bf16_t*>(L->lora_a);
+  qd.d1 = static_cast<const ft::bf16_t*>(L->stab_down);
+  qd.r0 = (int)L->rank; qd.rt = (int)rt; qd.u_cols = false;
+  qd.low = static_cast<ft::bf16_t*>(xl_saved);
+  qd.partials = partials;
+  TRY(hip_check(ft::launch_quant_down(qd, x_dt == FT_BF16, st), "linear_fwd quant_down"));
+  return run_gemm_fwd(L, xq_codes, xq_scales, xl_saved, m, y, y_dt, st);
+}
+
 }  // namespace
+
+namespace ft {
+
+ft_status linear_fwd_scratch(const ft_linear* L, const void* x, ft_dtype x_dt, int64_t m, void* y, ft_dtype y_dt,
+                             void* xl_saved, ft_mx4* xq_out, float* scratch, size_t scratch_bytes, void* stream,
+                             const char* who) {
+  TRY(check_linear_fwd_args(L, x, x_dt, m, y, y_dt, xl_saved, xq_out, who));
+  REQUIRE(xq_out != nullptr, FT_ERR_NULL, "%s: xq_out is required (Q(X) is an output here)", who);
+  if (m == 0) return ok();
+  const size_t need = quant_down_partial_bytes(m, L->k, (int)L->rank, (int)(L->rank + L->stab_rank));
+  REQUIRE(need <= scratch_bytes, FT_ERR_UNSUPPORTED,
+          "%s: m=%lld, k=%lld, rank + stab_rank=%lld need %zu bytes of scratch, %zu available", who, (long long)m,
+          (long long)L->k, (long long)(L->rank + L->stab_rank), need, scratch_bytes);
+  TRY(launch_linear_fwd(L, x, x_dt, m, y, y_dt, xl_saved, xq_out->codes, xq_out->scales, scratch,
+                        static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+ft_status set_error(ft_status s, const char* msg) { return fail(s, "%s", msg); }
+
+}  // namespace ft
 
 extern "C" {
 
@@ -338,35 +392,16 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const void* x, ft_dtype x_dt, 
                               ft_dtype y_dt, void* xl_saved, ft_mx4* xq_out, void* ws,
                               size_t ws_bytes, void* stream) {
   const char* who = "linear_fwd";
-  TRY(check_linear(L, who));
-  REQUIRE(dtype_ok(x_dt) && dtype_ok(y_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
-  REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
+  TRY(check_linear_fwd_args(L, x, x_dt, m, y, y_dt, xl_saved, xq_out, who));
   if (m == 0) return ok();
-  TRY(check_m(m, L, who));
-  const int64_t rt = L->rank + L->stab_rank;
-  TRY(check_tensor(x, who, "x"));
-  TRY(check_tensor(y, who, "y"));
-  if (rt > 0) TRY(check_tensor(xl_saved, who, "xl_saved"));
-  if (xq_out) TRY(check_mx4(xq_out, m, L->k, "linear_fwd: xq_out"));
   const FwdLayout lay = fwd_layout(ws, m, L, xq_out == nullptr);
   REQUIRE(lay.bytes == 0 || (ws != nullptr && ws_bytes >= lay.bytes), FT_ERR_WORKSPACE,
           "%s: workspace of %zu bytes, %zu needed", who, ws_bytes, lay.bytes);
   if (lay.bytes) REQUIRE(aligned16(ws), FT_ERR_ALIGN, "%s: workspace misaligned", who);
-  hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* xq_codes = xq_out ? xq_out->codes : lay.xq_codes;
   uint8_t* xq_scales = xq_out ? xq_out->scales : lay.xq_scales;
-
-  ft::QuantDownArgs qd{};
-  qd.mode = ft::QD_QUANT;
-  qd.x = x; qd.M = m; qd.K = L->k; qd.ldx = L->k;
-  qd.codes = xq_codes; qd.scales = xq_scales;
-  qd.d0 = static_cast<const ft::bf16_t*>(L->lora_a);
-  qd.d1 = static_cast<const ft::bf16_t*>(L->stab_down);
-  qd.r0 = (int)L->rank; qd.rt = (int)rt; qd.u_cols = false;
-  qd.low = static_cast<ft::bf16_t*>(xl_saved);
-  qd.partials = lay.partials;
-  TRY(hip_check(ft::launch_quant_down(qd, x_dt == FT_BF16, st), "linear_fwd quant_down"));
-  TRY(run_gemm_fwd(L, xq_codes, xq_scales, xl_saved, m, y, y_dt, st));
+  TRY(launch_linear_fwd(L, x, x_dt, m, y, y_dt, xl_saved, xq_codes, xq_scales, lay.partials,
+                        static_cast<hipStream_t>(stream)));
   return ok();
 }
 
