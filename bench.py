@@ -7,6 +7,7 @@
     python bench.py --granularity        (32x32 blocks vs 1x32 groups: error study; one JSON line)
     python bench.py --precision          (the four precision configurations at c2; one JSON line)
     python bench.py --gemm-sweep         (both 4-bit GEMMs of every linear of c2..c5; one JSON line)
+    python bench.py --hbm-sweep          (quantizer, fused quantize + down-projection, MLP pass, c2..c5)
 
 One step = the whole hot path once over one batch: the layer's forward (fused
 quantize + down-projection, 4-bit GEMM + up-projection) and backward (fused quantize +
@@ -62,6 +63,8 @@ def parse():
                     help="32x32 blocks vs 1x32 groups for X and dY: quantization error study")
     ap.add_argument("--precision", action="store_true",
                     help="W4A4G4 vs W4A16G4 / W4A4G16 / W4A16G16 at c2")
+    ap.add_argument("--hbm-sweep", action="store_true",
+                    help="HBM-bound kernels (quantizer, fused quantize + down-projection, MLP pass) of c2..c5")
     ap.add_argument("--gemm-sweep", action="store_true",
                     help="4-bit GEMM TFLOPS and MXFP4-peak fraction for every linear of c2..c5")
     ap.add_argument("--double-blocks", type=int, default=19)
@@ -496,6 +499,94 @@ def gemm_sweep(args):
     return 0
 
 
+# --------------------------------------------------------------------------- HBM-bound kernels
+def hbm_sweep(args):
+    """The HBM-bound kernels of every workload at full size, against the 8 TB/s peak:
+    the quantizer on each activation (bf16 read 2 B + codes 0.5 B + scales 1/1024 B per
+    element), the fused quantize + down-projection of each linear's forward with its
+    partial sum (plus 2 rt / K B per element for the saved XL; taken as the linear's
+    forward minus its GEMM), and the MLP's pass over the saved P^ (GELU, Q(H), HL2: P^
+    read 2 B + 0.5 B codes per element; taken as the MLP forward minus FC1's linear
+    forward and FC2's GEMM). Graph replays over rotated input sets, median per launch;
+    random bf16 operands (the kernels' time does not depend on the values). Per-kernel
+    durations of the same run come from rocprofv3's kernel trace."""
+    import torch
+    from bit_quantized_lora_fp4_amd import abi
+    from synth import workloads as wl
+
+    abi.lib()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+
+    def bf(shape, std=1.0):
+        return (torch.randn(shape, generator=gen, device="cuda") * std).to(torch.bfloat16)
+
+    def lin(n, k, r, s):
+        return abi.Linear(abi.quantize(bf((n, k), 0.02)), bf((r, k), 0.01), bf((n, r), 0.01), bf((s, k), 0.1),
+                          bf((n, s), 0.1))
+
+    def gbps(nbytes, t):
+        return round(nbytes / t / 1e9, 1)
+
+    res = {}
+    for key in ("c2", "c3", "c4", "c5"):
+        spec = wl.WORKLOADS[key]
+        m = spec.m
+        for ls in spec.layers:
+            is_mlp = not isinstance(ls, wl.LinearSpec)
+            k = ls.d if is_mlp else ls.k
+            n = ls.f if is_mlp else ls.n
+            r, s_ = ls.r, ls.s
+            rt = r + s_
+            nsets = 2 if m * max(n, k) > 1 << 27 else 4
+            sets = []
+            for _ in range(nsets):
+                st = dict(x=bf((m, k)), L=lin(n, k, r, s_), y=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+                          xl=torch.empty((m, rt), dtype=torch.bfloat16, device="cuda"), xq=abi.Mx4.empty(m, k))
+                if is_mlp:
+                    st["fc2"] = lin(ls.d, ls.f, r, s_)
+                    st["hq"] = abi.quantize(bf((m, ls.f)))
+                    st["hl2"] = bf((m, rt), 0.1)
+                    st["out"] = torch.empty((m, ls.d), dtype=torch.bfloat16, device="cuda")
+                    st["ws"] = abi.workspace(max(abi.fourtune_mlp_workspace_bytes(m, st["L"], st["fc2"]),
+                                                 abi.fourtune_linear_workspace_bytes(m, st["L"])))
+                else:
+                    st["ws"] = abi.workspace(abi.fourtune_linear_workspace_bytes(m, st["L"]))
+                sets.append(st)
+            torch.cuda.synchronize()
+            S = lambda i: sets[i % nsets]
+            tq = time_graph_stats(torch, lambda i: abi.fourtune_quantize(S(i)["x"], S(i)["xq"]))[0]
+            tf = time_graph_stats(torch, lambda i: abi.fourtune_linear_fwd(S(i)["L"], S(i)["x"], S(i)["y"], S(i)["xl"],
+                                                                           S(i)["ws"]))[0]
+            tg = time_graph_stats(torch, lambda i: abi.fourtune_gemm_fwd(S(i)["L"], S(i)["xq"], S(i)["xl"], S(i)["y"]))[0]
+            q_bytes = m * k * 2.5 + ((m + 31) // 32) * (k // 32)
+            qd_bytes = q_bytes + m * rt * 2
+            name = f"{key}.{ls.name}" + (".fc1" if is_mlp else "")
+            row = {"m": m, "k": k, "n": n, "rt": rt,
+                   "quantize_us": round(tq * 1e6, 2), "quantize_gbps": gbps(q_bytes, tq),
+                   "quantize_frac": round(q_bytes / tq / 1e9 / PEAK_HBM_GBPS, 4),
+                   "quant_down_us": round((tf - tg) * 1e6, 2), "quant_down_gbps": gbps(qd_bytes, tf - tg),
+                   "quant_down_frac": round(qd_bytes / (tf - tg) / 1e9 / PEAK_HBM_GBPS, 4)}
+            if is_mlp:
+                f = ls.f
+                tm = time_graph_stats(torch, lambda i: abi.fourtune_mlp_fwd(S(i)["L"], S(i)["fc2"], S(i)["x"], S(i)["out"],
+                                                                            S(i)["xl"], S(i)["y"], S(i)["hl2"],
+                                                                            S(i)["ws"]))[0]
+                tg2 = time_graph_stats(torch, lambda i: abi.fourtune_gemm_fwd(S(i)["fc2"], S(i)["hq"], S(i)["hl2"],
+                                                                              S(i)["out"]))[0]
+                tp = tm - tf - tg2
+                p_bytes = m * f * 2.5 + ((m + 31) // 32) * (f // 32) + m * rt * 2
+                row.update({"gelu_pass_us": round(tp * 1e6, 2), "gelu_pass_gbps": gbps(p_bytes, tp),
+                            "gelu_pass_frac": round(p_bytes / tp / 1e9 / PEAK_HBM_GBPS, 4)})
+            res[name] = row
+            log(f"[hbm-sweep] {name}: " + ", ".join(f"{k_}={v}" for k_, v in row.items()))
+            del sets
+            torch.cuda.empty_cache()
+    print(json.dumps({"metric": "HBM-bound kernels: algorithmic bytes / time, fraction of 8 TB/s",
+                      "unit": "GB/s", "peak": PEAK_HBM_GBPS, "n_gpus": 1, "data": "synthetic", **res}), flush=True)
+    return 0
+
+
 # --------------------------------------------------------------------------- precision configurations
 def precision(args):
     """The c2 linear's fwd+bwd in the four precision configurations of the pages'
@@ -771,6 +862,8 @@ def main():
         return precision(args)
     if args.gemm_sweep:
         return gemm_sweep(args)
+    if args.hbm_sweep:
+        return hbm_sweep(args)
     import torch
     from bit_quantized_lora_fp4_amd import abi
     from synth import workloads as wl
