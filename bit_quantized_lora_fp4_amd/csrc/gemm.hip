@@ -22,7 +22,9 @@
 // elements per step. A step's two code tiles (32 KB each, 128-byte rows: whole cache
 // lines) land in one of two LDS stages by direct-to-LDS buffer loads issued during the
 // step before, one 1 KB segment per scheduling region so the loads go out between
-// MFMAs; a 4-byte touch per line pulls the step after that into L2. The block scales
+// MFMAs. (An L2 prefetch of the step after that, one 4-byte load per line, made the
+// kernel 4-6% slower at every size: it doubles the cache-line requests a step issues.)
+// The block scales
 // of the workgroup's rows and columns for the whole reduction are staged into LDS
 // once, before the main loop. Each stage is its own LDS object, so the compiler knows
 // which loads a fragment read can alias. The up-projection's operands (its first 64
@@ -54,7 +56,6 @@ constexpr int SUBSTEPS = BK / 64;              // MFMA reduction substeps per st
 constexpr int TILE_BYTES = 256 * BK / 2;       // 32 KB of codes per operand tile per step
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;    // activation tile + R tile
 constexpr int SCALE_BYTES = 8192;              // LDS for the two operands' block scales
-constexpr int TOUCH_BYTES = 1024;              // landing slots of the L2 prefetch loads
 constexpr int MAX_NKB = SCALE_BYTES / 2 / 8;   // 8 block rows per operand: Kred <= 16384
 #ifndef GEMM_NWN
 #define GEMM_NWN 4
@@ -70,7 +71,6 @@ struct Waves {
   static constexpr int WCOLS = BN / NWN;             // output columns per wave
   static constexpr int TI = WCOLS / 32;              // 32x32 MFMA tiles per wave, R side
   static constexpr int SEGS = TILE_BYTES / 1024 / N; // 1 KB load segments per wave per tile
-  static constexpr int TOUCHES = 8 / N;              // L2 prefetch loads per wave per step
   static constexpr int SW = 8 * MAX_NKB / 4 / NT;    // scale words staged per thread per operand
 };
 
@@ -200,7 +200,7 @@ __device__ __forceinline__ void quant_tile_store(const float (&v)[16], int lane,
 template <bool TRANS_B, bool OUT_BF16, int EPI, int NWN>
 __global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g) {
   using W = Waves<NWN>;
-  constexpr int TI = W::TI, SEGS = W::SEGS, TOUCHES = W::TOUCHES, SW = W::SW, NT = W::NT;
+  constexpr int TI = W::TI, SEGS = W::SEGS, SW = W::SW, NT = W::NT;
   constexpr int WCOLS = W::WCOLS;
   // Separate LDS objects per stage: the compiler then knows a transposed LDS read of one
   // stage cannot alias the direct-to-LDS loads still filling the other, and does not
@@ -208,7 +208,6 @@ __global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g
   __shared__ __align__(16) char st0_raw[STAGE_BYTES];
   __shared__ __align__(16) char st1_raw[STAGE_BYTES];
   __shared__ __align__(16) char scale_raw[SCALE_BYTES];
-  __shared__ __align__(16) char touch_raw[TOUCH_BYTES];
   lds_char* const st0 = (lds_char*)st0_raw;
   lds_char* const st1 = (lds_char*)st1_raw;
 
@@ -292,47 +291,6 @@ __global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g
     }
   };
 
-  // ---- L2 prefetch of a later step: one 4-byte load per 128-byte line of both operand
-  // tiles (lane l of wave w touches row 64(w%4) + l: of both tiles with 4 waves, of the
-  // activation tile for waves 0-3 and the R tile for waves 4-7 with 8), landing in a
-  // dummy LDS slot. Issued after a step's stage loads and allowed to stay in flight
-  // across the step's wait, it turns the stage loads of the step after into L2 hits.
-  lds_char* touch = (lds_char*)touch_raw + (wave & 3) * 256;
-  const int trow = (wave & 3) * 64 + lane;
-  const bool ta_ok = m0 + trow < g.M;
-  const uint32_t ta_base = (uint32_t)((m0 + trow) * a_pitch);
-  uint32_t tr_base;
-  bool tr_ok;
-  if constexpr (!TRANS_B) {
-    tr_ok = n0 + trow < g.N;
-    tr_base = (uint32_t)((n0 + trow) * g.b_pitch);
-  } else {
-    tr_ok = n0 < g.N;
-    tr_base = (uint32_t)(trow * g.b_pitch + (n0 >> 1));
-  }
-  auto prefetch = [&](int kt) {
-    const bool live = kt < KT;
-    const bool ak = live && ta_ok;
-    const uint32_t ao = ta_base + (uint32_t)kt * (BK / 2);
-    uint32_t ro;
-    bool rk = live && tr_ok;
-    if constexpr (!TRANS_B) ro = tr_base + (uint32_t)kt * (BK / 2);
-    else {
-      ro = tr_base + (uint32_t)((int64_t)kt * BK * g.b_pitch);
-      rk = rk && (int64_t)kt * BK + trow < Kred;
-    }
-    if constexpr (W::N == 4) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)touch, 4,
-                                               (int)sel_off(ak, ao), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void*)touch, 4,
-                                               (int)sel_off(rk, ro), 0, 0, 0);
-    } else {
-      const bool act = wave < 4;  // uniform
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(act ? ra : rr, (__attribute__((address_space(3))) void*)touch, 4,
-                                               (int)sel_off(act ? ak : rk, act ? ao : ro), 0, 0, 0);
-    }
-  };
-
   // ---- block scales for the whole reduction, staged once, step-major: for step kt,
   // lane half h and block row b (0..7) of the tile's operand, the word at
   //   64*kt + 32*h + 4*b
@@ -391,9 +349,9 @@ __global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g
   }
   // reduction blocks 4kw .. 4kw+3 of block row b: bytes 0, 2 go to half 0 and bytes
   // 1, 3 to half 1, each pair at substeps 2(kw%2), 2(kw%2)+1 of step kw/2
-  // The staging stores are written from inline asm: they run while stage 0 and the
-  // first prefetch are in flight, and the compiler, seeing plain LDS stores there,
-  // would wait for every load in flight first (the prefetch included). Their
+  // The staging stores are written from inline asm: they run while stage 0 is in
+  // flight, and the compiler, seeing plain LDS stores there, would wait for every
+  // load in flight first. Their
   // completion is awaited by the lgkmcnt wait before the barrier that follows.
   auto put_word = [&](lds_char* dst, int b, int kw, uint32_t w) {
     const uint32_t o = (uint32_t)(uintptr_t)(dst + 64 * (kw >> 1) + 4 * b + 2 * (kw & 1));
@@ -694,23 +652,20 @@ __global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g
            buf_load16(ru1, sel_off(ok && !first, (uint32_t)(((int64_t)(j - g.up_split) * g.up1_ld + col) * 2)));
   };
   // ---------------------------------------------------------------- main loop
-  // Two stages: step kt+1's 64 KB land while step kt is multiplied. Past the last step
-  // the touch loads go to out-of-range offsets.
+  // Two stages: step kt+1's 64 KB land while step kt is multiplied.
   issue_stage(st0, 0);
   asm volatile("" ::: "memory");
   write_scales();
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the staging stores are done
   vm_barrier<0>();  // step 0 landed; scales in LDS
-  prefetch(1);
   // One step: step kt+1's loads go into the stage step kt-1 used (every wave left it at
   // the last barrier), then step kt's MFMAs run while they land. Unrolled by two so each
   // step names its stage statically. The last step loads the up-projection's operands.
   auto step = [&](lds_char* cur, lds_char* nxt, int kt) __attribute__((always_inline)) {
     compute(cur, kt, nxt);  // also issues step kt+1's stage loads into nxt
     asm volatile("" ::: "memory");
-    prefetch(kt + 2);       // the last two loads before the wait: they may stay in flight
     __builtin_amdgcn_sched_barrier(0);
-    vm_barrier<TOUCHES>();
+    vm_barrier<0>();
   };
   for (int kt = 0; kt < KT; kt += 2) {
     if (kt + 1 == KT) switch_to_low();
