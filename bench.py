@@ -550,7 +550,8 @@ def hbm_sweep(args):
             n = ls.f if is_mlp else ls.n
             r, s_ = ls.r, ls.s
             rt = r + s_
-            nsets = 2 if m * max(n, k) > 1 << 27 else 4
+            # enough input sets that the rotation streams from HBM, not the 256 MB cache
+            nsets = max(2, -(-(640 << 20) // (m * max(n, k) * 2)))
             sets = []
             for _ in range(nsets):
                 st = dict(x=bf((m, k)), L=lin(n, k, r, s_), y=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),

@@ -157,13 +157,8 @@ ft_status check_linear(const ft_linear* L, const char* who) {
           FT_ERR_SHAPE, "%s: rank=%lld, stab_rank=%lld must be multiples of 16", who,
           (long long)L->rank, (long long)L->stab_rank);
   const int64_t rt = L->rank + L->stab_rank;
-  // The fused quantize + down-projection kernels work the low-rank width in pairs of
-  // 16-wide tiles; a width of 16 (mod 32) is a valid layer this build does not handle.
-  REQUIRE(rt % 32 == 0, FT_ERR_UNSUPPORTED, "%s: rank + stab_rank = %lld is not a multiple of 32", who,
-          (long long)rt);
-  REQUIRE(rt <= 128, FT_ERR_UNSUPPORTED, "%s: rank + stab_rank = %lld > 128", who, (long long)rt);
-  REQUIRE(ft::quant_down_tiles((int)L->rank, (int)rt) <= ft::QD_MAX_TILES, FT_ERR_UNSUPPORTED,
-          "%s: ceil(rank/32) + ceil(stab_rank/32) > %d", who, ft::QD_MAX_TILES);
+  REQUIRE(rt <= 128 && ft::quant_down_tiles((int)L->rank, (int)rt) <= ft::QD_MAX_TILES, FT_ERR_UNSUPPORTED,
+          "%s: rank + stab_rank = %lld > 128", who, (long long)rt);
   REQUIRE(L->n <= ft::GEMM_MAX_KRED && L->k <= ft::GEMM_MAX_KRED, FT_ERR_UNSUPPORTED,
           "%s: n=%lld, k=%lld; the 4-bit GEMMs reduce over at most %lld elements", who,
           (long long)L->n, (long long)L->k, (long long)ft::GEMM_MAX_KRED);

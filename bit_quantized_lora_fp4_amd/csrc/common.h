@@ -195,6 +195,19 @@ __device__ __forceinline__ void buf_load16_lds(bufres r, lds_char* lds, uint32_t
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
                                            (int)off, 0, 0, 0);
 }
+// Nontemporal forms (cache-policy operand NT = 2): for data read or written once, so
+// it streams past the caches instead of displacing what is reused.
+constexpr int CPOL_NT = 2;
+__device__ __forceinline__ void buf_load16_lds_nt(bufres r, lds_char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           (int)off, 0, 0, CPOL_NT);
+}
+__device__ __forceinline__ v4i buf_load16_nt(bufres r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, CPOL_NT);
+}
+__device__ __forceinline__ void buf_store16_nt(bufres r, uint32_t off, v4i v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, CPOL_NT);
+}
 
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }

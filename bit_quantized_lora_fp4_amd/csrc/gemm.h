@@ -80,7 +80,8 @@ struct QuantDownArgs {
 };
 
 hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t stream);
-// Bound on the low-rank width (in 32-wide units) that the fused kernels are built for.
+// The low-rank width in 32-wide units (rank + stab_rank rounded up to a multiple of
+// 32: the fused kernels take 16-wide tiles in pairs), at most QD_MAX_TILES.
 int quant_down_tiles(int r0, int rt);
 constexpr int QD_MAX_TILES = 4;
 int quant_down_splits(int64_t M, int64_t K, int rt);

@@ -19,7 +19,10 @@
 // conversion is the hardware one.
 //
 // Low-rank side, in 16-wide tiles (ranks are multiples of 16, so tiles never mix the
-// two factors and need no padding): forward, tile t's rows of [A; L1] are loaded into
+// two factors). The kernels take the tiles in pairs: a width rank + stab_rank of 16
+// (mod 32) runs with one more tile past the second factor, which reads zeros (its
+// loads are out of range or masked) and whose output columns are not stored. Forward,
+// tile t's rows of [A; L1] are loaded into
 // registers in the same layout as the input (they are the MFMA's first operand);
 // backward, [B | L2] is rt-contiguous, so each wave stages its chunk's rows in LDS
 // with direct-to-LDS loads and reads them transposed (ds_read_b64_tr_b16).
@@ -169,7 +172,8 @@ __device__ __forceinline__ void fetch_u(lds_char* sd, bufres rd0, bufres rd1, in
     const bool first = q < 2 * ta;  // uniform
     const int j0 = first ? 8 * q : 8 * (q - 2 * ta);
     const uint32_t off = first ? (uint32_t)((n * r0 + j0) * 2) : (uint32_t)((n * (rt - r0) + j0) * 2);
-    buf_load16_lds(first ? rd0 : rd1, sd + q * UStage<TP>::QSTRIDE, sel_off(nok, off));
+    // units past the second factor (the padding tile) load zeros, not the next row
+    buf_load16_lds(first ? rd0 : rd1, sd + q * UStage<TP>::QSTRIDE, sel_off(nok && (first || j0 < rt - r0), off));
   }
 }
 
@@ -215,7 +219,6 @@ __device__ __forceinline__ void lds_tr_tiles(const lds_char* sd, int b, int lane
 template <int TP, int NW = QD_WAVES>
 __device__ __forceinline__ void reduce_waves(const v4f (&acc)[4][TP], float* red, const QuantDownArgs& a, int64_t r0,
                                              int split, int S, int wave, int lane, int tid) {
-  constexpr int RT = 16 * TP;
   // acc[g][t] register r of lane l: row 16g + l%16, column 16t + 4(l/16) + r
 #pragma unroll
   for (int g = 0; g < 4; ++g)
@@ -226,7 +229,8 @@ __device__ __forceinline__ void reduce_waves(const v4f (&acc)[4][TP], float* red
   __syncthreads();
   constexpr int NI = 4 * TP * 64;
   const bool partial = S > 1;
-  float* part = a.partials + ((int64_t)split * a.M) * RT;
+  // outputs (and partials) are [M x rt]; a padding tile's columns (>= rt) are dropped
+  float* part = a.partials + ((int64_t)split * a.M) * a.rt;
   for (int e = tid; e < NI; e += 64 * NW) {
     const int l = e & 63, t = (e >> 6) % TP, g = e / (64 * TP);
     v4f s = v4f{0.f, 0.f, 0.f, 0.f};
@@ -237,11 +241,11 @@ __device__ __forceinline__ void reduce_waves(const v4f (&acc)[4][TP], float* red
     }
     const int64_t orow = r0 + 16 * g + (l & 15);
     const int col = 16 * t + 4 * (l >> 4);
-    if (orow < a.M) {
+    if (orow < a.M && col < a.rt) {
       if (partial)
-        *reinterpret_cast<v4f*>(part + orow * RT + col) = s;
+        *reinterpret_cast<v4f*>(part + orow * a.rt + col) = s;
       else
-        *reinterpret_cast<uint2*>(a.low + orow * RT + col) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
+        *reinterpret_cast<uint2*>(a.low + orow * a.rt + col) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
     }
   }
 }
@@ -265,7 +269,7 @@ __device__ __forceinline__ void store_h(const QuantDownArgs& a, const float (&hv
 
 template <typename T, int TP, bool UCOLS, int MODE>
 __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
-  static_assert(TP % 2 == 0, "rank + stab_rank is a multiple of 32");
+  static_assert(TP % 2 == 0, "16-wide low-rank tiles come in pairs");
   constexpr int NS = (MODE == QD_QUANT || MODE == QD_GELU_QUANT) ? QD_STORES : 0;  // stores per chunk
   constexpr int WAVE_LDS = UCOLS ? 2 * UStage<TP>::BYTES : 0;
   constexpr int RED = QD_WAVES * 4 * TP * 4 * 64 * 4;
@@ -664,7 +668,9 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
         } else {
           const int rf = first ? a.r0 : r1;
           const int o = (first ? i : i - a.r0 / 8) * 1024 + 16 * lane;
-          const bool ok = live && (int64_t)o < (a.K - c0) * 2 * rf;
+          // the chunk's rows of a factor are 128 rf bytes; past them (the padding tile)
+          // nothing is loaded
+          const bool ok = live && (int64_t)o < (a.K - c0) * 2 * rf && o < 128 * rf;
           buf_load16_lds(first ? rd0 : rd1, sd + i * 1024, sel_off(ok, (uint32_t)(c0 * 2 * rf + o)));
         }
       }
@@ -741,6 +747,7 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
             const int n = 32 * b + 8 * gq + (s >> 2);
             pitch[u] = (uint32_t)(2 * rf);
             p[u] = lds_addr(sd + (first ? 0 : 128 * a.r0)) + (uint32_t)(n * 2 * rf + 2 * jl);
+            if (16 * (t + u) >= a.rt) p[u] = lds_addr(sd), pitch[u] = 0;  // padding tile: read in range, zeroed below
           }
           v2i w, x, y, z;
           asm volatile(
@@ -754,6 +761,8 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
               : "memory");
           dv[t] = v4i{w.x, w.y, x.x, x.y};
           dv[t + 1] = v4i{y.x, y.y, z.x, z.y};
+          if (16 * t >= a.rt) dv[t] = v4i{0, 0, 0, 0};
+          if (16 * (t + 1) >= a.rt) dv[t + 1] = v4i{0, 0, 0, 0};
         }
       }
       if (b == 1) dma(pf);
@@ -899,7 +908,10 @@ hipError_t launch_staged(const QuantDownArgs& a, int tp, int splits, hipStream_t
 
 }  // namespace
 
-int quant_down_tiles(int r0, int rt) { return (r0 + 31) / 32 + (rt - r0 + 31) / 32; }
+int quant_down_tiles(int r0, int rt) {
+  (void)r0;
+  return (rt + 31) / 32;  // the low-rank width in pairs of 16-wide tiles, padded
+}
 
 int quant_down_splits(int64_t M, int64_t K, int rt) {
   if (rt == 0) return 1;
@@ -919,8 +931,8 @@ size_t quant_down_partial_bytes(int64_t M, int64_t K, int r0, int rt) {
 
 hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t stream) {
   if (a.M == 0) return hipSuccess;
-  if (a.rt % 32 != 0 || a.r0 % 16 != 0 || a.rt > 128 || a.r0 < 0 || a.r0 > a.rt) return hipErrorInvalidValue;
-  const int tp = a.rt / 16;
+  if (a.rt % 16 != 0 || a.r0 % 16 != 0 || a.rt > 128 || a.r0 < 0 || a.r0 > a.rt) return hipErrorInvalidValue;
+  const int tp = 2 * quant_down_tiles(a.r0, a.rt);  // 16-wide tiles, an even count
   const int S = quant_down_splits(a.M, a.K, a.rt);
   if (S > 1 && a.partials == nullptr) return hipErrorInvalidValue;
   hipError_t e;

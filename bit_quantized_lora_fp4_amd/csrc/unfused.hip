@@ -210,7 +210,7 @@ int elementwise_grid(int64_t n8) {
 
 hipError_t launch_up_add(const UpAddArgs& a, bool bwd, bool out_bf16, hipStream_t stream) {
   if (a.M == 0 || a.C == 0) return hipSuccess;
-  if (a.rt <= 0 || a.rt % 32 != 0 || a.rt > 128 || a.r0 % 16 != 0 || a.r0 < 0 || a.r0 > a.rt || a.C % 8 != 0)
+  if (a.rt <= 0 || a.rt % 16 != 0 || a.rt > 128 || a.r0 % 16 != 0 || a.r0 < 0 || a.r0 > a.rt || a.C % 8 != 0)
     return hipErrorInvalidValue;
   // 32-bit buffer offsets
   if ((uint64_t)a.M * a.C * (out_bf16 ? 2 : 4) >= 0xFFFFFF00ull || (uint64_t)(a.M + UA_ROWS) * a.rt * 2 >= 0xFFFFFF00ull)

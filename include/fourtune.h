@@ -76,10 +76,8 @@ typedef struct {
 /* One W4A4G4 linear: Y = Q(X) Q(R)^T + X^ L1^T L2^T + X^ A^T B^T (FourTune §3.1).
  * n = out features, k = in features (multiples of 32). rank = r (LoRA), stab_rank = s;
  * each a multiple of 16 (FT_ERR_SHAPE otherwise); either may be 0 (branch absent).
- * Limits of this build (FT_ERR_UNSUPPORTED beyond them): r + s a multiple of 32 (so
- * r = 16, s = 32 is refused); n, k <= 16384; r + s <= 128 and
- * ceil(r/32) + ceil(s/32) <= 4; (m + 64) * max(n, k) * 4 bytes below 4 GiB (32-bit
- * buffer addressing). */
+ * Limits of this build (FT_ERR_UNSUPPORTED beyond them): n, k <= 16384; r + s <= 128;
+ * (m + 64) * max(n, k) * 4 bytes below 4 GiB (32-bit buffer addressing). */
 typedef struct {
   ft_mx4 r;               /* Q(R), rows = n, cols = k (frozen; from fourtune_quantize) */
   const void *lora_a;     /* A  [rank x k]      bf16, trainable down-projection     */

@@ -107,13 +107,13 @@ def test_new_entry_points_validate_before_launch():
     odd = _fake_linear(r=8, s=24)
     assert L.fourtune_linear_fwd_prec(ctypes.byref(odd), 1, x, abi.FT_BF16, 64, y, abi.FT_BF16, xl, ws, 1 << 30,
                                       None) == 2
-    # multiples of 16 whose sum is 16 (mod 32): valid, not handled by this build
-    for r, s in ((16, 32), (32, 16), (16, 0), (0, 48)):
-        lin48 = _fake_linear(r=r, s=s)
-        assert L.fourtune_linear_fwd(ctypes.byref(lin48), x, abi.FT_BF16, 64, y, abi.FT_BF16, xl, None, ws,
+    # multiples of 16 wider than 128 in all: valid layers the fused kernels are not built for
+    for r, s in ((64, 80), (128, 16), (0, 144)):
+        wide = _fake_linear(r=r, s=s)
+        assert L.fourtune_linear_fwd(ctypes.byref(wide), x, abi.FT_BF16, 64, y, abi.FT_BF16, xl, None, ws,
                                      1 << 30, None) == 6, (r, s)
-        assert "multiple of 32" in abi.fourtune_last_error()
-        assert L.fourtune_mlp_bwd(ctypes.byref(lin48), ctypes.byref(_fake_linear(n=256, k=256)), x, abi.FT_BF16, x,
+        assert "> 128" in abi.fourtune_last_error()
+        assert L.fourtune_mlp_bwd(ctypes.byref(wide), ctypes.byref(_fake_linear(n=256, k=256)), x, abi.FT_BF16, x,
                                   abi.FT_BF16, xl, y, xl, 64, y, abi.FT_BF16, y, y, y, y, None, None, ws, 1 << 30,
                                   None) == 6
     # group quantizer: as the block quantizer

@@ -90,6 +90,14 @@ CASES = [
     (600, 1120, 1088, 16, 16, "bf16"),
     # tiny: a single reduction block (K = 32), a partial first row block, ragged tiles
     (7, 96, 32, 16, 16, "bf16"),
+    # rank + stab_rank = 16 (mod 32): the fused kernels add a padding tile of zeros
+    (300, 544, 384, 16, 32, "bf16"),     # staged kernel, LoRA tile alone in its pair
+    (257, 512, 416, 32, 16, "fp32"),     # register kernel, stabilizer tile alone
+    (200, 320, 288, 16, 0, "bf16"),      # width 16
+    (200, 320, 288, 0, 48, "bf16"),
+    (130, 384, 320, 48, 32, "bf16"),     # width 80: register kernel, six tiles
+    (96, 256, 512, 64, 48, "bf16"),      # width 112: eight tiles
+    (640, 1056, 1056, 16, 32, "bf16"),   # width 48 with split reductions
     (33, 64, 96, 0, 32, "bf16"),
 ]
 

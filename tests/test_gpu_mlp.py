@@ -72,9 +72,11 @@ def _check_all(case, got, out_bf16=False):
 MLP_CASES = [
     # m, d, f, r, s, x_dtype
     (200, 256, 512, 32, 32, "bf16"),
-    (300, 384, 768, 16, 16, "bf16"),    # r % 32 == 16: padded low-rank tiles
+    (300, 384, 768, 16, 16, "bf16"),    # each factor 16 wide
     (96, 256, 512, 32, 0, "fp32"),
     (130, 320, 640, 0, 32, "bf16"),
+    (200, 256, 512, 16, 32, "bf16"),    # rank + stab_rank = 48: a padding tile
+    (130, 320, 640, 48, 32, "bf16"),    # width 80: the register kernel's pass over P^
     # the pass over FC1's output in four column ranges, one range's last chunk pair
     # reaching into the next, the last chunk half past F
     (640, 512, 2080, 32, 32, "bf16"),
