@@ -519,9 +519,10 @@ def hbm_sweep(args):
     partial sum (plus 2 rt / K B per element for the saved XL; taken as the linear's
     forward minus its GEMM), and the MLP's pass over the saved P^ (GELU, Q(H), HL2: P^
     read 2 B + 0.5 B codes per element; taken as the MLP forward minus FC1's linear
-    forward and FC2's GEMM). Graph replays over rotated input sets, median per launch;
-    random bf16 operands (the kernels' time does not depend on the values). Per-kernel
-    durations of the same run come from rocprofv3's kernel trace."""
+    forward and FC2's GEMM). Graph replays over rotated input sets, at least 640 MB of X
+    in rotation so that it streams from HBM rather than the 256 MB Infinity Cache;
+    median per launch; random bf16 operands (the kernels' time does not depend on the
+    values). Per-kernel durations of the same run come from rocprofv3's kernel trace."""
     import torch
     from bit_quantized_lora_fp4_amd import abi
     from synth import workloads as wl
@@ -550,8 +551,8 @@ def hbm_sweep(args):
             n = ls.f if is_mlp else ls.n
             r, s_ = ls.r, ls.s
             rt = r + s_
-            # enough input sets that the rotation streams from HBM, not the 256 MB cache
-            nsets = max(2, -(-(640 << 20) // (m * max(n, k) * 2)))
+            # enough input sets that X streams from HBM in rotation, not from the 256 MB cache
+            nsets = max(2, -(-(640 << 20) // (m * k * 2)))
             sets = []
             for _ in range(nsets):
                 st = dict(x=bf((m, k)), L=lin(n, k, r, s_), y=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
