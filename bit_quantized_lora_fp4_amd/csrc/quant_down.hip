@@ -53,6 +53,9 @@ constexpr int QD_ROWS = 64;    // rows per workgroup (two block rows, four row g
 constexpr int CHUNK = 64;      // columns per wave iteration (two blocks)
 constexpr int QD_STORES = 12;  // stores per chunk: 8 code words + 4 scale bytes
 constexpr int QD_TARGET_WGS = 256;
+#ifndef QD_STAGED_MAX_TP
+#define QD_STAGED_MAX_TP 8
+#endif
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -594,22 +597,28 @@ __device__ __forceinline__ void lds_read16x2(const uint32_t (&ad)[2], v4i (&o)[2
                : "memory");
 }
 
-constexpr int SQ_WAVES = 8;
+// Waves per workgroup: 8 (two per SIMD) up to four low-rank tiles. With six or eight,
+// a wave's accumulators and operand tiles need more than the 256 registers two waves
+// per SIMD leave it (six waves spilled 35-82 registers), so 4 waves run, one per SIMD.
+template <int TP>
+constexpr int sq_waves() { return TP <= 4 ? 8 : 4; }
 // LDS of the staged kernel: per wave one stage (X chunk, low-rank operand chunk) and the
 // code buffer; after the loop the same bytes hold the waves' partial products.
 template <int TP>
 struct SqLds {
+  static constexpr int NW = sq_waves<TP>();
   static constexpr int DB = 2048 * TP;  // low-rank operand per stage: 16 TP x 64 bf16
   static constexpr int STAGE = SQ_XB + DB;
   static constexpr int WAVE = STAGE + SQ_CB;
-  static constexpr int RED = SQ_WAVES * 4 * TP * 4 * 64 * 4;
-  static constexpr int BYTES = SQ_WAVES * WAVE > RED ? SQ_WAVES * WAVE : RED;
+  static constexpr int RED = NW * 4 * TP * 4 * 64 * 4;
+  static constexpr int BYTES = NW * WAVE > RED ? NW * WAVE : RED;
+  static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
 template <int TP, bool UCOLS, int MODE>
-__global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDownArgs a) {
-  static_assert(TP == 0 || TP == 2 || TP == 4, "staged kernel: rank + stab_rank <= 64");
-  constexpr int NW = SQ_WAVES;
+__global__ __launch_bounds__(64 * sq_waves<TP>()) void k_quant_down_lds(const QuantDownArgs a) {
+  static_assert(TP % 2 == 0 && TP <= 8, "staged kernel: rank + stab_rank <= 128");
+  constexpr int NW = sq_waves<TP>();
   using L = SqLds<TP>;
   constexpr bool QUANT = MODE == QD_QUANT || MODE == QD_GELU_QUANT;
   constexpr int NS = QUANT ? 5 : 0;  // stores per pair: 4 code blocks, 1 scale
@@ -732,8 +741,16 @@ __global__ __launch_bounds__(64 * SQ_WAVES) void k_quant_down_lds(const QuantDow
           const int jj = 16 * t + lr;
           ad[t] = lds_addr(sd + jj * 128 + (((4 * b + lq) ^ sq_swz(jj)) << 4));
         }
-        if constexpr (TP == 4) lds_read16x4(ad, dv);
-        else lds_read16x2(ad, dv);
+#pragma unroll
+        for (int t0 = 0; t0 < TP; t0 += 4) {
+          if constexpr (TP % 4 == 0) {
+            lds_read16x4(*reinterpret_cast<const uint32_t(*)[4]>(ad + t0), *reinterpret_cast<v4i(*)[4]>(dv + t0));
+          } else if (t0 + 4 <= TP) {
+            lds_read16x4(*reinterpret_cast<const uint32_t(*)[4]>(ad + t0), *reinterpret_cast<v4i(*)[4]>(dv + t0));
+          } else {
+            lds_read16x2(*reinterpret_cast<const uint32_t(*)[2]>(ad + t0), *reinterpret_cast<v4i(*)[2]>(dv + t0));
+          }
+        }
       } else {
         const int gq = lane >> 4, s = lane & 15;
 #pragma unroll
@@ -896,11 +913,13 @@ hipError_t launch_t(const QuantDownArgs& a, int tp, int splits, hipStream_t stre
 
 template <bool UCOLS, int MODE>
 hipError_t launch_staged(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
-  dim3 grid((unsigned)((a.M + QD_ROWS - 1) / QD_ROWS), (unsigned)splits), block(64 * SQ_WAVES);
+  dim3 grid((unsigned)((a.M + QD_ROWS - 1) / QD_ROWS), (unsigned)splits);
   switch (tp) {
-    case 0: hipLaunchKernelGGL((k_quant_down_lds<0, UCOLS, MODE>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_quant_down_lds<2, UCOLS, MODE>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_quant_down_lds<4, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 0: hipLaunchKernelGGL((k_quant_down_lds<0, UCOLS, MODE>), grid, dim3(64 * sq_waves<0>()), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_quant_down_lds<2, UCOLS, MODE>), grid, dim3(64 * sq_waves<2>()), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_quant_down_lds<4, UCOLS, MODE>), grid, dim3(64 * sq_waves<4>()), 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((k_quant_down_lds<6, UCOLS, MODE>), grid, dim3(64 * sq_waves<6>()), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_quant_down_lds<8, UCOLS, MODE>), grid, dim3(64 * sq_waves<8>()), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -938,7 +957,7 @@ hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t st
   hipError_t e;
   if (a.mode == QD_GELU_QUANT && (!x_bf16 || a.u_cols)) return hipErrorInvalidValue;
   if (a.mode == QD_DOWN && tp == 0) return hipErrorInvalidValue;
-  if (x_bf16 && tp <= 4) {  // the staged kernel (whole-row loads, LDS-staged code stores)
+  if (x_bf16 && tp <= QD_STAGED_MAX_TP) {  // the staged kernel (whole-row loads, LDS-staged code stores)
     if (a.mode == QD_GELU_QUANT) e = launch_staged<false, QD_GELU_QUANT>(a, tp, S, stream);
     else if (a.mode == QD_DOWN) e = a.u_cols ? launch_staged<true, QD_DOWN>(a, tp, S, stream)
                                              : launch_staged<false, QD_DOWN>(a, tp, S, stream);
