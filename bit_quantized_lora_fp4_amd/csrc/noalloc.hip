@@ -5,9 +5,10 @@
 // file-scope device array, one copy per GPU, instead of a caller workspace. Q(X) is an
 // output the caller passes. No allocation, no free, no allocating library call.
 //
-// Size: a split reduction writes S * M * (rank + stab_rank) floats with S * M <= 16384
-// (S column ranges for about one workgroup per CU: S <= 256 / ceil(M / 64)), so
-// rank + stab_rank <= 128 needs at most 8 MiB. Every call on one GPU uses that GPU's
+// Size: a split reduction writes S * M * (rank + stab_rank) floats with S * M <= 36864
+// (S column ranges for about one workgroup per CU, S <= 256 / ceil(M / 64), or three
+// ranges over at most 192 row stripes of 64), so rank + stab_rank <= 128 needs at most
+// 18 MiB; the array holds 24 MiB. Every call on one GPU uses that GPU's
 // array and overwrites what it uses (nothing must start at zero); calls that overlap
 // in time on one GPU race on it.
 #include <hip/hip_runtime.h>
@@ -20,7 +21,7 @@
 
 namespace {
 
-constexpr size_t SCRATCH_BYTES = size_t(8) << 20;
+constexpr size_t SCRATCH_BYTES = size_t(24) << 20;
 constexpr int MAX_DEVICES = 64;
 
 // In host code `scratch` names a host-side stand-in; the device address of each GPU's

@@ -282,9 +282,10 @@ ft_status fourtune_linear_bwd_prec(const ft_linear *L, int prec, const void *dy,
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): no workspace argument, and the library allocates nothing. Q(X) is an
  * output here, so xq_out is required ([m x k] MXFP4); the split reduction's fp32
- * partial sums live in a device array inside the library, 8 MiB per GPU, held until the
- * process ends. Results equal fourtune_linear_fwd's bit for bit. Sizes whose partial
- * sums exceed 8 MiB return FT_ERR_UNSUPPORTED (with rank + stab_rank <= 128 none do).
+ * partial sums live in a device array inside the library, 24 MiB per GPU, held until
+ * the process ends. Results equal fourtune_linear_fwd's bit for bit. Sizes whose
+ * partial sums exceed 24 MiB return FT_ERR_UNSUPPORTED (with rank + stab_rank <= 128
+ * none do: at most 18 MiB).
  * Calls that overlap in time on one GPU (different streams, threads) share the array
  * and race: serialize them. Other arguments and errors as fourtune_linear_fwd. */
 ft_status fourtune_linear_fwd_noalloc(const ft_linear *L, const void *x, ft_dtype x_dt, int64_t m,

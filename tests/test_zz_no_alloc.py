@@ -52,6 +52,18 @@ def test_noalloc_forward_equals_workspace_forward(xdt, out_dtype):
     _pair(d, out_dtype)
 
 
+def test_noalloc_forward_largest_partials():
+    """Long rows at a width above 64 over 144 row stripes take three column ranges: the
+    largest partial sums the array holds for rank + stab_rank <= 128 (14 MiB here),
+    then a smaller call on the same array."""
+    log("noalloc forward: m=9216 n=256 k=8192 r=s=64 (three ranges)")
+    d = wl.random_linear(9216, 256, 8192, 64, 64, seed=44, x_dtype="bf16", dy_dtype="bf16")
+    _pair(d, torch.bfloat16)
+    log("noalloc forward: m=600 n=1120 k=1088 r=32 s=64")
+    d = wl.random_linear(600, 1120, 1088, 32, 64, seed=45, x_dtype="bf16", dy_dtype="bf16")
+    _pair(d, torch.float32)
+
+
 def test_noalloc_argument_errors():
     d = wl.random_linear(64, 256, 256, 16, 16, seed=43)
     L = abi.make_linear(dev(d["R"], "fp32"), dev(d["A"]), dev(d["B"]), dev(d["L1"]), dev(d["L2"]))
