@@ -180,6 +180,17 @@ ft_status check_tensor(const void* p, const char* who, const char* name) {
   return FT_OK;
 }
 
+// An empty batch (m = 0) reads nothing; its LoRA gradients dA [rank x k] and
+// dB [n x rank] are zero and are written as such.
+ft_status zero_lora_grads(const ft_linear* L, float* d_a, float* d_b, void* stream, const char* who) {
+  if (L->rank == 0) return FT_OK;
+  TRY(check_tensor(d_a, who, "d_lora_a"));
+  TRY(check_tensor(d_b, who, "d_lora_b"));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  TRY(hip_check(ft::launch_fill_zero(d_a, L->rank * L->k, st), who));
+  return hip_check(ft::launch_fill_zero(d_b, L->n * L->rank, st), who);
+}
+
 // Workspace: the call's scratch (Q(X) or Q(dY) when the caller does not take them,
 // GB, fp32 partial sums of the split reductions). Nothing in it outlives a call.
 struct FwdLayout {
@@ -408,7 +419,10 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
   TRY(check_linear(L, who));
   REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
   REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
-  if (m == 0) return ok();
+  if (m == 0) {
+    TRY(zero_lora_grads(L, d_lora_a, d_lora_b, stream, who));
+    return ok();
+  }
   TRY(check_m(m, L, who));
   const int64_t rt = L->rank + L->stab_rank;
   TRY(check_tensor(dy, who, "dy"));
@@ -602,7 +616,11 @@ ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const voi
   const char* who = "mlp_bwd";
   TRY(check_mlp(fc1, fc2, m, who));
   REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
-  if (m == 0) return ok();
+  if (m == 0) {
+    TRY(zero_lora_grads(fc1, d_a1, d_b1, stream, who));
+    TRY(zero_lora_grads(fc2, d_a2, d_b2, stream, who));
+    return ok();
+  }
   TRY(check_tensor(dy, who, "dy"));
   TRY(check_tensor(dx, who, "dx"));
   TRY(check_tensor(pre_saved, who, "pre_saved"));
@@ -760,7 +778,10 @@ ft_status fourtune_linear_bwd_unfused(const ft_linear* L, const void* dy, ft_dty
   TRY(check_linear(L, who));
   REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
   REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
-  if (m == 0) return ok();
+  if (m == 0) {
+    TRY(zero_lora_grads(L, d_lora_a, d_lora_b, stream, who));
+    return ok();
+  }
   TRY(check_m(m, L, who));
   REQUIRE(m < (int64_t)65535 * 32, FT_ERR_UNSUPPORTED, "%s: m=%lld too large", who, (long long)m);
   const int64_t rt = L->rank + L->stab_rank;
@@ -825,7 +846,11 @@ ft_status fourtune_mlp_bwd_unfused(const ft_linear* fc1, const ft_linear* fc2, i
                                    void* ws, size_t ws_bytes, void* stream) {
   const char* who = "mlp_bwd_unfused";
   TRY(check_mlp(fc1, fc2, m, who));
-  if (m == 0) return ok();
+  if (m == 0) {
+    TRY(zero_lora_grads(fc1, d_a1, d_b1, stream, who));
+    TRY(zero_lora_grads(fc2, d_a2, d_b2, stream, who));
+    return ok();
+  }
   TRY(check_tensor(pre_saved, who, "pre_saved"));
   TRY(check_tensor(h_saved, who, "h_saved"));
   REQUIRE(ws != nullptr && aligned16(ws), FT_ERR_WORKSPACE, "%s: workspace missing or misaligned", who);
@@ -929,7 +954,10 @@ ft_status fourtune_linear_bwd_prec(const ft_linear* L, int prec, const void* dy,
   TRY(check_linear(L, who));
   REQUIRE(dtype_ok(dy_dt) && dtype_ok(x_dt) && dtype_ok(dx_dt), FT_ERR_DTYPE, "%s: unknown dtype", who);
   REQUIRE(m >= 0, FT_ERR_SHAPE, "%s: m=%lld < 0", who, (long long)m);
-  if (m == 0) return ok();
+  if (m == 0) {
+    TRY(zero_lora_grads(L, d_lora_a, d_lora_b, stream, who));
+    return ok();
+  }
   TRY(check_m(m, L, who));
   REQUIRE(m < (int64_t)65535 * 128, FT_ERR_UNSUPPORTED, "%s: m=%lld too large", who, (long long)m);
   const int64_t rt = L->rank + L->stab_rank;

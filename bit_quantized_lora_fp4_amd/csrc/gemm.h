@@ -119,6 +119,7 @@ struct LoraGradArgs {
 };
 
 hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 
 // 16-bit activation x 4-bit weight GEMM (precision variants W4A16 / G16):
 //   forward : out[M x N] = bf16(act)[M x Kred] deq Q(R)^T + low[M x rt] U^T

@@ -291,6 +291,19 @@ size_t lora_grad_partial_bytes(int64_t M, int64_t K, int64_t N, int r) {
   return (size_t)S * lora_grad_tiles(K, N) * rp * LG_Q * 4;
 }
 
+// Zero fill (the LoRA gradients of an empty batch): a kernel, not a memset node, so the
+// call stays safe to capture in a graph.
+__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.0f;
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream) {
   if (a.r == 0 || a.M == 0) return hipSuccess;
   const int S = lora_grad_splits(a.M, a.K, a.N);

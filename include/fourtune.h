@@ -143,7 +143,10 @@ ft_status fourtune_linear_fwd(const ft_linear *L, const void *x, ft_dtype x_dt, 
  *   d_lora_a  [rank x k] fp32, overwritten (may be NULL only when rank == 0).
  *   d_lora_b  [n x rank] fp32, overwritten (may be NULL only when rank == 0).
  *   gq_out    optional (may be NULL): receives Q(dY) ([m x n] MXFP4).
- *   ws        workspace of fourtune_linear_workspace_bytes(m, L) bytes. */
+ *   ws        workspace of fourtune_linear_workspace_bytes(m, L) bytes.
+ * m = 0 (an empty batch) reads nothing and sets dA and dB to zero; the same holds for
+ * every backward entry point (the MLP's for both linears, the ablation and precision
+ * forms). */
 ft_status fourtune_linear_bwd(const ft_linear *L, const void *dy, ft_dtype dy_dt,
                               const void *x, ft_dtype x_dt, const void *xl_saved, int64_t m,
                               void *dx, ft_dtype dx_dt, float *d_lora_a, float *d_lora_b,

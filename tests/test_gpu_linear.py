@@ -109,6 +109,44 @@ def test_small_cases(m, n, k, r, s, xdt):
     _check_full(d, _run(d))
 
 
+@pytest.mark.parametrize("n,k", [(512, 16384), (16384, 512)])
+def test_longest_reductions(n, k):
+    """The longest reductions this build accepts (16384 elements: the forward's over K,
+    the backward's over N), where the GEMMs stage the most block scales, against the
+    whole oracle."""
+    log(f"linear m=96 n={n} k={k} r=16 s=16 (longest reduction)")
+    d = wl.random_linear(96, n, k, 16, 16, seed=n + 3 * k)
+    _check_full(d, _run(d))
+
+
+def _nan(shape, dtype=torch.float32):
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+def test_empty_batch():
+    """m = 0: nothing is read, the calls succeed, and the LoRA gradients of the empty
+    batch are zero (every backward entry point), not left as they were."""
+    d = wl.random_linear(64, 256, 320, 32, 16, seed=5)
+    L = _gpu_linear(d)
+    n, k, r, rt = 256, 320, 32, 48
+    x, dy = torch.empty((0, k), dtype=torch.bfloat16, device="cuda"), torch.empty((0, n), dtype=torch.bfloat16,
+                                                                                  device="cuda")
+    y, xl, dx = torch.empty((0, n), device="cuda"), torch.empty((0, rt), dtype=torch.bfloat16, device="cuda"), \
+        torch.empty((0, k), device="cuda")
+    ws = abi.workspace(abi.fourtune_linear_workspace_bytes(64, L))
+    abi.fourtune_linear_fwd(L, x, y, xl, ws)
+    for name, call in (
+            ("linear_bwd", lambda da, db: abi.fourtune_linear_bwd(L, dy, x, xl, dx, da, db, ws)),
+            ("linear_bwd_unfused", lambda da, db: abi.fourtune_linear_bwd_unfused(L, dy, x, xl, dx, da, db, ws)),
+            ("linear_bwd_prec W4A4G16", lambda da, db: abi.fourtune_linear_bwd_prec(L, "W4A4G16", dy, x, xl, dx, da,
+                                                                                     db, ws))):
+        da, db = _nan((r, k)), _nan((n, r))
+        call(da, db)
+        torch.cuda.synchronize()
+        log(f"  {name}: m = 0")
+        assert torch.equal(da, torch.zeros_like(da)) and torch.equal(db, torch.zeros_like(db)), name
+
+
 def test_bf16_outputs():
     log("linear bf16 outputs")
     d = wl.random_linear(300, 544, 384, 32, 32, seed=9)

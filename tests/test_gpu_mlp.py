@@ -188,6 +188,35 @@ def test_mlp_exact_epilogue_codes(m):
     _check_all(case, got)
 
 
+def test_mlp_empty_batch():
+    """m = 0: the MLP calls (fused and unfused) succeed and set all four LoRA gradients
+    to zero."""
+    case = wl.random_mlp(64, 256, 512, 32, 16, seed=7)
+    fc1, fc2 = _gpu_lin(case["fc1"]), _gpu_lin(case["fc2"])
+    d, f, r = 256, 512, 32
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    x, dy, y, dx = (torch.empty((0, d), **bf), torch.empty((0, d), **bf), torch.empty((0, d), **bf),
+                    torch.empty((0, d), **bf))
+    xl1, pre, h, hl2 = torch.empty((0, 48), **bf), torch.empty((0, f), **bf), torch.empty((0, f), **bf), \
+        torch.empty((0, 48), **bf)
+    ws = abi.workspace(abi.fourtune_mlp_workspace_bytes(64, fc1, fc2))
+    abi.fourtune_mlp_fwd(fc1, fc2, x, y, xl1, pre, hl2, ws)
+
+    def grads():
+        return [torch.full(sh, float("nan"), device="cuda") for sh in ((r, d), (f, r), (r, f), (d, r))]
+
+    for name in ("mlp_bwd", "mlp_bwd_unfused"):
+        g = grads()
+        if name == "mlp_bwd":
+            abi.fourtune_mlp_bwd(fc1, fc2, dy, x, xl1, pre, hl2, dx, *g, ws)
+        else:
+            abi.fourtune_mlp_bwd_unfused(fc1, fc2, False, dy, x, xl1, pre, h, hl2, dx, *g, ws)
+        torch.cuda.synchronize()
+        log(f"  {name}: m = 0")
+        for t in g:
+            assert torch.equal(t, torch.zeros_like(t)), name
+
+
 def test_mlp_argument_errors():
     case = wl.random_mlp(64, 256, 512, 16, 16, seed=5)
     fc1, fc2 = _gpu_lin(case["fc1"]), _gpu_lin(case["fc2"])
