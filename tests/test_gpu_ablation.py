@@ -41,6 +41,7 @@ LIN_CASES = [
     (96, 256, 320, 0, 32, "bf16", torch.bfloat16),   # no LoRA
     (64, 128, 160, 0, 0, "bf16", torch.float32),     # backbone alone
     (300, 640, 384, 64, 64, "bf16", torch.bfloat16),  # widest low-rank part
+    (160, 384, 352, 16, 32, "bf16", torch.float32),   # rank + stab_rank = 48 (16 mod 32)
 ]
 
 
@@ -110,6 +111,7 @@ MLP_CASES = [
     (256, 512, 1024, 16, 16, "bf16"),
     (130, 256, 512, 32, 32, "bf16"),
     (96, 256, 512, 0, 32, "fp32"),
+    (130, 256, 512, 16, 32, "bf16"),    # rank + stab_rank = 48
 ]
 
 

@@ -28,6 +28,7 @@ CASES = [
     (64, 128, 160, 0, 0, "bf16", torch.float32),      # backbone alone, K % 64 = 32
     (130, 384, 288, 32, 32, "bf16", torch.bfloat16),  # N % 128 != 0, K % 64 = 32
     (300, 640, 384, 64, 64, "bf16", torch.float32),   # widest low-rank part
+    (160, 384, 352, 32, 16, "bf16", torch.float32),   # rank + stab_rank = 48 (16 mod 32)
 ]
 
 
