@@ -6,17 +6,20 @@
 //   backward: G -> Q(G), GB = bf16( bf16(G) [B | L2] )       U rows given (rt-contiguous)
 //
 // HBM-bound: 2 (bf16) or 4 (fp32) bytes read and 0.5 written per input element, plus
-// the small [M x rt] output. The down-projection runs on bf16 MFMA 16x16x32 straight
-// from the registers the quantizer loaded.
+// the small [M x rt] output. The down-projection runs on bf16 MFMA 16x16x32. Two
+// kernels: bf16 input (every shape the library runs, and the MLP's pass over the saved
+// FC1 output with GELU in front) takes the staged kernel further below, which moves
+// every operand through LDS; fp32 input takes the register kernel described here,
+// which multiplies straight from the registers the quantizer loaded.
 //
 // Work split. A workgroup of 4 waves owns 64 rows (two block rows) and one of S
 // contiguous column ranges; wave w walks the range's 64-column chunks w, w+4, ....
 // Register layout of a chunk = the 16x16x32 MFMA operand layout: lane l holds, for
 // row group g (rows 16g + l%16) and column block b (32 columns), the 8 values at
-// columns 32b + 8(l/16) .. +8. One load instruction thus reads 64 contiguous bytes
-// of each of 16 rows (bf16); a 32x32 quantization block is row groups 2h, 2h+1 of
-// column block b, its maximum met over the 64 lanes in VALU exchanges, and the E2M1
-// conversion is the hardware one.
+// columns 32b + 8(l/16) .. +8 (two 16-byte loads per row, rounded to bf16 for the
+// MFMA); a 32x32 quantization block is row groups 2h, 2h+1 of column block b, its
+// maximum met over the 64 lanes in VALU exchanges, and the E2M1 conversion is the
+// hardware one.
 //
 // Low-rank side, in 16-wide tiles (ranks are multiples of 16, so tiles never mix the
 // two factors). The kernels take the tiles in pairs: a width rank + stab_rank of 16
@@ -53,9 +56,6 @@ constexpr int QD_ROWS = 64;    // rows per workgroup (two block rows, four row g
 constexpr int CHUNK = 64;      // columns per wave iteration (two blocks)
 constexpr int QD_STORES = 12;  // stores per chunk: 8 code words + 4 scale bytes
 constexpr int QD_TARGET_WGS = 256;
-#ifndef QD_STAGED_MAX_TP
-#define QD_STAGED_MAX_TP 8
-#endif
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -68,37 +68,9 @@ __device__ __forceinline__ v4f mfma16(v4i a, v4i b, v4f c) {
                                                  0, 0, 0);
 }
 
-template <typename T>
-struct XChunk;
-
-template <>
-struct XChunk<bf16_t> {
-  static constexpr int LOADS = 8;
-  v4i v[4][2];  // [row group][column block]: 8 bf16
-  __device__ void load(bufres r, const uint32_t (&row_off)[4], const bool (&row_ok)[4], int64_t c0, int64_t K,
-                       int lq) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int64_t c = c0 + 32 * b + 8 * lq;
-        v[g][b] = buf_load16(r, sel_off(row_ok[g] && c < K, row_off[g] + (uint32_t)(c * 2)));
-      }
-  }
-  __device__ uint32_t absmax(int g, int b) const {
-    return umax(umax(bf16x2_absmax_bits(v[g][b].x), bf16x2_absmax_bits(v[g][b].y)),
-                umax(bf16x2_absmax_bits(v[g][b].z), bf16x2_absmax_bits(v[g][b].w)));
-  }
-  __device__ uint32_t codes(int g, int b, float scale) const {
-    return cvt8_bf16(v[g][b].x, v[g][b].y, v[g][b].z, v[g][b].w, scale);
-  }
-  __device__ v4i operand(int g, int b) const { return v[g][b]; }
-};
-
 // fp32 values are kept as float vectors: converting whole vectors (never single int
 // lanes bit-cast to float) keeps the compiler's E2M1 conversion operands intact.
-template <>
-struct XChunk<float> {
+struct XChunk {
   static constexpr int LOADS = 16;
   v4f v[4][2][2];
   __device__ void load(bufres r, const uint32_t (&row_off)[4], const bool (&row_ok)[4], int64_t c0, int64_t K,
@@ -253,31 +225,15 @@ __device__ __forceinline__ void reduce_waves(const v4f (&acc)[4][TP], float* red
   }
 }
 
-// The fp32 H = GELU(P^) of a chunk's two column blocks (hv[g][b]: row 16g + lr, columns
-// c0 + 32b + 8lq .. +8), stored to a.hdbg [M x K] for inspection. Chunks past the range
-// have c0 = K: every store is then out of range.
-__device__ __forceinline__ void store_h(const QuantDownArgs& a, const float (&hv)[4][2][8], int64_t r0, int64_t c0,
-                                        int lr, int lq) {
-  const bufres rh = make_buf(a.hdbg, (uint64_t)a.M * a.K * 4);
-#pragma unroll
-  for (int g = 0; g < 4; ++g)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int64_t row = r0 + 16 * g + lr, col = c0 + 32 * b + 8 * lq;
-      const uint32_t off = sel_off(row < a.M && col < a.K, (uint32_t)((row * a.K + col) * 4));
-      buf_store16(rh, off, __builtin_bit_cast(v4i, v4f{hv[g][b][0], hv[g][b][1], hv[g][b][2], hv[g][b][3]}));
-      buf_store16(rh, off + 16, __builtin_bit_cast(v4i, v4f{hv[g][b][4], hv[g][b][5], hv[g][b][6], hv[g][b][7]}));
-    }
-}
-
-template <typename T, int TP, bool UCOLS, int MODE>
+template <int TP, bool UCOLS, int MODE>
 __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   static_assert(TP % 2 == 0, "16-wide low-rank tiles come in pairs");
-  constexpr int NS = (MODE == QD_QUANT || MODE == QD_GELU_QUANT) ? QD_STORES : 0;  // stores per chunk
+  static_assert(MODE == QD_QUANT || MODE == QD_DOWN, "quantize + down-projection, or down-projection alone");
+  constexpr int NS = MODE == QD_QUANT ? QD_STORES : 0;  // stores per chunk
   constexpr int WAVE_LDS = UCOLS ? 2 * UStage<TP>::BYTES : 0;
   constexpr int RED = QD_WAVES * 4 * TP * 4 * 64 * 4;
   constexpr int SMEM = QD_WAVES * WAVE_LDS > RED ? QD_WAVES * WAVE_LDS : RED;
-  constexpr int NX = XChunk<T>::LOADS, NU = UStage<TP>::LOADS;
+  constexpr int NX = XChunk::LOADS, NU = UStage<TP>::LOADS;
   __shared__ __align__(16) char smem_raw[SMEM > 0 ? SMEM : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -291,7 +247,7 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   const int64_t cpitch = a.K >> 1, nkb = a.K >> 5;
   const int ta = a.r0 / 16;  // tiles of the first factor
 
-  const bufres rx = make_buf(a.x, (uint64_t)a.M * a.ldx * sizeof(T));
+  const bufres rx = make_buf(a.x, (uint64_t)a.M * a.ldx * 4);
   const bufres rcodes = make_buf(a.codes, (uint64_t)a.M * cpitch);
   const bufres rscales = make_buf(a.scales, (uint64_t)((a.M + 31) / 32) * nkb);
   uint32_t row_off[4];
@@ -300,7 +256,7 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   for (int g = 0; g < 4; ++g) {
     const int64_t row = r0 + 16 * g + lr;
     row_ok[g] = row < a.M;
-    row_off[g] = (uint32_t)(row * a.ldx * sizeof(T));
+    row_off[g] = (uint32_t)(row * a.ldx * 4);
   }
   const bufres rd0 = make_buf(a.d0, (uint64_t)a.K * a.r0 * 2);
   const bufres rd1 = make_buf(a.d1, (uint64_t)a.K * (a.rt - a.r0) * 2);
@@ -315,66 +271,8 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
   auto cstart = [&](int64_t ch) { return ch < ch1 ? ch * CHUNK : a.K; };
 
   // ---- one chunk: down-projection MFMAs, then the quantization of its four blocks
-  auto work = [&](const XChunk<T>& x, const DChunk<TP>& d, const lds_char* sd, int64_t ch) {
+  auto work = [&](const XChunk& x, const DChunk<TP>& d, const lds_char* sd, int64_t ch) {
     const int64_t c0 = cstart(ch);
-    if constexpr (MODE == QD_GELU_QUANT) {
-      // x is the saved FC1 output P^ (bf16). H = GELU(P^) in fp32 for every element:
-      // Q(H) is decided on these fp32 values, bf16(H) is the down-projection operand
-      float hv[4][2][8];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const uint32_t w[4] = {(uint32_t)x.v[g][b].x, (uint32_t)x.v[g][b].y, (uint32_t)x.v[g][b].z,
-                                 (uint32_t)x.v[g][b].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hv[g][b][2 * e] = gelu_f(bf16_lo(w[e]));
-            hv[g][b][2 * e + 1] = gelu_f(bf16_hi(w[e]));
-          }
-        }
-      if (a.hdbg != nullptr) store_h(a, hv, r0, c0, lr, lq);
-      if constexpr (TP > 0) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          v4i xop[4];
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            xop[g] = v4i{(int)pack_bf16x2(hv[g][b][0], hv[g][b][1]), (int)pack_bf16x2(hv[g][b][2], hv[g][b][3]),
-                         (int)pack_bf16x2(hv[g][b][4], hv[g][b][5]), (int)pack_bf16x2(hv[g][b][6], hv[g][b][7])};
-#pragma unroll
-          for (int t = 0; t < TP; ++t)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) acc[g][t] = mfma16(d.v[t][b], xop[g], acc[g][t]);
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int64_t bc = c0 + 32 * b;
-          const bool bok = bc < a.K;
-          uint32_t m = 0;
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m = umax(m, __builtin_bit_cast(uint32_t, hv[2 * h + q][b][e]) & 0x7FFFFFFFu);
-          const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
-          const float scale = e8m0_to_f32_scale(sb);
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int g = 2 * h + q;
-            const int64_t row = r0 + 16 * g + lr;
-            uint32_t cw = cvt8_f32(hv[g][b], scale);
-            if (sb == 0xFFu) cw = 0;
-            buf_store4(rcodes, sel_off(bok && row_ok[g], (uint32_t)(row * cpitch + ((bc + 8 * lq) >> 1))), cw);
-          }
-          buf_store1(rscales,
-                     sel_off(bok && lane == 0 && r0 + 32 * h < a.M, (uint32_t)((r0 / 32 + h) * nkb + (bc >> 5))),
-                     sb);
-        }
-      return;
-    }
     if constexpr (TP > 0) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -420,11 +318,10 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
         }
   };
 
-  // Operand rows given (forward): a ring of three register sets, below. Operand staged
-  // in LDS (backward): two chunks per trip, each in its own register set and LDS stage;
-  // the second may lie past the range: it then loads zeros and stores nothing, which
-  // keeps the trip branch-free and its memory-operation count fixed.
-  XChunk<T> x0, x1;
+  // Two chunks per trip, each in its own register set (and, operand staged in LDS, its
+  // own LDS stage); the second may lie past the range: it then loads zeros and stores
+  // nothing, which keeps the trip branch-free and its memory-operation count fixed.
+  XChunk x0, x1;
   DChunk<TP> d0, d1;
   int64_t ch = ch0 + wave;
   // The empty asm statements with a memory clobber pin the order of the groups of
@@ -444,65 +341,31 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
     }
   };
   if constexpr (!UCOLS) {
-    // Register sets in a ring: while one chunk is worked on, the next NBUF - 1 chunks'
-    // loads are in flight (one workgroup per CU, so a wave's own loads are all that
-    // covers the memory latency; with one chunk ahead the loop waited about twice as
-    // long per chunk). Three sets where the registers allow (bf16 input, rank + stab
-    // rank <= 64, no GELU values to hold), else two. The wait before each chunk is the
-    // compiler's, counted exactly: the chunks issued after it and one chunk's stores
-    // stay in flight.
-    constexpr int NBUF = (sizeof(T) == 2 && TP <= 4 && MODE != QD_GELU_QUANT) ? 3 : 2;
-    XChunk<T> x2;
-    DChunk<TP> d2;
+    // Two register sets: while one chunk is worked on, the next chunk's loads are in
+    // flight. Both chunks of a trip run; the second may lie past the range (then it
+    // loads zeros and stores nothing). The wait before each chunk is the compiler's,
+    // counted exactly: the chunk issued after it and one chunk's stores stay in flight.
     x0.load(rx, row_off, row_ok, cstart(ch), a.K, lq);
     d0.load(rd0, rd1, ta, cstart(ch), a.K, lr, lq);
     asm volatile("" ::: "memory");
-    if constexpr (NBUF == 3) {
-      x1.load(rx, row_off, row_ok, cstart(ch + QD_WAVES), a.K, lq);
-      d1.load(rd0, rd1, ta, cstart(ch + QD_WAVES), a.K, lr, lq);
-    } else {
-      dummy_stores();
-    }
+    dummy_stores();
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    auto ring = [&](XChunk<T>& xw, DChunk<TP>& dw, XChunk<T>& xl, DChunk<TP>& dl) __attribute__((always_inline)) {
-      // load chunk ch + NBUF - 1 (in wave strides) into (xl, dl), then work on chunk ch
-      xl.load(rx, row_off, row_ok, cstart(ch + (NBUF - 1) * QD_WAVES), a.K, lq);
-      dl.load(rd0, rd1, ta, cstart(ch + (NBUF - 1) * QD_WAVES), a.K, lr, lq);
+    for (; ch < ch1; ch += 2 * QD_WAVES) {
+      x1.load(rx, row_off, row_ok, cstart(ch + QD_WAVES), a.K, lq);
+      d1.load(rd0, rd1, ta, cstart(ch + QD_WAVES), a.K, lr, lq);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      work(xw, dw, nullptr, ch);
+      work(x0, d0, nullptr, ch);
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      ch += QD_WAVES;
-    };
-    if constexpr (NBUF == 3) {
-      while (ch < ch1) {
-        ring(x0, d0, x2, d2);
-        if (ch >= ch1) break;
-        ring(x1, d1, x0, d0);
-        if (ch >= ch1) break;
-        ring(x2, d2, x1, d1);
-      }
-    } else {
-      // two sets: both chunks of a trip run; the second may lie past the range (then it
-      // loads zeros and stores nothing)
-      for (; ch < ch1; ch += 2 * QD_WAVES) {
-        x1.load(rx, row_off, row_ok, cstart(ch + QD_WAVES), a.K, lq);
-        d1.load(rd0, rd1, ta, cstart(ch + QD_WAVES), a.K, lr, lq);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        work(x0, d0, nullptr, ch);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        x0.load(rx, row_off, row_ok, cstart(ch + 2 * QD_WAVES), a.K, lq);
-        d0.load(rd0, rd1, ta, cstart(ch + 2 * QD_WAVES), a.K, lr, lq);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        work(x1, d1, nullptr, ch + QD_WAVES);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      x0.load(rx, row_off, row_ok, cstart(ch + 2 * QD_WAVES), a.K, lq);
+      d0.load(rd0, rd1, ta, cstart(ch + 2 * QD_WAVES), a.K, lr, lq);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      work(x1, d1, nullptr, ch + QD_WAVES);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     lds_char* sd0 = (lds_char*)smem_raw + wave * WAVE_LDS;
@@ -547,15 +410,15 @@ __global__ __launch_bounds__(256) void k_quant_down(const QuantDownArgs a) {
 }
 
 // ---------------------------------------------------------------- staged kernel
-// bf16 input with rank + stab_rank <= 64. The same work split as k_quant_down (64 rows
+// bf16 input, rank + stab_rank <= 128. The same work split as k_quant_down (64 rows
 // per workgroup, one of S column ranges, 64-column chunks, the same MFMA layouts), but
 // every operand reaches LDS by direct-to-LDS loads of whole rows of a chunk and the
-// codes leave through LDS, 64 contiguous bytes per row. Measured on k_quant_down at
-// 4608 x 3072 (rank + stab_rank = 64): without its code stores its loop ran 31% faster,
-// without its X loads or its operand loads about a third faster each, without its
-// quantization arithmetic or its MFMAs about 5%: the time went to the number of memory
-// requests (a load there spans 16 rows x 64 bytes, a code store 16 rows x 16 bytes),
-// not to arithmetic.
+// codes leave through LDS, 64 contiguous bytes per row. Measured on the register kernel
+// with bf16 input (which it then also served) at 4608 x 3072 (rank + stab_rank = 64):
+// without its code stores its loop ran 31% faster, without its X loads or its operand
+// loads about a third faster each, without its quantization arithmetic or its MFMAs
+// about 5%: the time went to the number of memory requests (a load there spans 16 rows
+// x 64 bytes, a code store 16 rows x 16 bytes), not to arithmetic.
 //
 // 8 waves, two per SIMD, each on its own LDS area with no barrier until the final
 // reduction: one stage (one chunk of X and of the low-rank operand) and a code buffer
@@ -897,15 +760,15 @@ __global__ __launch_bounds__(256) void k_sum_partials(const float* __restrict__ 
   *reinterpret_cast<uint2*>(low + 4 * i) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
 }
 
-template <typename T, bool UCOLS, int MODE>
-hipError_t launch_t(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
+template <bool UCOLS, int MODE>
+hipError_t launch_reg(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
   dim3 grid((unsigned)((a.M + QD_ROWS - 1) / QD_ROWS), (unsigned)splits), block(256);
   switch (tp) {
-    case 0: hipLaunchKernelGGL((k_quant_down<T, 0, UCOLS, MODE>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((k_quant_down<T, 2, UCOLS, MODE>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((k_quant_down<T, 4, UCOLS, MODE>), grid, block, 0, stream, a); break;
-    case 6: hipLaunchKernelGGL((k_quant_down<T, 6, UCOLS, MODE>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((k_quant_down<T, 8, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 0: hipLaunchKernelGGL((k_quant_down<0, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((k_quant_down<2, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_quant_down<4, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((k_quant_down<6, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_quant_down<8, UCOLS, MODE>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -964,23 +827,15 @@ hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t st
   hipError_t e;
   if (a.mode == QD_GELU_QUANT && (!x_bf16 || a.u_cols)) return hipErrorInvalidValue;
   if (a.mode == QD_DOWN && tp == 0) return hipErrorInvalidValue;
-  if (x_bf16 && tp <= QD_STAGED_MAX_TP) {  // the staged kernel (whole-row loads, LDS-staged code stores)
+  if (x_bf16) {  // the staged kernel (whole-row loads, LDS-staged code stores)
     if (a.mode == QD_GELU_QUANT) e = launch_staged<false, QD_GELU_QUANT>(a, tp, S, stream);
     else if (a.mode == QD_DOWN) e = a.u_cols ? launch_staged<true, QD_DOWN>(a, tp, S, stream)
                                              : launch_staged<false, QD_DOWN>(a, tp, S, stream);
     else e = a.u_cols ? launch_staged<true, QD_QUANT>(a, tp, S, stream) : launch_staged<false, QD_QUANT>(a, tp, S, stream);
-  } else if (a.mode == QD_GELU_QUANT) {  // the saved P^: Q(GELU(P^)) and [A2; L1_2] down
-    e = launch_t<bf16_t, false, QD_GELU_QUANT>(a, tp, S, stream);
-  } else if (a.mode == QD_DOWN) {  // down-projection alone, either side
-    if (tp == 0) return hipErrorInvalidValue;
-    if (a.u_cols)
-      e = x_bf16 ? launch_t<bf16_t, true, QD_DOWN>(a, tp, S, stream) : launch_t<float, true, QD_DOWN>(a, tp, S, stream);
-    else
-      e = x_bf16 ? launch_t<bf16_t, false, QD_DOWN>(a, tp, S, stream) : launch_t<float, false, QD_DOWN>(a, tp, S, stream);
-  } else if (a.u_cols) {
-    e = x_bf16 ? launch_t<bf16_t, true, QD_QUANT>(a, tp, S, stream) : launch_t<float, true, QD_QUANT>(a, tp, S, stream);
+  } else if (a.mode == QD_DOWN) {  // fp32 input: the register kernel
+    e = a.u_cols ? launch_reg<true, QD_DOWN>(a, tp, S, stream) : launch_reg<false, QD_DOWN>(a, tp, S, stream);
   } else {
-    e = x_bf16 ? launch_t<bf16_t, false, QD_QUANT>(a, tp, S, stream) : launch_t<float, false, QD_QUANT>(a, tp, S, stream);
+    e = a.u_cols ? launch_reg<true, QD_QUANT>(a, tp, S, stream) : launch_reg<false, QD_QUANT>(a, tp, S, stream);
   }
   if (e != hipSuccess || S == 1) return e;
   const int64_t n4 = a.M * a.rt / 4;
