@@ -478,6 +478,67 @@ struct SqLds {
   static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
+// The low-rank operand of column block b (32 columns) of a staged chunk at sd, as the
+// 16x16x32 MFMA's first operand: dv[t] = tile t (16 low-rank columns). Forward layout:
+// [A; L1] rows jj at 128 jj, unit u at slot u ^ sq_swz(jj). Backward layout: the chunk's
+// 64 rows of each factor of [B | L2] as in memory (row pitch 2 r_f bytes; first factor,
+// then second), read transposed with ds_read_b64_tr_b16. A padding tile (16t >= rt)
+// reads in range and is zeroed. The reads wait for themselves (see the kernels' notes
+// on direct-to-LDS loads).
+template <int TP, bool UCOLS>
+__device__ __forceinline__ void read_lowrank(const lds_char* const sd, int b, int lane, int ta, int r0, int r1, int rt,
+                                             v4i (&dv)[TP]) {
+  const int lr = lane & 15, lq = lane >> 4;
+  if constexpr (!UCOLS) {
+    uint32_t ad[TP];
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      const int jj = 16 * t + lr;
+      ad[t] = lds_addr(sd + jj * 128 + (((4 * b + lq) ^ sq_swz(jj)) << 4));
+    }
+#pragma unroll
+    for (int t0 = 0; t0 < TP; t0 += 4) {
+      if constexpr (TP % 4 == 0) {
+        lds_read16x4(*reinterpret_cast<const uint32_t(*)[4]>(ad + t0), *reinterpret_cast<v4i(*)[4]>(dv + t0));
+      } else if (t0 + 4 <= TP) {
+        lds_read16x4(*reinterpret_cast<const uint32_t(*)[4]>(ad + t0), *reinterpret_cast<v4i(*)[4]>(dv + t0));
+      } else {
+        lds_read16x2(*reinterpret_cast<const uint32_t(*)[2]>(ad + t0), *reinterpret_cast<v4i(*)[2]>(dv + t0));
+      }
+    }
+  } else {
+    const int gq = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int t = 0; t < TP; t += 2) {
+      uint32_t p[2], pitch[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const bool first = t + u < ta;
+        const int rf = first ? r0 : r1;
+        const int jl = 16 * (first ? t + u : t + u - ta) + 4 * (s & 3);
+        const int n = 32 * b + 8 * gq + (s >> 2);
+        pitch[u] = (uint32_t)(2 * rf);
+        p[u] = lds_addr(sd + (first ? 0 : 128 * r0)) + (uint32_t)(n * 2 * rf + 2 * jl);
+        if (16 * (t + u) >= rt) p[u] = lds_addr(sd), pitch[u] = 0;  // padding tile: read in range, zeroed below
+      }
+      v2i w, x, y, z;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4\n\t"
+          "ds_read_b64_tr_b16 %1, %5\n\t"
+          "ds_read_b64_tr_b16 %2, %6\n\t"
+          "ds_read_b64_tr_b16 %3, %7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(w), "=&v"(x), "=&v"(y), "=&v"(z)
+          : "v"(p[0]), "v"(p[0] + 4 * pitch[0]), "v"(p[1]), "v"(p[1] + 4 * pitch[1])
+          : "memory");
+      dv[t] = v4i{w.x, w.y, x.x, x.y};
+      dv[t + 1] = v4i{y.x, y.y, z.x, z.y};
+      if (16 * t >= rt) dv[t] = v4i{0, 0, 0, 0};
+      if (16 * (t + 1) >= rt) dv[t + 1] = v4i{0, 0, 0, 0};
+    }
+  }
+}
+
 template <int TP, bool UCOLS, int MODE>
 __global__ __launch_bounds__(64 * sq_waves<TP>()) void k_quant_down_lds(const QuantDownArgs a) {
   static_assert(TP % 2 == 0 && TP <= 8, "staged kernel: rank + stab_rank <= 128");
@@ -596,55 +657,7 @@ __global__ __launch_bounds__(64 * sq_waves<TP>()) void k_quant_down_lds(const Qu
     }
     if constexpr (TP > 0) {
       v4i dv[TP];
-      const lds_char* const sd = st + SQ_XB;
-      if constexpr (!UCOLS) {
-        uint32_t ad[TP];
-#pragma unroll
-        for (int t = 0; t < TP; ++t) {
-          const int jj = 16 * t + lr;
-          ad[t] = lds_addr(sd + jj * 128 + (((4 * b + lq) ^ sq_swz(jj)) << 4));
-        }
-#pragma unroll
-        for (int t0 = 0; t0 < TP; t0 += 4) {
-          if constexpr (TP % 4 == 0) {
-            lds_read16x4(*reinterpret_cast<const uint32_t(*)[4]>(ad + t0), *reinterpret_cast<v4i(*)[4]>(dv + t0));
-          } else if (t0 + 4 <= TP) {
-            lds_read16x4(*reinterpret_cast<const uint32_t(*)[4]>(ad + t0), *reinterpret_cast<v4i(*)[4]>(dv + t0));
-          } else {
-            lds_read16x2(*reinterpret_cast<const uint32_t(*)[2]>(ad + t0), *reinterpret_cast<v4i(*)[2]>(dv + t0));
-          }
-        }
-      } else {
-        const int gq = lane >> 4, s = lane & 15;
-#pragma unroll
-        for (int t = 0; t < TP; t += 2) {
-          uint32_t p[2], pitch[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bool first = t + u < ta;
-            const int rf = first ? a.r0 : r1;
-            const int jl = 16 * (first ? t + u : t + u - ta) + 4 * (s & 3);
-            const int n = 32 * b + 8 * gq + (s >> 2);
-            pitch[u] = (uint32_t)(2 * rf);
-            p[u] = lds_addr(sd + (first ? 0 : 128 * a.r0)) + (uint32_t)(n * 2 * rf + 2 * jl);
-            if (16 * (t + u) >= a.rt) p[u] = lds_addr(sd), pitch[u] = 0;  // padding tile: read in range, zeroed below
-          }
-          v2i w, x, y, z;
-          asm volatile(
-              "ds_read_b64_tr_b16 %0, %4\n\t"
-              "ds_read_b64_tr_b16 %1, %5\n\t"
-              "ds_read_b64_tr_b16 %2, %6\n\t"
-              "ds_read_b64_tr_b16 %3, %7\n\t"
-              "s_waitcnt lgkmcnt(0)"
-              : "=&v"(w), "=&v"(x), "=&v"(y), "=&v"(z)
-              : "v"(p[0]), "v"(p[0] + 4 * pitch[0]), "v"(p[1]), "v"(p[1] + 4 * pitch[1])
-              : "memory");
-          dv[t] = v4i{w.x, w.y, x.x, x.y};
-          dv[t + 1] = v4i{y.x, y.y, z.x, z.y};
-          if (16 * t >= a.rt) dv[t] = v4i{0, 0, 0, 0};
-          if (16 * (t + 1) >= a.rt) dv[t + 1] = v4i{0, 0, 0, 0};
-        }
-      }
+      read_lowrank<TP, UCOLS>(st + SQ_XB, b, lane, ta, a.r0, r1, a.rt, dv);
       if (b == 1) dma(pf);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -748,6 +761,296 @@ __global__ __launch_bounds__(64 * sq_waves<TP>()) void k_quant_down_lds(const Qu
   }
 }
 
+// ---------------------------------------------------------------- row-split kernel
+// bf16 input with a wide low-rank operand (rank + stab_rank above 64) over many rows.
+// The staged kernel above gives each wave its own chunk and its own copy of that chunk's
+// low-rank operand: at rank + stab_rank = 128 a wave's stage is 8 KB of X and 16 KB of
+// operand, one stage per wave fits, and a CU has about 32 KB of X in flight. At
+// 32760 x 5120 that ran at 38% of HBM while the quantizer alone reached 73%: with a
+// latency of ~3 us under full load, 256 CUs x 32 KB in flight is ~2.8 TB/s.
+//
+// Here a workgroup of 4 waves owns 128 rows (wave w: rows 32w .. 32w+31, one block row)
+// and works on one chunk at a time, all waves together. The chunk's X rows and its
+// low-rank operand pass through a ring of four stages shared by the workgroup: each wave
+// loads its own 32 X rows and a quarter of the operand, so three chunks (48 KB of X) are
+// in flight and the operand is fetched once per 128 rows instead of once per 64. Each wave multiplies its rows by the whole
+// operand and keeps its [32 x rt] sums to the end: no cross-wave reduction. The price is
+// one workgroup barrier per chunk.
+//
+// Waits. Every wave issues, per chunk, its loads of the chunk STAGES - 1 ahead (at
+// out-of-range offsets past the column range), and after every second chunk the pair's
+// code and scale stores, so the count of its own operations issued after a chunk's
+// loads is fixed by the chunk's parity; the wait before a chunk leaves exactly those in
+// flight, and the barrier after it makes every wave's loads of the chunk visible. The
+// loads into a stage are issued only after the barrier that follows every wave's last
+// read of it. LDS accesses in the loop are asm that waits for itself, as in the staged
+// kernel.
+constexpr int QR_ROWS = 128;
+constexpr int QR_WAVES = 4;
+#ifndef QR_MAX_STAGES
+#define QR_MAX_STAGES 4
+#endif
+#ifndef QR_MIN_M
+#define QR_MIN_M 4096
+#endif
+#ifndef QR_MIN_RT
+#define QR_MIN_RT 64
+#endif
+template <int TP>
+struct QrLds {
+  static constexpr int XB = QR_ROWS * 128;  // X per stage: 128 rows x 64 bf16
+  static constexpr int DB = 2048 * TP;      // low-rank operand per stage (either layout)
+  static constexpr int STAGE = XB + DB;
+  static constexpr int CB = 32 * 64;        // per wave: codes of a chunk pair, 32 rows x 64 bytes
+  // QR_MAX_STAGES stages where 160 KB holds them (eight tiles hold four); deeper rings
+  // for narrower operands measured slower (at 4608 x 3072, width 64: 16.5 us with six
+  // stages, 14.5 with four)
+  static constexpr int FIT = (160 * 1024 - QR_WAVES * CB) / STAGE;
+  static constexpr int STAGES = FIT < QR_MAX_STAGES ? FIT : QR_MAX_STAGES;
+  static constexpr int BYTES = STAGES * STAGE + QR_WAVES * CB;
+  static_assert(STAGES >= 3 && BYTES <= 160 * 1024, "LDS");
+};
+
+template <int TP, bool UCOLS, int MODE>
+__global__ __launch_bounds__(64 * QR_WAVES) void k_quant_down_rows(const QuantDownArgs a) {
+  static_assert(TP % 2 == 0 && TP >= 2 && TP <= 8, "row-split kernel: 2 .. 8 low-rank tiles");
+  using L = QrLds<TP>;
+  constexpr bool QUANT = MODE == QD_QUANT || MODE == QD_GELU_QUANT;
+  constexpr int NS = QUANT ? 3 : 0;    // stores per chunk pair: 2 code pieces, 1 scale byte
+  constexpr int NL = 4 + TP / 2;       // direct-to-LDS loads per chunk and wave
+  constexpr int AHEAD = L::STAGES - 1;  // chunks in flight
+  // operations a wave issues after a chunk's loads until that chunk is worked on
+  constexpr int WAIT_EVEN = (AHEAD - 1) * NL + NS * ((AHEAD + 1) / 2);
+  constexpr int WAIT_ODD = (AHEAD - 1) * NL + NS * (AHEAD / 2);
+  static_assert(WAIT_EVEN < 64 && WAIT_ODD < 64, "vmcnt field");
+  __shared__ __align__(16) char smem_raw[L::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lq = lane >> 4;
+  const int wrow = 32 * wave;  // this wave's first row in the stripe
+  const int64_t r0 = (int64_t)blockIdx.x * QR_ROWS;
+  const int rows_left = (int)min<int64_t>(a.M - r0, QR_ROWS);
+  const int split = blockIdx.y, S = gridDim.y;
+  const int64_t nchunks = (a.K + CHUNK - 1) / CHUNK;
+  const int64_t per = (nchunks + S - 1) / S;
+  const int64_t ch0 = split * per, ch1 = min(nchunks, ch0 + per);
+  const int trips = (int)((max<int64_t>(ch1 - ch0, 0) + 1) / 2);
+  const int64_t cpitch = a.K >> 1, nkb = a.K >> 5;
+  const int ta = a.r0 / 16, r1 = a.rt - a.r0;
+
+  const bufres rx = make_buf(a.x, (uint64_t)a.M * a.ldx * 2);
+  const bufres rcodes = make_buf(a.codes, (uint64_t)a.M * cpitch);
+  const bufres rscales = make_buf(a.scales, (uint64_t)((a.M + 31) / 32) * nkb);
+  const bufres rd0 = make_buf(a.d0, (uint64_t)a.K * a.r0 * 2);
+  const bufres rd1 = make_buf(a.d1, (uint64_t)a.K * r1 * 2);
+
+  lds_char* const stages = (lds_char*)smem_raw;
+  lds_char* const cbuf = stages + L::STAGES * L::STAGE + wave * L::CB;
+
+  v4f acc[2][TP];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int t = 0; t < TP; ++t) acc[g][t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // loads of local chunk j (column chunk ch0 + j) into stage j % L::STAGES: this wave's
+  // 32 X rows (4 x 1 KB) and its quarter of the operand (TP/2 x 1 KB)
+  auto dma = [&](int j) __attribute__((always_inline)) {
+    const int64_t c = ch0 + j;
+    const bool live = c < ch1;
+    const int64_t c0 = c * CHUNK;
+    lds_char* const st = stages + (j % L::STAGES) * L::STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wrow + 8 * i + (lane >> 3);
+      const int64_t col = c0 + 8 * ((lane & 7) ^ sq_swz(row));
+      buf_load16_lds(rx, st + (4 * wave + i) * 1024,
+                     sel_off(live & (row < rows_left) & (col < a.K), (uint32_t)(((r0 + row) * a.ldx + col) * 2)));
+    }
+    lds_char* const sd = st + L::XB;
+#pragma unroll
+    for (int k = 0; k < TP / 2; ++k) {
+      const int i = wave * (TP / 2) + k;  // 1 KB piece i of the 2 TP
+      const bool first = 8 * i < a.r0;
+      if constexpr (!UCOLS) {
+        const int jj = 8 * i + (lane >> 3);
+        const int64_t jr = first ? jj : jj - a.r0;
+        const int64_t col = c0 + 8 * ((lane & 7) ^ sq_swz(jj));
+        buf_load16_lds(first ? rd0 : rd1, sd + i * 1024, sel_off(live & (col < a.K), (uint32_t)((jr * a.K + col) * 2)));
+      } else {
+        const int rf = first ? a.r0 : r1;
+        const int o = (first ? i : i - a.r0 / 8) * 1024 + 16 * lane;
+        // a factor's rows of the chunk are 128 rf bytes; past them (the padding tile)
+        // nothing is loaded
+        const bool ok = live & ((int64_t)o < (a.K - c0) * 2 * rf) & (o < 128 * rf);
+        buf_load16_lds(first ? rd0 : rd1, sd + i * 1024, sel_off(ok, (uint32_t)(c0 * 2 * rf + o)));
+      }
+    }
+  };
+  auto dummy_stores = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      uint32_t off = BUF_OOB + 16u * i;  // distinct, opaque: none may be merged away
+      asm volatile("" : "+v"(off));
+      buf_store4(rcodes, off, 0u);
+    }
+  };
+
+  uint32_t sbs = 0;  // the pair's four scale bytes of this wave's block row
+  // local chunk j, position i (0, 1) in its pair
+  auto work = [&](int i, int j) __attribute__((always_inline)) {
+    const lds_char* const st = stages + (j % L::STAGES) * L::STAGE;
+    const int64_t cc = ch0 + j;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      v4i xv[2];  // rows wrow + 16g + l%16, columns 32b + 8(l/16) .. +8
+      {
+        uint32_t ad[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const int row = wrow + 16 * g + lr;
+          ad[g] = lds_addr(st + row * 128 + (((4 * b + lq) ^ sq_swz(row)) << 4));
+        }
+        lds_read16x2(ad, xv);
+      }
+      float hv[2][8];
+      if constexpr (MODE == QD_GELU_QUANT) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const uint32_t ws[4] = {(uint32_t)xv[g].x, (uint32_t)xv[g].y, (uint32_t)xv[g].z, (uint32_t)xv[g].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            hv[g][2 * e] = gelu_f(bf16_lo(ws[e]));
+            hv[g][2 * e + 1] = gelu_f(bf16_hi(ws[e]));
+          }
+        }
+        // optional export of the fp32 H that Q(H) quantizes: extra operations ahead of
+        // the pair's stores only make the waits stricter
+        if (a.hdbg != nullptr) {
+          const bufres rh = make_buf(a.hdbg, (uint64_t)a.M * a.K * 4);
+          const int64_t col = cc * CHUNK + 32 * b + 8 * lq;
+#pragma unroll
+          for (int g = 0; g < 2; ++g) {
+            const int64_t row = r0 + wrow + 16 * g + lr;
+            const uint32_t off = sel_off(cc < ch1 && row < a.M && col < a.K, (uint32_t)((row * a.K + col) * 4));
+            buf_store16(rh, off, __builtin_bit_cast(v4i, v4f{hv[g][0], hv[g][1], hv[g][2], hv[g][3]}));
+            buf_store16(rh, off + 16, __builtin_bit_cast(v4i, v4f{hv[g][4], hv[g][5], hv[g][6], hv[g][7]}));
+          }
+        }
+      }
+      v4i dv[TP];
+      read_lowrank<TP, UCOLS>(st + L::XB, b, lane, ta, a.r0, r1, a.rt, dv);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        v4i xop;
+        if constexpr (MODE == QD_GELU_QUANT)
+          xop = v4i{(int)pack_bf16x2(hv[g][0], hv[g][1]), (int)pack_bf16x2(hv[g][2], hv[g][3]),
+                    (int)pack_bf16x2(hv[g][4], hv[g][5]), (int)pack_bf16x2(hv[g][6], hv[g][7])};
+        else
+          xop = xv[g];
+#pragma unroll
+        for (int t = 0; t < TP; ++t) acc[g][t] = mfma16(dv[t], xop, acc[g][t]);
+      }
+      if constexpr (QUANT) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          if constexpr (MODE == QD_GELU_QUANT) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = umax(m, __builtin_bit_cast(uint32_t, hv[g][e]) & 0x7FFFFFFFu);
+          } else {
+            const v4i w = xv[g];
+            m = umax(m, umax(umax(bf16x2_absmax_bits(w.x), bf16x2_absmax_bits(w.y)),
+                             umax(bf16x2_absmax_bits(w.z), bf16x2_absmax_bits(w.w))));
+          }
+        }
+        const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
+        const float scale = e8m0_to_f32_scale(sb);
+        sbs |= sb << (8 * (2 * i + b));
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          uint32_t cw;
+          if constexpr (MODE == QD_GELU_QUANT) {
+            cw = cvt8_f32(hv[g], scale);
+          } else {
+            const v4i w = xv[g];
+            cw = cvt8_bf16(w.x, w.y, w.z, w.w, scale);
+          }
+          if (sb == 0xFFu) cw = 0;
+          const int row = 16 * g + lr;
+          const uint32_t ad = lds_addr(cbuf + row * 64 + (((2 * i + b) ^ ((row >> 2) & 3)) << 4) + 4 * lq);
+          asm volatile("ds_write_b32 %0, %1" ::"v"(ad), "v"(cw) : "memory");
+        }
+      }
+    }
+  };
+
+  // codes of trip k's two chunks: 64 contiguous bytes of each of the wave's 32 rows
+  auto store_pair = [&](int k) __attribute__((always_inline)) {
+    const int64_t pc = (ch0 + 2 * k) * CHUNK;
+    uint32_t ad[2];
+    v4i cv[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = 16 * q + (lane >> 2), u = lane & 3;
+      ad[q] = lds_addr(cbuf + row * 64 + ((u ^ ((row >> 2) & 3)) << 4));
+    }
+    lds_read16x2(ad, cv);
+    const int u = lane & 3;
+    const bool uok = ch0 + 2 * k + (u >> 1) < ch1 && pc + 32 * u < a.K;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = wrow + 16 * q + (lane >> 2);
+      buf_store16(rcodes, sel_off(uok && row < rows_left, (uint32_t)((r0 + row) * cpitch + (pc >> 1) + 16 * u)),
+                  cv[q]);
+    }
+    const uint32_t v = (sbs >> (8 * u)) & 0xFFu;
+    const bool sok = lane < 4 && r0 + wrow < a.M && ch0 + 2 * k + (u >> 1) < ch1 && pc + 32 * u < a.K;
+    buf_store1(rscales, sel_off(sok, (uint32_t)(((r0 + wrow) / 32) * nkb + (pc >> 5) + u)), v);
+  };
+
+  // the issue sequence of the AHEAD chunks before the first: as if issued by chunks
+  // -AHEAD .. -1, the odd ones of which end with a pair's stores
+#pragma unroll
+  for (int j = 0; j < AHEAD; ++j) {
+    dma(j);
+    if constexpr (NS > 0)
+      if (((j - AHEAD) & 1) != 0) dummy_stores();
+  }
+  for (int k = 0; k < trips; ++k) {
+    sbs = 0;
+    wait_vmcnt<WAIT_EVEN>();  // this wave's loads of chunk 2k landed
+    asm volatile("s_barrier" ::: "memory");  // and every wave's; stage of chunk 2k - 1 read
+    dma(2 * k + AHEAD);
+    work(0, 2 * k);
+    wait_vmcnt<WAIT_ODD>();
+    asm volatile("s_barrier" ::: "memory");
+    dma(2 * k + 1 + AHEAD);
+    work(1, 2 * k + 1);
+    if constexpr (NS > 0) store_pair(k);
+  }
+  wait_vmcnt<0>();  // no direct-to-LDS load may outlive the workgroup
+
+  // this wave's [32 x rt] result: bf16 once, or this range's fp32 partial
+  // acc[g][t] register r of lane l: row wrow + 16g + l%16, column 16t + 4(l/16) + r
+  float* part = a.partials + ((int64_t)split * a.M) * a.rt;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      const int64_t orow = r0 + wrow + 16 * g + lr;
+      const int col = 16 * t + 4 * lq;
+      if (orow < a.M && col < a.rt) {
+        const v4f v = acc[g][t];
+        if (S > 1)
+          *reinterpret_cast<v4f*>(part + orow * a.rt + col) = v;
+        else
+          *reinterpret_cast<uint2*>(a.low + orow * a.rt + col) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+      }
+    }
+}
+
 // Sum of the S column-range partials of each row, in range order, rounded once to
 // bf16.
 __global__ __launch_bounds__(256) void k_sum_partials(const float* __restrict__ partials, int S, int64_t n4,
@@ -775,6 +1078,23 @@ hipError_t launch_reg(const QuantDownArgs& a, int tp, int splits, hipStream_t st
 }
 
 template <bool UCOLS, int MODE>
+hipError_t launch_rows(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
+  dim3 grid((unsigned)((a.M + QR_ROWS - 1) / QR_ROWS), (unsigned)splits), block(64 * QR_WAVES);
+  switch (tp) {
+    case 2: hipLaunchKernelGGL((k_quant_down_rows<2, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((k_quant_down_rows<4, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((k_quant_down_rows<6, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_quant_down_rows<8, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// The row-split kernel serves widths above 64 (six or eight 16-wide tiles) when the rows
+// are many; below that the staged kernel's 64-row stripes give more workgroups.
+bool use_rows_kernel(int64_t M, int rt) { return rt > QR_MIN_RT && M >= QR_MIN_M; }
+
+template <bool UCOLS, int MODE>
 hipError_t launch_staged(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
   dim3 grid((unsigned)((a.M + QD_ROWS - 1) / QD_ROWS), (unsigned)splits);
   switch (tp) {
@@ -797,6 +1117,13 @@ int quant_down_tiles(int r0, int rt) {
 
 int quant_down_splits(int64_t M, int64_t K, int rt) {
   if (rt == 0) return 1;
+  if (use_rows_kernel(M, rt)) {  // 128-row stripes; about one workgroup per CU
+    const int64_t stripes = (M + QR_ROWS - 1) / QR_ROWS;
+    const int64_t nchunks = (K + CHUNK - 1) / CHUNK;
+    int64_t s = QD_TARGET_WGS / stripes;
+    if (s > nchunks / 8) s = nchunks / 8;  // at least 8 chunks per range
+    return (int)(s < 1 ? 1 : s);
+  }
   const int64_t stripes = (M + QD_ROWS - 1) / QD_ROWS;
   const int64_t nchunks = (K + CHUNK - 1) / CHUNK;
   int64_t s = QD_TARGET_WGS / (stripes > 0 ? stripes : 1);  // about one workgroup per CU
@@ -827,7 +1154,12 @@ hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t st
   hipError_t e;
   if (a.mode == QD_GELU_QUANT && (!x_bf16 || a.u_cols)) return hipErrorInvalidValue;
   if (a.mode == QD_DOWN && tp == 0) return hipErrorInvalidValue;
-  if (x_bf16) {  // the staged kernel (whole-row loads, LDS-staged code stores)
+  if (x_bf16 && use_rows_kernel(a.M, a.rt)) {  // wide operand, many rows: the row-split kernel
+    if (a.mode == QD_GELU_QUANT) e = launch_rows<false, QD_GELU_QUANT>(a, tp, S, stream);
+    else if (a.mode == QD_DOWN) e = a.u_cols ? launch_rows<true, QD_DOWN>(a, tp, S, stream)
+                                             : launch_rows<false, QD_DOWN>(a, tp, S, stream);
+    else e = a.u_cols ? launch_rows<true, QD_QUANT>(a, tp, S, stream) : launch_rows<false, QD_QUANT>(a, tp, S, stream);
+  } else if (x_bf16) {  // the staged kernel (whole-row loads, LDS-staged code stores)
     if (a.mode == QD_GELU_QUANT) e = launch_staged<false, QD_GELU_QUANT>(a, tp, S, stream);
     else if (a.mode == QD_DOWN) e = a.u_cols ? launch_staged<true, QD_DOWN>(a, tp, S, stream)
                                              : launch_staged<false, QD_DOWN>(a, tp, S, stream);

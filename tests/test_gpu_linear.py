@@ -109,6 +109,25 @@ def test_small_cases(m, n, k, r, s, xdt):
     _check_full(d, _run(d))
 
 
+ROW_SPLIT_CASES = [
+    # m >= 4096 with rank + stab_rank above 64: the row-split quantize + down-projection
+    # (128 rows per workgroup, a ring of stages shared by its four waves)
+    (16400, 256, 416, 64, 32, "bf16"),   # width 96; last stripe 16 rows, last chunk half past K
+    (16384, 256, 1056, 64, 64, "bf16"),  # width 128 in two column ranges (128 stripes)
+    (16416, 320, 288, 48, 32, "bf16"),   # width 80: a padding tile
+    (16390, 256, 256, 64, 48, "bf16"),   # width 112: a padding tile, a 6-row last stripe
+    (16384, 256, 1024, 64, 64, "fp32"),  # fp32 input: the register kernel, two ranges
+    (4100, 256, 2080, 64, 32, "bf16"),   # 33 stripes in 4 column ranges of 9 chunks (odd)
+]
+
+
+@pytest.mark.parametrize("m,n,k,r,s,xdt", ROW_SPLIT_CASES)
+def test_row_split_cases(m, n, k, r, s, xdt):
+    log(f"linear m={m} n={n} k={k} r={r} s={s} x={xdt} (row-split range)")
+    d = wl.random_linear(m, n, k, r, s, seed=m + n + k + 1, x_dtype=xdt, dy_dtype=xdt)
+    _check_full(d, _run(d))
+
+
 @pytest.mark.parametrize("n,k", [(512, 16384), (16384, 512)])
 def test_longest_reductions(n, k):
     """The longest reductions this build accepts (16384 elements: the forward's over K,

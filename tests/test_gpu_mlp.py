@@ -80,6 +80,11 @@ MLP_CASES = [
     # the pass over FC1's output in four column ranges, one range's last chunk pair
     # reaching into the next, the last chunk half past F
     (640, 512, 2080, 32, 32, "bf16"),
+    # many rows at widths above 64: the row-split kernel's pass over P^ (GELU, Q(H))
+    # and its down-projection of dP, with a ragged last stripe
+    (16400, 128, 256, 64, 64, "bf16"),
+    (16390, 128, 288, 48, 32, "bf16"),  # width 80: a padding tile
+    (4160, 256, 2080, 64, 32, "bf16"),  # pass over P^ in column ranges, 33 stripes
 ]
 
 
