@@ -5,10 +5,11 @@
 // file-scope device array, one copy per GPU, instead of a caller workspace. Q(X) is an
 // output the caller passes. No allocation, no free, no allocating library call.
 //
-// Size: a split reduction writes S * M * (rank + stab_rank) floats with S * M <= 36864
-// (S column ranges for about one workgroup per CU, S <= 256 / ceil(M / 64), or three
-// ranges over at most 192 row stripes of 64), so rank + stab_rank <= 128 needs at most
-// 18 MiB; the array holds 24 MiB. Every call on one GPU uses that GPU's
+// Size: a split reduction writes S * M * (rank + stab_rank) floats. S column ranges are
+// chosen for about one workgroup per CU (S <= 256 / ceil(M / 64) with 64-row stripes,
+// S <= 256 / ceil(M / 128) with the 128-row stripes of the wide-operand kernel), so
+// S * M <= 32768 whenever S > 1 and rank + stab_rank <= 128 needs at most 16 MiB; the
+// array holds 24 MiB. Every call on one GPU uses that GPU's
 // array and overwrites what it uses (nothing must start at zero); calls that overlap
 // in time on one GPU race on it.
 #include <hip/hip_runtime.h>

@@ -1124,13 +1124,6 @@ int quant_down_splits(int64_t M, int64_t K, int rt) {
   const int64_t nchunks = (K + CHUNK - 1) / CHUNK;
   int64_t s = QD_TARGET_WGS / (stripes > 0 ? stripes : 1);  // about one workgroup per CU
   const int64_t maxs = nchunks / (2 * QD_WAVES);             // at least two chunks per wave
-  // Widths above 64 run 4-wave workgroups, one per CU. When those leave over a quarter
-  // of the CUs idle in a single round and the rows are long, three column ranges (two
-  // rounds, at least 8 chunks per wave) finish sooner than one: at 9216 x 12288, rt 96,
-  // the MLP's pass over P^ went from 156-164 to 110 us. Short rows lose (9216 x 3072:
-  // 37-40 us with one range, 41 with three): the partial sums cost more than the idle
-  // CUs.
-  if (rt > 64 && s == 1 && stripes * 4 <= QD_TARGET_WGS * 3 && K >= 8192) s = 3;
   if (s > maxs) s = maxs;
   return (int)(s < 1 ? 1 : s);
 }

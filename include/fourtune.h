@@ -288,7 +288,7 @@ ft_status fourtune_linear_bwd_prec(const ft_linear *L, int prec, const void *dy,
  * partial sums live in a device array inside the library, 24 MiB per GPU, held until
  * the process ends. Results equal fourtune_linear_fwd's bit for bit. Sizes whose
  * partial sums exceed 24 MiB return FT_ERR_UNSUPPORTED (with rank + stab_rank <= 128
- * none do: at most 18 MiB).
+ * none do: at most 16 MiB).
  * Calls that overlap in time on one GPU (different streams, threads) share the array
  * and race: serialize them. Other arguments and errors as fourtune_linear_fwd. */
 ft_status fourtune_linear_fwd_noalloc(const ft_linear *L, const void *x, ft_dtype x_dt, int64_t m,

@@ -53,9 +53,9 @@ def test_noalloc_forward_equals_workspace_forward(xdt, out_dtype):
 
 
 def test_noalloc_forward_largest_partials():
-    """Long rows at a width above 64 over 144 row stripes take three column ranges: the
-    largest partial sums the array holds for rank + stab_rank <= 128 (14 MiB here),
-    then a smaller call on the same array."""
+    """Width 128 over 72 row stripes of 128 rows takes three column ranges: partial
+    sums near the largest the array holds for rank + stab_rank <= 128 (14 MiB here, at
+    most 16 MiB), then a smaller call on the same array."""
     log("noalloc forward: m=9216 n=256 k=8192 r=s=64 (three ranges)")
     d = wl.random_linear(9216, 256, 8192, 64, 64, seed=44, x_dtype="bf16", dy_dtype="bf16")
     _pair(d, torch.bfloat16)
