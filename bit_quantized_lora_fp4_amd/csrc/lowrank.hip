@@ -269,15 +269,21 @@ int lora_grad_tiles(int64_t K, int64_t N) {
   return (int)((K + LG_Q - 1) / LG_Q + (N + LG_Q - 1) / LG_Q);
 }
 
-// Row ranges per tile: enough for about 192 workgroups. Fewer ranges mean fewer fp32
-// partials (written here, read again by k_lora_reduce) and longer-lived waves; at
-// 4608 x 3072 (96 tiles) 2 ranges ran the fused linear ~1.5% faster than 6 (a 512
-// target), and 1 range (96 workgroups) was slower.
+// Row ranges per tile: enough for about 192 workgroups while the tiles fit one round
+// of the 256 CUs. Fewer ranges mean fewer fp32 partials (written here, read again by
+// k_lora_reduce) and longer-lived waves; at 4608 x 3072 (96 tiles) 2 ranges ran the
+// fused linear ~1.5% faster than 6 (a 512 target), and 1 range (96 workgroups) was
+// slower. Past 256 tiles one range per tile leaves the CUs unevenly loaded (at 32760
+// rows, 320 tiles: 64 CUs hold two workgroups and finish last, 441 us at 3.05 TB/s);
+// about 1024 workgroups even that out (4 ranges: 315 us + 6.6 us of reduction, against
+// 351 with 2 ranges and 331 with 7), and 240 or 192 tiles gained nothing from them.
 constexpr int LG_TARGET_WGS = 192;
+constexpr int LG_TARGET_WGS_WIDE = 1024;
 
 int lora_grad_splits(int64_t M, int64_t K, int64_t N) {
   const int tiles = lora_grad_tiles(K, N);
-  int64_t s = (LG_TARGET_WGS + tiles - 1) / tiles;
+  const int64_t target = tiles > 256 ? LG_TARGET_WGS_WIDE : LG_TARGET_WGS;
+  int64_t s = (target + tiles - 1) / tiles;
   const int64_t maxs = M / (2 * LG_WAVES * LG_SLAB);  // at least two slabs per wave
   if (s > maxs) s = maxs;
   if (s > 64) s = 64;

@@ -99,6 +99,8 @@ CASES = [
     (96, 256, 512, 64, 48, "bf16"),      # width 112: eight tiles
     (640, 1056, 1056, 16, 32, "bf16"),   # width 48 with split reductions
     (33, 64, 96, 0, 32, "bf16"),
+    # more than 256 LoRA-gradient tiles (N = 16384): four row ranges and their reduction
+    (1024, 16384, 512, 32, 32, "bf16"),
 ]
 
 
