@@ -218,6 +218,7 @@ struct BwdLayout {
   uint8_t* gq_scales;
   ft::bf16_t* GB;
   float* partials;  // quant_down's, then lora_grad's (the kernels run in turn)
+  ft::bf16_t* ut;   // [B | L2] transposed, where the wide-operand kernel runs (else null)
   size_t bytes;
 };
 
@@ -233,6 +234,8 @@ BwdLayout bwd_layout(void* ws, int64_t m, const ft_linear* L, bool need_gq) {
   const size_t pq = ft::quant_down_partial_bytes(m, L->n, (int)L->rank, rt);
   const size_t pl = ft::lora_grad_partial_bytes(m, L->k, L->n, (int)L->rank);
   b.partials = c.take<float>(pq > pl ? pq : pl);
+  const size_t ub = ft::quant_down_ut_bytes(m, L->n, rt);
+  b.ut = ub ? c.take<ft::bf16_t>(ub) : nullptr;
   b.bytes = c.used;
   return b;
 }
@@ -293,7 +296,7 @@ ft_status run_gemm_bwd(const ft_linear* L, const uint8_t* gq_codes, const uint8_
 // [B | L2] (output side).
 ft_status run_quant_down(int mode, const ft_linear* L, bool down, const void* x, bool x_bf16, int64_t m,
                          int64_t cols, uint8_t* codes, uint8_t* scales, void* low, float* partials,
-                         hipStream_t st, const char* what, float* hdbg = nullptr) {
+                         hipStream_t st, const char* what, float* hdbg = nullptr, ft::bf16_t* ut = nullptr) {
   ft::QuantDownArgs qd{};
   qd.mode = mode;
   qd.x = x; qd.M = m; qd.K = cols; qd.ldx = cols;
@@ -304,6 +307,7 @@ ft_status run_quant_down(int mode, const ft_linear* L, bool down, const void* x,
   qd.low = static_cast<ft::bf16_t*>(low);
   qd.partials = partials;
   qd.hdbg = hdbg;
+  qd.ut = ut;
   return hip_check(ft::launch_quant_down(qd, x_bf16, st), what);
 }
 
@@ -451,6 +455,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
   qd.r0 = (int)L->rank; qd.rt = (int)rt; qd.u_cols = true;
   qd.low = lay.GB;
   qd.partials = lay.partials;
+  qd.ut = lay.ut;
   TRY(hip_check(ft::launch_quant_down(qd, dy_dt == FT_BF16, st), "linear_bwd quant_down"));
 
   TRY(run_gemm_bwd(L, gq_codes, gq_scales, lay.GB, m, dx, dx_dt, st));
@@ -527,6 +532,7 @@ struct MlpBwdLayout {
   uint8_t *gq_codes, *gq_scales, *dpq_codes, *dpq_scales;
   ft::bf16_t *gb2, *gb1, *dp;
   float* partials;
+  ft::bf16_t* ut;  // fc2's, then fc1's [B | L2] transposed (else null)
   size_t bytes;
 };
 
@@ -548,6 +554,9 @@ MlpBwdLayout mlp_bwd_layout(void* ws, int64_t m, const ft_linear* fc1, const ft_
   p = std::max(p, lg_partials(m, fc2));
   p = std::max(p, lg_partials(m, fc1));
   b.partials = c.take<float>(p);
+  const size_t ub = std::max(ft::quant_down_ut_bytes(m, dout, (int)(fc2->rank + fc2->stab_rank)),
+                             ft::quant_down_ut_bytes(m, fdim, (int)(fc1->rank + fc1->stab_rank)));
+  b.ut = ub ? c.take<ft::bf16_t>(ub) : nullptr;
   b.bytes = c.used;
   return b;
 }
@@ -647,7 +656,7 @@ ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const voi
   uint8_t* dpq_scales = dpq_out ? dpq_out->scales : lay.dpq_scales;
 
   TRY(run_quant_down(ft::QD_QUANT, fc2, false, dy, dy_dt == FT_BF16, m, dout, lay.gq_codes, lay.gq_scales,
-                     lay.gb2, lay.partials, st, "mlp_bwd quant_down(dY)"));
+                     lay.gb2, lay.partials, st, "mlp_bwd quant_down(dY)", nullptr, lay.ut));
   Epi e;
   e.kind = ft::GEMM_EPI_DGELU_Q; e.pre = pre_saved; e.q_codes = dpq_codes; e.q_scales = dpq_scales;
   e.dbg = dp_debug;
@@ -656,7 +665,7 @@ ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const voi
                     lay.partials, st, "mlp_bwd lora_grad(fc2)"));
   if (fc1->rank + fc1->stab_rank > 0)
     TRY(run_quant_down(ft::QD_DOWN, fc1, false, lay.dp, true, m, fdim, nullptr, nullptr, lay.gb1, lay.partials, st,
-                       "mlp_bwd down(dP)"));
+                       "mlp_bwd down(dP)", nullptr, lay.ut));
   TRY(run_gemm_bwd(fc1, dpq_codes, dpq_scales, lay.gb1, m, dx, dx_dt, st));
   TRY(run_lora_grad(fc1, m, lay.gb1, x, x_dt == FT_BF16, false, xl1_saved, lay.dp, true, d_a1, d_b1,
                     lay.partials, st, "mlp_bwd lora_grad(fc1)"));

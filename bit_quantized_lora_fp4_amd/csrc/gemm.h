@@ -77,9 +77,15 @@ struct QuantDownArgs {
   bf16_t* low;
   float* partials;
   float* hdbg;  // QD_GELU_QUANT only, optional
+  // u_cols only, optional: scratch of quant_down_ut_bytes(M, K, rt) bytes. Where the
+  // wide-operand kernel runs, [B | L2] is first transposed into it ([rt x K], the
+  // forward's layout), which that kernel reads with fewer LDS instructions.
+  bf16_t* ut;
 };
 
 hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t stream);
+// Bytes of the optional u_cols scratch (0 where it would not be used).
+size_t quant_down_ut_bytes(int64_t M, int64_t K, int rt);
 // The low-rank width in 32-wide units (rank + stab_rank rounded up to a multiple of
 // 32: the fused kernels take 16-wide tiles in pairs), at most QD_MAX_TILES.
 int quant_down_tiles(int r0, int rt);

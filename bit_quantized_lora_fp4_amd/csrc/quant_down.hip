@@ -769,6 +769,9 @@ __global__ __launch_bounds__(64 * sq_waves<TP>()) void k_quant_down_lds(const Qu
 // 32760 x 5120 that ran at 38% of HBM while the quantizer alone reached 73%: with a
 // latency of ~3 us under full load, 256 CUs x 32 KB in flight is ~2.8 TB/s.
 //
+// The low-rank operand is read K-contiguous, as [A; L1] is stored; the backward's
+// [B | L2] is transposed into that layout first (launch_quant_down).
+//
 // Here a workgroup of 4 waves owns 128 rows (wave w: rows 32w .. 32w+31, one block row)
 // and works on one chunk at a time, all waves together. The chunk's X rows and its
 // low-rank operand pass through a ring of four stages shared by the workgroup: each wave
@@ -808,7 +811,7 @@ struct QrLds {
   static_assert(STAGES >= 3 && BYTES <= 160 * 1024, "LDS");
 };
 
-template <int TP, bool UCOLS, int MODE>
+template <int TP, int MODE>
 __global__ __launch_bounds__(64 * QR_WAVES) void k_quant_down_rows(const QuantDownArgs a) {
   static_assert(TP % 2 == 0 && TP >= 2 && TP <= 8, "row-split kernel: 2 .. 8 low-rank tiles (launched with 6, 8)");
   using L = QrLds<TP>;
@@ -870,19 +873,10 @@ __global__ __launch_bounds__(64 * QR_WAVES) void k_quant_down_rows(const QuantDo
     for (int k = 0; k < TP / 2; ++k) {
       const int i = wave * (TP / 2) + k;  // 1 KB piece i of the 2 TP
       const bool first = 8 * i < a.r0;
-      if constexpr (!UCOLS) {
-        const int jj = 8 * i + (lane >> 3);
-        const int64_t jr = first ? jj : jj - a.r0;
-        const int64_t col = c0 + 8 * ((lane & 7) ^ sq_swz(jj));
-        buf_load16_lds(first ? rd0 : rd1, sd + i * 1024, sel_off(live & (col < a.K), (uint32_t)((jr * a.K + col) * 2)));
-      } else {
-        const int rf = first ? a.r0 : r1;
-        const int o = (first ? i : i - a.r0 / 8) * 1024 + 16 * lane;
-        // a factor's rows of the chunk are 128 rf bytes; past them (the padding tile)
-        // nothing is loaded
-        const bool ok = live & ((int64_t)o < (a.K - c0) * 2 * rf) & (o < 128 * rf);
-        buf_load16_lds(first ? rd0 : rd1, sd + i * 1024, sel_off(ok, (uint32_t)(c0 * 2 * rf + o)));
-      }
+      const int jj = 8 * i + (lane >> 3);
+      const int64_t jr = first ? jj : jj - a.r0;
+      const int64_t col = c0 + 8 * ((lane & 7) ^ sq_swz(jj));
+      buf_load16_lds(first ? rd0 : rd1, sd + i * 1024, sel_off(live & (col < a.K), (uint32_t)((jr * a.K + col) * 2)));
     }
   };
   auto dummy_stores = [&]() __attribute__((always_inline)) {
@@ -937,7 +931,7 @@ __global__ __launch_bounds__(64 * QR_WAVES) void k_quant_down_rows(const QuantDo
         }
       }
       v4i dv[TP];
-      read_lowrank<TP, UCOLS>(st + L::XB, b, lane, ta, a.r0, r1, a.rt, dv);
+      read_lowrank<TP, false>(st + L::XB, b, lane, ta, a.r0, r1, a.rt, dv);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         v4i xop;
@@ -1060,6 +1054,41 @@ __global__ __launch_bounds__(256) void k_sum_partials(const float* __restrict__ 
   *reinterpret_cast<uint2*>(low + 4 * i) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
 }
 
+// [B | L2] (K rows: r0 values of the first factor, then r1 of the second, each factor
+// row-major) transposed into ut [rt x K]: row j < r0 is column j of the first factor,
+// row r0 + j column j of the second. A thread moves one 8 x 8 block: eight 16-byte
+// loads (8 rows of the input, 8 consecutive columns each), the transpose in registers,
+// eight 16-byte stores; consecutive threads take consecutive column blocks, so each
+// input row is read in whole. Ranks are multiples of 16 and K of 32, so a block never
+// straddles the two factors or the end of a row.
+__device__ __forceinline__ uint32_t pick16(uint32_t lo_src, uint32_t hi_src, bool high) {
+  return high ? (lo_src >> 16) | (hi_src & 0xFFFF0000u) : (lo_src & 0xFFFFu) | (hi_src << 16);
+}
+__global__ __launch_bounds__(256) void k_transpose_u(const bf16_t* __restrict__ d0, const bf16_t* __restrict__ d1,
+                                                     int r0, int r1, int64_t K, bf16_t* __restrict__ ut) {
+  const int jbs = (r0 + r1) / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= (K / 8) * jbs) return;
+  const int jb = (int)(t % jbs);
+  const int64_t n0 = 8 * (t / jbs);
+  const int j0 = 8 * jb;
+  const bool first = j0 < r0;
+  const bf16_t* src = first ? d0 + j0 : d1 + (j0 - r0);
+  const int64_t ld = first ? r0 : r1;
+  v4i a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = *reinterpret_cast<const v4i*>(src + (n0 + i) * ld);
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int w = jj >> 1;
+    const bool high = jj & 1;
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pick16((uint32_t)a[2 * q][w], (uint32_t)a[2 * q + 1][w], high);
+    *reinterpret_cast<v4i*>(ut + (int64_t)(j0 + jj) * K + n0) = v4i{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+  }
+}
+
 template <bool UCOLS, int MODE>
 hipError_t launch_reg(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
   dim3 grid((unsigned)((a.M + QD_ROWS - 1) / QD_ROWS), (unsigned)splits), block(256);
@@ -1074,12 +1103,12 @@ hipError_t launch_reg(const QuantDownArgs& a, int tp, int splits, hipStream_t st
   return hipGetLastError();
 }
 
-template <bool UCOLS, int MODE>
+template <int MODE>
 hipError_t launch_rows(const QuantDownArgs& a, int tp, int splits, hipStream_t stream) {
   dim3 grid((unsigned)((a.M + QR_ROWS - 1) / QR_ROWS), (unsigned)splits), block(64 * QR_WAVES);
   switch (tp) {
-    case 6: hipLaunchKernelGGL((k_quant_down_rows<6, UCOLS, MODE>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((k_quant_down_rows<8, UCOLS, MODE>), grid, block, 0, stream, a); break;
+    case 6: hipLaunchKernelGGL((k_quant_down_rows<6, MODE>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((k_quant_down_rows<8, MODE>), grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1128,6 +1157,10 @@ int quant_down_splits(int64_t M, int64_t K, int rt) {
   return (int)(s < 1 ? 1 : s);
 }
 
+size_t quant_down_ut_bytes(int64_t M, int64_t K, int rt) {
+  return use_rows_kernel(M, rt) ? (size_t)rt * K * 2 : 0;
+}
+
 size_t quant_down_partial_bytes(int64_t M, int64_t K, int r0, int rt) {
   (void)r0;
   const int S = quant_down_splits(M, K, rt);
@@ -1143,11 +1176,26 @@ hipError_t launch_quant_down(const QuantDownArgs& a, bool x_bf16, hipStream_t st
   hipError_t e;
   if (a.mode == QD_GELU_QUANT && (!x_bf16 || a.u_cols)) return hipErrorInvalidValue;
   if (a.mode == QD_DOWN && tp == 0) return hipErrorInvalidValue;
-  if (x_bf16 && use_rows_kernel(a.M, a.rt)) {  // wide operand, many rows: the row-split kernel
-    if (a.mode == QD_GELU_QUANT) e = launch_rows<false, QD_GELU_QUANT>(a, tp, S, stream);
-    else if (a.mode == QD_DOWN) e = a.u_cols ? launch_rows<true, QD_DOWN>(a, tp, S, stream)
-                                             : launch_rows<false, QD_DOWN>(a, tp, S, stream);
-    else e = a.u_cols ? launch_rows<true, QD_QUANT>(a, tp, S, stream) : launch_rows<false, QD_QUANT>(a, tp, S, stream);
+  const bool rows = x_bf16 && use_rows_kernel(a.M, a.rt) && (!a.u_cols || a.ut != nullptr);
+  if (rows && a.u_cols) {
+    // the backward's [B | L2] transposed once into the forward's layout, the only one the
+    // row-split kernel reads (at 32760 x 15360, width 128, the kernel took 317 us on the
+    // transposed operand against 425 us for a variant reading [B | L2] as stored, whose
+    // transposed LDS reads issue twice the instructions); without the scratch the call
+    // takes the staged kernel
+    const int64_t blocks = a.K / 8 * (a.rt / 8);  // 8 x 8 blocks, one per thread
+    hipLaunchKernelGGL(k_transpose_u, dim3((unsigned)((blocks + 255) / 256)), dim3(256), 0, stream, a.d0, a.d1, a.r0,
+                       a.rt - a.r0, a.K, a.ut);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    QuantDownArgs b = a;
+    b.u_cols = false;
+    b.d0 = a.ut;
+    b.d1 = a.ut + (int64_t)a.r0 * a.K;
+    e = a.mode == QD_DOWN ? launch_rows<QD_DOWN>(b, tp, S, stream) : launch_rows<QD_QUANT>(b, tp, S, stream);
+  } else if (rows) {  // wide operand, many rows: the row-split kernel
+    if (a.mode == QD_GELU_QUANT) e = launch_rows<QD_GELU_QUANT>(a, tp, S, stream);
+    else if (a.mode == QD_DOWN) e = launch_rows<QD_DOWN>(a, tp, S, stream);
+    else e = launch_rows<QD_QUANT>(a, tp, S, stream);
   } else if (x_bf16) {  // the staged kernel (whole-row loads, LDS-staged code stores)
     if (a.mode == QD_GELU_QUANT) e = launch_staged<false, QD_GELU_QUANT>(a, tp, S, stream);
     else if (a.mode == QD_DOWN) e = a.u_cols ? launch_staged<true, QD_DOWN>(a, tp, S, stream)

@@ -42,6 +42,9 @@ LIN_CASES = [
     (64, 128, 160, 0, 0, "bf16", torch.float32),     # backbone alone
     (300, 640, 384, 64, 64, "bf16", torch.bfloat16),  # widest low-rank part
     (160, 384, 352, 16, 32, "bf16", torch.float32),   # rank + stab_rank = 48 (16 mod 32)
+    # width 96 from 4096 rows: the forward's down-projection on the row-split kernel, the
+    # backward's ([B | L2] as stored, no transposed copy) on the staged kernel
+    (4100, 256, 320, 64, 32, "bf16", torch.bfloat16),
 ]
 
 
