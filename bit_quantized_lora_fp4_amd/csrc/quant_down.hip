@@ -772,65 +772,74 @@ __global__ __launch_bounds__(64 * sq_waves<TP>()) void k_quant_down_lds(const Qu
 // The low-rank operand is read K-contiguous, as [A; L1] is stored; the backward's
 // [B | L2] is transposed into that layout first (launch_quant_down).
 //
-// Here a workgroup of 4 waves owns 128 rows (wave w: rows 32w .. 32w+31, one block row)
-// and works on one chunk at a time, all waves together. The chunk's X rows and its
-// low-rank operand pass through a ring of four stages shared by the workgroup: each wave
-// loads its own 32 X rows and a quarter of the operand, so three chunks (48 KB of X) are
-// in flight and the operand is fetched once per 128 rows instead of once per 64. Each
-// wave multiplies its rows by the whole operand and keeps its [32 x rt] sums to the end:
-// no cross-wave reduction. The price is one workgroup barrier per chunk. At 32760 x 5120
-// it moves 52% of 8 TB/s; X in registers instead of LDS, with more chunks in flight,
-// was slower there: the limit is not the depth of the load pipeline.
+// Here a workgroup owns 128 rows and works on one chunk at a time, all waves together.
+// The chunk's X rows and its low-rank operand pass through a ring of four stages shared
+// by the workgroup, so three chunks (48 KB of X) are in flight and the operand is
+// fetched once per 128 rows instead of once per 64. 8 waves, two per SIMD: waves w and
+// w + 4 own rows 32(w%4) .. +32 (one block row), wave w the first 32-column block of
+// every chunk and w + 4 the second, so each still quantizes whole 32x32 blocks, and each
+// keeps its partial [32 x rt] sums to the end, where the pair's two meet once in LDS.
+// With one wave per SIMD (4 waves of 32 rows, both blocks each) the vector work (GELU,
+// block maxima, conversions) did not overlap the loads: the MLP's pass over P^ at
+// 32760 x 13824 took 414 us against 370 with two. Each chunk costs one workgroup
+// barrier. At 32760 x 5120 the kernel moves 52-54% of 8 TB/s; X in registers instead of
+// LDS, with more chunks in flight, was slower there: the limit is not the depth of the
+// load pipeline.
 //
-// Waits. Every wave issues, per chunk, its loads of the chunk STAGES - 1 ahead (at
-// out-of-range offsets past the column range), and after every second chunk the pair's
-// code and scale stores, so the count of its own operations issued after a chunk's
-// loads is fixed by the chunk's parity; the wait before a chunk leaves exactly those in
-// flight, and the barrier after it makes every wave's loads of the chunk visible. The
-// loads into a stage are issued only after the barrier that follows every wave's last
-// read of it. LDS accesses in the loop are asm that waits for itself, as in the staged
-// kernel.
+// Waits. Every wave issues, per chunk, its loads of the chunk three ahead (at
+// out-of-range offsets past the column range), and after every even chunk's loads the
+// stores of the pair before (its codes are complete once both waves of the row group
+// have passed the barrier; the code buffer alternates between pairs). The count of a
+// wave's own operations issued after a chunk's loads is thus fixed by the chunk's
+// parity; the wait before a chunk leaves exactly those in flight, and the barrier after
+// it makes every wave's loads of the chunk visible. The loads into a stage are issued
+// only after the barrier that follows every wave's last read of it. LDS accesses in the
+// loop are asm that waits for itself, as in the staged kernel.
 constexpr int QR_ROWS = 128;
-constexpr int QR_WAVES = 4;
-#ifndef QR_MAX_STAGES
-#define QR_MAX_STAGES 4
-#endif
+constexpr int QR_WAVES = 8;   // two per SIMD
+constexpr int QR_STAGES = 4;
 #ifndef QR_MIN_M
 #define QR_MIN_M 4096
 #endif
 template <int TP>
 struct QrLds {
   static constexpr int XB = QR_ROWS * 128;  // X per stage: 128 rows x 64 bf16
-  static constexpr int DB = 2048 * TP;      // low-rank operand per stage: 16 TP rows x 64 bf16
+  static constexpr int DB = 16 * 1024;      // low-rank operand per stage: up to 128 rows x 64 bf16
   static constexpr int STAGE = XB + DB;
-  static constexpr int CB = 32 * 64;        // per wave: codes of a chunk pair, 32 rows x 64 bytes
-  // QR_MAX_STAGES stages where 160 KB holds them (eight tiles hold four); deeper rings
-  // for narrower operands measured slower (at 4608 x 3072, width 64: 16.5 us with six
-  // stages, 14.5 with four)
-  static constexpr int FIT = (160 * 1024 - QR_WAVES * CB) / STAGE;
-  static constexpr int STAGES = FIT < QR_MAX_STAGES ? FIT : QR_MAX_STAGES;
-  static constexpr int BYTES = STAGES * STAGE + QR_WAVES * CB;
-  static_assert(STAGES >= 3 && BYTES <= 160 * 1024, "LDS");
+  static constexpr int CB = 32 * 64;        // codes of a chunk pair for 32 rows, 64 bytes each
+  // stages, then the code buffers: [pair parity][row group of waves]
+  static constexpr int BYTES = QR_STAGES * STAGE + 2 * 4 * CB;
+  static constexpr int RED = 4 * 2 * TP * 64 * 16;  // the second column block's partial sums
+  static_assert(BYTES <= 160 * 1024 && RED <= QR_STAGES * STAGE, "LDS");
 };
+
+__device__ __forceinline__ v4i lds_read16(uint32_t ad) {
+  v4i o;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(o) : "v"(ad) : "memory");
+  return o;
+}
 
 template <int TP, int MODE>
 __global__ __launch_bounds__(64 * QR_WAVES) void k_quant_down_rows(const QuantDownArgs a) {
   static_assert(TP % 2 == 0 && TP >= 2 && TP <= 8, "row-split kernel: 2 .. 8 low-rank tiles (launched with 6, 8)");
   using L = QrLds<TP>;
   constexpr bool QUANT = MODE == QD_QUANT || MODE == QD_GELU_QUANT;
-  constexpr int NS = QUANT ? 3 : 0;    // stores per chunk pair: 2 code pieces, 1 scale byte
-  constexpr int NL = 4 + TP / 2;       // direct-to-LDS loads per chunk and wave
-  constexpr int AHEAD = L::STAGES - 1;  // chunks in flight
-  // operations a wave issues after a chunk's loads until that chunk is worked on
-  constexpr int WAIT_EVEN = (AHEAD - 1) * NL + NS * ((AHEAD + 1) / 2);
-  constexpr int WAIT_ODD = (AHEAD - 1) * NL + NS * (AHEAD / 2);
+  constexpr int NS = QUANT ? 2 : 0;     // stores per chunk pair and wave: a code piece, the scale bytes
+  constexpr int NL = 4;                 // direct-to-LDS loads per chunk and wave: 2 of X, 2 of the operand
+  constexpr int AHEAD = QR_STAGES - 1;  // chunks in flight
+  // operations a wave issues after a chunk's loads until that chunk is worked on: the
+  // loads of the AHEAD - 1 chunks after it, and the stores of the even chunks among the
+  // AHEAD from the chunk's issue on (a pair's stores follow its next chunk's loads)
+  constexpr int WAIT_EVEN = (AHEAD - 1) * NL + NS * (AHEAD / 2);
+  constexpr int WAIT_ODD = (AHEAD - 1) * NL + NS * ((AHEAD + 1) / 2);
   static_assert(WAIT_EVEN < 64 && WAIT_ODD < 64, "vmcnt field");
   __shared__ __align__(16) char smem_raw[L::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = wave & 3, bsel = wave >> 2;  // row group of 32, column block of each chunk
   const int lr = lane & 15, lq = lane >> 4;
-  const int wrow = 32 * wave;  // this wave's first row in the stripe
+  const int wrow = 32 * rw;  // this wave's first row in the stripe
   const int64_t r0 = (int64_t)blockIdx.x * QR_ROWS;
   const int rows_left = (int)min<int64_t>(a.M - r0, QR_ROWS);
   const int split = blockIdx.y, S = gridDim.y;
@@ -848,7 +857,8 @@ __global__ __launch_bounds__(64 * QR_WAVES) void k_quant_down_rows(const QuantDo
   const bufres rd1 = make_buf(a.d1, (uint64_t)a.K * r1 * 2);
 
   lds_char* const stages = (lds_char*)smem_raw;
-  lds_char* const cbuf = stages + L::STAGES * L::STAGE + wave * L::CB;
+  lds_char* const codes_lds = stages + QR_STAGES * L::STAGE;
+  auto cbuf = [&](int pair) { return codes_lds + ((pair & 1) * 4 + rw) * L::CB; };
 
   v4f acc[2][TP];
 #pragma unroll
@@ -856,24 +866,26 @@ __global__ __launch_bounds__(64 * QR_WAVES) void k_quant_down_rows(const QuantDo
 #pragma unroll
     for (int t = 0; t < TP; ++t) acc[g][t] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // loads of local chunk j (column chunk ch0 + j) into stage j % L::STAGES: this wave's
-  // 32 X rows (4 x 1 KB) and its quarter of the operand (TP/2 x 1 KB)
+  // loads of local chunk j (column chunk ch0 + j) into stage j % QR_STAGES, pieces
+  // 2 wave and 2 wave + 1 of each: X rows 16 wave .. +16, and operand rows 16 wave .. +16
+  // (rows past 16 TP, and past the second factor, read as zeros and are never used)
   auto dma = [&](int j) __attribute__((always_inline)) {
     const int64_t c = ch0 + j;
     const bool live = c < ch1;
     const int64_t c0 = c * CHUNK;
-    lds_char* const st = stages + (j % L::STAGES) * L::STAGE;
+    lds_char* const st = stages + (j % QR_STAGES) * L::STAGE;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wrow + 8 * i + (lane >> 3);
+    for (int q = 0; q < 2; ++q) {
+      const int i = 2 * wave + q;
+      const int row = 8 * i + (lane >> 3);
       const int64_t col = c0 + 8 * ((lane & 7) ^ sq_swz(row));
-      buf_load16_lds(rx, st + (4 * wave + i) * 1024,
+      buf_load16_lds(rx, st + i * 1024,
                      sel_off(live & (row < rows_left) & (col < a.K), (uint32_t)(((r0 + row) * a.ldx + col) * 2)));
     }
     lds_char* const sd = st + L::XB;
 #pragma unroll
-    for (int k = 0; k < TP / 2; ++k) {
-      const int i = wave * (TP / 2) + k;  // 1 KB piece i of the 2 TP
+    for (int q = 0; q < 2; ++q) {
+      const int i = 2 * wave + q;
       const bool first = 8 * i < a.r0;
       const int jj = 8 * i + (lane >> 3);
       const int64_t jr = first ? jj : jj - a.r0;
@@ -890,152 +902,161 @@ __global__ __launch_bounds__(64 * QR_WAVES) void k_quant_down_rows(const QuantDo
     }
   };
 
-  uint32_t sbs = 0;  // the pair's four scale bytes of this wave's block row
-  // local chunk j, position i (0, 1) in its pair
+  uint32_t sbs = 0;  // this wave's two scale bytes of the current pair (chunk 0, chunk 1)
+  // local chunk j, position i (0, 1) in its pair: this wave's column block of it
   auto work = [&](int i, int j) __attribute__((always_inline)) {
-    const lds_char* const st = stages + (j % L::STAGES) * L::STAGE;
+    const lds_char* const st = stages + (j % QR_STAGES) * L::STAGE;
     const int64_t cc = ch0 + j;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      v4i xv[2];  // rows wrow + 16g + l%16, columns 32b + 8(l/16) .. +8
-      {
-        uint32_t ad[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const int row = wrow + 16 * g + lr;
-          ad[g] = lds_addr(st + row * 128 + (((4 * b + lq) ^ sq_swz(row)) << 4));
-        }
-        lds_read16x2(ad, xv);
-      }
-      float hv[2][8];
-      if constexpr (MODE == QD_GELU_QUANT) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const uint32_t ws[4] = {(uint32_t)xv[g].x, (uint32_t)xv[g].y, (uint32_t)xv[g].z, (uint32_t)xv[g].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            hv[g][2 * e] = gelu_f(bf16_lo(ws[e]));
-            hv[g][2 * e + 1] = gelu_f(bf16_hi(ws[e]));
-          }
-        }
-        // optional export of the fp32 H that Q(H) quantizes: extra operations ahead of
-        // the pair's stores only make the waits stricter
-        if (a.hdbg != nullptr) {
-          const bufres rh = make_buf(a.hdbg, (uint64_t)a.M * a.K * 4);
-          const int64_t col = cc * CHUNK + 32 * b + 8 * lq;
-#pragma unroll
-          for (int g = 0; g < 2; ++g) {
-            const int64_t row = r0 + wrow + 16 * g + lr;
-            const uint32_t off = sel_off(cc < ch1 && row < a.M && col < a.K, (uint32_t)((row * a.K + col) * 4));
-            buf_store16(rh, off, __builtin_bit_cast(v4i, v4f{hv[g][0], hv[g][1], hv[g][2], hv[g][3]}));
-            buf_store16(rh, off + 16, __builtin_bit_cast(v4i, v4f{hv[g][4], hv[g][5], hv[g][6], hv[g][7]}));
-          }
-        }
-      }
-      v4i dv[TP];
-      read_lowrank<TP, false>(st + L::XB, b, lane, ta, a.r0, r1, a.rt, dv);
+    const int b = bsel;
+    v4i xv[2];  // rows wrow + 16g + l%16, columns 32b + 8(l/16) .. +8
+    {
+      uint32_t ad[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        v4i xop;
-        if constexpr (MODE == QD_GELU_QUANT)
-          xop = v4i{(int)pack_bf16x2(hv[g][0], hv[g][1]), (int)pack_bf16x2(hv[g][2], hv[g][3]),
-                    (int)pack_bf16x2(hv[g][4], hv[g][5]), (int)pack_bf16x2(hv[g][6], hv[g][7])};
-        else
-          xop = xv[g];
-#pragma unroll
-        for (int t = 0; t < TP; ++t) acc[g][t] = mfma16(dv[t], xop, acc[g][t]);
+        const int row = wrow + 16 * g + lr;
+        ad[g] = lds_addr(st + row * 128 + (((4 * b + lq) ^ sq_swz(row)) << 4));
       }
-      if constexpr (QUANT) {
-        uint32_t m = 0;
+      lds_read16x2(ad, xv);
+    }
+    float hv[2][8];
+    if constexpr (MODE == QD_GELU_QUANT) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const uint32_t ws[4] = {(uint32_t)xv[g].x, (uint32_t)xv[g].y, (uint32_t)xv[g].z, (uint32_t)xv[g].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          hv[g][2 * e] = gelu_f(bf16_lo(ws[e]));
+          hv[g][2 * e + 1] = gelu_f(bf16_hi(ws[e]));
+        }
+      }
+      // optional export of the fp32 H that Q(H) quantizes: extra operations ahead of
+      // the pair's stores only make the waits stricter
+      if (a.hdbg != nullptr) {
+        const bufres rh = make_buf(a.hdbg, (uint64_t)a.M * a.K * 4);
+        const int64_t col = cc * CHUNK + 32 * b + 8 * lq;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          if constexpr (MODE == QD_GELU_QUANT) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m = umax(m, __builtin_bit_cast(uint32_t, hv[g][e]) & 0x7FFFFFFFu);
-          } else {
-            const v4i w = xv[g];
-            m = umax(m, umax(umax(bf16x2_absmax_bits(w.x), bf16x2_absmax_bits(w.y)),
-                             umax(bf16x2_absmax_bits(w.z), bf16x2_absmax_bits(w.w))));
-          }
+          const int64_t row = r0 + wrow + 16 * g + lr;
+          const uint32_t off = sel_off(cc < ch1 && row < a.M && col < a.K, (uint32_t)((row * a.K + col) * 4));
+          buf_store16(rh, off, __builtin_bit_cast(v4i, v4f{hv[g][0], hv[g][1], hv[g][2], hv[g][3]}));
+          buf_store16(rh, off + 16, __builtin_bit_cast(v4i, v4f{hv[g][4], hv[g][5], hv[g][6], hv[g][7]}));
         }
-        const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
-        const float scale = e8m0_to_f32_scale(sb);
-        sbs |= sb << (8 * (2 * i + b));
+      }
+    }
+    v4i dv[TP];
+    read_lowrank<TP, false>(st + L::XB, b, lane, ta, a.r0, r1, a.rt, dv);
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          uint32_t cw;
-          if constexpr (MODE == QD_GELU_QUANT) {
-            cw = cvt8_f32(hv[g], scale);
-          } else {
-            const v4i w = xv[g];
-            cw = cvt8_bf16(w.x, w.y, w.z, w.w, scale);
-          }
-          if (sb == 0xFFu) cw = 0;
-          const int row = 16 * g + lr;
-          const uint32_t ad = lds_addr(cbuf + row * 64 + (((2 * i + b) ^ ((row >> 2) & 3)) << 4) + 4 * lq);
-          asm volatile("ds_write_b32 %0, %1" ::"v"(ad), "v"(cw) : "memory");
+    for (int g = 0; g < 2; ++g) {
+      v4i xop;
+      if constexpr (MODE == QD_GELU_QUANT)
+        xop = v4i{(int)pack_bf16x2(hv[g][0], hv[g][1]), (int)pack_bf16x2(hv[g][2], hv[g][3]),
+                  (int)pack_bf16x2(hv[g][4], hv[g][5]), (int)pack_bf16x2(hv[g][6], hv[g][7])};
+      else
+        xop = xv[g];
+#pragma unroll
+      for (int t = 0; t < TP; ++t) acc[g][t] = mfma16(dv[t], xop, acc[g][t]);
+    }
+    if constexpr (QUANT) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        if constexpr (MODE == QD_GELU_QUANT) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m = umax(m, __builtin_bit_cast(uint32_t, hv[g][e]) & 0x7FFFFFFFu);
+        } else {
+          const v4i w = xv[g];
+          m = umax(m, umax(umax(bf16x2_absmax_bits(w.x), bf16x2_absmax_bits(w.y)),
+                           umax(bf16x2_absmax_bits(w.z), bf16x2_absmax_bits(w.w))));
         }
+      }
+      const uint32_t sb = scale_byte_from_amax(wave_max_u32(m));
+      const float scale = e8m0_to_f32_scale(sb);
+      sbs = i == 0 ? sb : (sbs | (sb << 8));
+      lds_char* const cb = cbuf(j >> 1);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        uint32_t cw;
+        if constexpr (MODE == QD_GELU_QUANT) {
+          cw = cvt8_f32(hv[g], scale);
+        } else {
+          const v4i w = xv[g];
+          cw = cvt8_bf16(w.x, w.y, w.z, w.w, scale);
+        }
+        if (sb == 0xFFu) cw = 0;
+        const int row = 16 * g + lr;
+        const uint32_t ad = lds_addr(cb + row * 64 + (((2 * i + b) ^ ((row >> 2) & 3)) << 4) + 4 * lq);
+        asm volatile("ds_write_b32 %0, %1" ::"v"(ad), "v"(cw) : "memory");
       }
     }
   };
 
-  // codes of trip k's two chunks: 64 contiguous bytes of each of the wave's 32 rows
+  // codes of pair k (both waves of the row group wrote them before the last barrier):
+  // this wave stores rows 16 bsel .. +16 of the group, 64 contiguous bytes each, and its
+  // own two scale bytes (blocks bsel and 2 + bsel of the pair's four)
   auto store_pair = [&](int k) __attribute__((always_inline)) {
     const int64_t pc = (ch0 + 2 * k) * CHUNK;
-    uint32_t ad[2];
-    v4i cv[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = 16 * q + (lane >> 2), u = lane & 3;
-      ad[q] = lds_addr(cbuf + row * 64 + ((u ^ ((row >> 2) & 3)) << 4));
-    }
-    lds_read16x2(ad, cv);
-    const int u = lane & 3;
+    const int row = 16 * bsel + (lane >> 2), u = lane & 3;
+    const v4i cv = lds_read16(lds_addr(cbuf(k) + row * 64 + ((u ^ ((row >> 2) & 3)) << 4)));
     const bool uok = ch0 + 2 * k + (u >> 1) < ch1 && pc + 32 * u < a.K;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = wrow + 16 * q + (lane >> 2);
-      buf_store16(rcodes, sel_off(uok && row < rows_left, (uint32_t)((r0 + row) * cpitch + (pc >> 1) + 16 * u)),
-                  cv[q]);
-    }
-    const uint32_t v = (sbs >> (8 * u)) & 0xFFu;
-    const bool sok = lane < 4 && r0 + wrow < a.M && ch0 + 2 * k + (u >> 1) < ch1 && pc + 32 * u < a.K;
-    buf_store1(rscales, sel_off(sok, (uint32_t)(((r0 + wrow) / 32) * nkb + (pc >> 5) + u)), v);
+    buf_store16(rcodes,
+                sel_off(uok && wrow + row < rows_left, (uint32_t)((r0 + wrow + row) * cpitch + (pc >> 1) + 16 * u)),
+                cv);
+    const int e = 2 * (lane & 1) + bsel;  // lanes 0, 1: chunk 0, 1 of the pair
+    const uint32_t v = (sbs >> (8 * (lane & 1))) & 0xFFu;
+    const bool sok = lane < 2 && r0 + wrow < a.M && ch0 + 2 * k + (lane & 1) < ch1 && pc + 32 * e < a.K;
+    buf_store1(rscales, sel_off(sok, (uint32_t)(((r0 + wrow) / 32) * nkb + (pc >> 5) + e)), v);
   };
 
   // the issue sequence of the AHEAD chunks before the first: as if issued by chunks
-  // -AHEAD .. -1, the odd ones of which end with a pair's stores
+  // -AHEAD .. -1, the even ones of which are followed by a pair's stores
 #pragma unroll
   for (int j = 0; j < AHEAD; ++j) {
     dma(j);
     if constexpr (NS > 0)
-      if (((j - AHEAD) & 1) != 0) dummy_stores();
+      if (((j - AHEAD) & 1) == 0) dummy_stores();
   }
   for (int k = 0; k < trips; ++k) {
-    sbs = 0;
     wait_vmcnt<WAIT_EVEN>();  // this wave's loads of chunk 2k landed
-    asm volatile("s_barrier" ::: "memory");  // and every wave's; stage of chunk 2k - 1 read
+    // and every wave's (the barrier); the stage of chunk 2k - 1 is read and the codes
+    // of pair k - 1 written
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     dma(2 * k + AHEAD);
+    if constexpr (NS > 0) {
+      if (k == 0) dummy_stores();
+      else store_pair(k - 1);
+    }
     work(0, 2 * k);
     wait_vmcnt<WAIT_ODD>();
-    asm volatile("s_barrier" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     dma(2 * k + 1 + AHEAD);
     work(1, 2 * k + 1);
-    if constexpr (NS > 0) store_pair(k);
   }
   wait_vmcnt<0>();  // no direct-to-LDS load may outlive the workgroup
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (NS > 0)
+    if (trips > 0) store_pair(trips - 1);
 
-  // this wave's [32 x rt] result: bf16 once, or this range's fp32 partial
+  // the row group's [32 x rt] result: the second column block's sums meet the first's
+  // in LDS (the stages are free), then bf16 once, or this range's fp32 partial
   // acc[g][t] register r of lane l: row wrow + 16g + l%16, column 16t + 4(l/16) + r
+  v4f* red = reinterpret_cast<v4f*>(smem_raw);
+  if (bsel == 1) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int t = 0; t < TP; ++t) red[((rw * 2 + g) * TP + t) * 64 + lane] = acc[g][t];
+  }
+  __syncthreads();
+  if (bsel == 1) return;
   float* part = a.partials + ((int64_t)split * a.M) * a.rt;
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int t = 0; t < TP; ++t) {
+      const v4f v = acc[g][t] + red[((rw * 2 + g) * TP + t) * 64 + lane];
       const int64_t orow = r0 + wrow + 16 * g + lr;
       const int col = 16 * t + 4 * lq;
       if (orow < a.M && col < a.rt) {
-        const v4f v = acc[g][t];
         if (S > 1)
           *reinterpret_cast<v4f*>(part + orow * a.rt + col) = v;
         else
