@@ -120,6 +120,8 @@ ROW_SPLIT_CASES = [
     (16390, 256, 256, 64, 48, "bf16"),   # width 112: a padding tile, a 6-row last stripe
     (16384, 256, 1024, 64, 64, "fp32"),  # fp32 input: the register kernel, two ranges
     (4100, 256, 2080, 64, 32, "bf16"),   # 33 stripes in 4 column ranges of 9 chunks (odd)
+    (4100, 256, 320, 0, 96, "bf16"),     # width 96 from the stabilizer alone (empty first factor)
+    (4100, 256, 320, 96, 0, "bf16"),     # width 96 from LoRA alone (empty second factor)
 ]
 
 
