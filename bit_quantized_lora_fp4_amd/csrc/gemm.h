@@ -166,8 +166,8 @@ hipError_t launch_up_add(const UpAddArgs& a, bool bwd, bool out_bf16, hipStream_
 // h = bf16(GELU(p)), dp = bf16(dh * GELU'(p)) over n elements (n a multiple of 8)
 hipError_t launch_gelu(const bf16_t* p, bf16_t* h, int64_t n, hipStream_t stream);
 hipError_t launch_gelu_bwd(const bf16_t* p, const bf16_t* dh, bf16_t* dp, int64_t n, hipStream_t stream);
-int lora_grad_splits(int64_t M, int64_t K, int64_t N);
-int lora_grad_tiles(int64_t K, int64_t N);
+int lora_grad_splits(int64_t M, int64_t K, int64_t N, int r);
+int lora_grad_tiles(int64_t M, int64_t K, int64_t N, int r);
 size_t lora_grad_partial_bytes(int64_t M, int64_t K, int64_t N, int r);
 
 }  // namespace ft
