@@ -276,7 +276,7 @@ ft_status run_gemm_fwd(const ft_linear* L, const uint8_t* xq_codes, const uint8_
 
 ft_status run_gemm_bwd(const ft_linear* L, const uint8_t* gq_codes, const uint8_t* gq_scales,
                        const void* gb, int64_t m, void* dx, ft_dtype dx_dt, hipStream_t st,
-                       const Epi& e = Epi()) {
+                       const Epi& e = Epi(), const ft::LoraReduce& tail = ft::LoraReduce{}) {
   ft::GemmArgs g{};
   g.a_codes = gq_codes; g.a_scales = gq_scales;
   g.b_codes = L->r.codes; g.b_scales = L->r.scales; g.b_pitch = L->k / 2;
@@ -288,6 +288,7 @@ ft_status run_gemm_bwd(const ft_linear* L, const uint8_t* gq_codes, const uint8_
   g.out = dx; g.ldo = L->k;
   g.epi = e.kind; g.pre = static_cast<const ft::bf16_t*>(e.pre); g.q_codes = e.q_codes; g.q_scales = e.q_scales;
   g.dbg = e.dbg;
+  g.tail = tail;
   return hip_check(ft::launch_gemm_mx4(g, true, dx_dt == FT_BF16, st), "gemm_bwd");
 }
 
@@ -322,7 +323,8 @@ size_t lg_partials(int64_t m, const ft_linear* L) {
 // LoRA gradients of one linear: dA = GB_A^T bf16(x) (or bf16(GELU(x))), dB = bf16(g)^T XL_A.
 ft_status run_lora_grad(const ft_linear* L, int64_t m, const void* gb, const void* x, bool x_bf16, bool gelu_x,
                         const void* xl, const void* g, bool g_bf16, float* dA, float* dB, float* partials,
-                        hipStream_t st, const char* what) {
+                        hipStream_t st, const char* what, ft::LoraReduce* deferred = nullptr) {
+  if (deferred) *deferred = ft::LoraReduce{};
   if (L->rank == 0) return FT_OK;
   const int64_t rt = L->rank + L->stab_rank;
   ft::LoraGradArgs lg{};
@@ -330,7 +332,7 @@ ft_status run_lora_grad(const ft_linear* L, int64_t m, const void* gb, const voi
   lg.gb = static_cast<const ft::bf16_t*>(gb); lg.ld_gb = rt; lg.x = x; lg.x_bf16 = x_bf16; lg.K = L->k; lg.dA = dA;
   lg.xl = static_cast<const ft::bf16_t*>(xl); lg.ld_xl = rt; lg.g = g; lg.g_bf16 = g_bf16; lg.N = L->n; lg.dB = dB;
   lg.partials = partials; lg.gelu_x = gelu_x;
-  return hip_check(ft::launch_lora_grad(lg, st), what);
+  return hip_check(ft::launch_lora_grad(lg, st, deferred), what);
 }
 
 // Argument checks of the linear forward (shared by the workspace and scratch forms).
@@ -458,8 +460,9 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
   qd.ut = lay.ut;
   TRY(hip_check(ft::launch_quant_down(qd, dy_dt == FT_BF16, st), "linear_bwd quant_down"));
 
-  TRY(run_gemm_bwd(L, gq_codes, gq_scales, lay.GB, m, dx, dx_dt, st));
-
+  // The LoRA gradients go first (they need GB, not dX); their row-range sum then runs
+  // as extra workgroups of the transposed GEMM's launch instead of a launch of its own.
+  ft::LoraReduce tail{};
   if (L->rank > 0) {
     ft::LoraGradArgs lg{};
     lg.M = m; lg.r = (int)L->rank;
@@ -467,8 +470,9 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const void* dy, ft_dtype dy_dt
     lg.xl = static_cast<const ft::bf16_t*>(xl_saved); lg.ld_xl = rt; lg.g = dy;
     lg.g_bf16 = dy_dt == FT_BF16; lg.N = L->n; lg.dB = d_lora_b;
     lg.partials = lay.partials;
-    TRY(hip_check(ft::launch_lora_grad(lg, st), "linear_bwd lora_grad"));
+    TRY(hip_check(ft::launch_lora_grad(lg, st, &tail), "linear_bwd lora_grad"));
   }
+  TRY(run_gemm_bwd(L, gq_codes, gq_scales, lay.GB, m, dx, dx_dt, st, Epi(), tail));
   return ok();
 }
 
@@ -661,12 +665,16 @@ ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const voi
   e.kind = ft::GEMM_EPI_DGELU_Q; e.pre = pre_saved; e.q_codes = dpq_codes; e.q_scales = dpq_scales;
   e.dbg = dp_debug;
   TRY(run_gemm_bwd(fc2, lay.gq_codes, lay.gq_scales, lay.gb2, m, lay.dp, FT_BF16, st, e));
-  TRY(run_lora_grad(fc2, m, lay.gb2, pre_saved, true, true, hl2_saved, dy, dy_dt == FT_BF16, d_a2, d_b2,
-                    lay.partials, st, "mlp_bwd lora_grad(fc2)"));
   if (fc1->rank + fc1->stab_rank > 0)
     TRY(run_quant_down(ft::QD_DOWN, fc1, false, lay.dp, true, m, fdim, nullptr, nullptr, lay.gb1, lay.partials, st,
                        "mlp_bwd down(dP)", nullptr, lay.ut));
-  TRY(run_gemm_bwd(fc1, dpq_codes, dpq_scales, lay.gb1, m, dx, dx_dt, st));
+  // FC2's LoRA gradients after the down-projection of dP (both use the partials
+  // scratch; the down-projection's are consumed by its own sum), their row-range sum
+  // as extra workgroups of FC1's transposed GEMM
+  ft::LoraReduce tail{};
+  TRY(run_lora_grad(fc2, m, lay.gb2, pre_saved, true, true, hl2_saved, dy, dy_dt == FT_BF16, d_a2, d_b2,
+                    lay.partials, st, "mlp_bwd lora_grad(fc2)", &tail));
+  TRY(run_gemm_bwd(fc1, dpq_codes, dpq_scales, lay.gb1, m, dx, dx_dt, st, Epi(), tail));
   TRY(run_lora_grad(fc1, m, lay.gb1, x, x_dt == FT_BF16, false, xl1_saved, lay.dp, true, d_a1, d_b1,
                     lay.partials, st, "mlp_bwd lora_grad(fc1)"));
   return ok();

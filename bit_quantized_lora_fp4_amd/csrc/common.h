@@ -236,4 +236,24 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return umax(q[0], q[1]);
 }
 
+// p[0] + p[stride] + ... + p[(S-1) stride] (S >= 1), added in range order. The loads
+// go out in batches of four before any add waits, so the ranges cost one memory round
+// trip per batch instead of one per range: a batch's loads past the last range repeat
+// the last range's address (no branches, which would make the compiler wait at each
+// one), and the adds of those are selected away.
+__device__ __forceinline__ v4f sum_ranges(const v4f* __restrict__ p, int S, int64_t stride) {
+  v4f s = p[0];
+  for (int b = 1; b < S; b += 4) {
+    v4f t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) t[u] = p[(int64_t)min(b + u, S - 1) * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const v4f n = s + t[u];
+      s = b + u < S ? n : s;
+    }
+  }
+  return s;
+}
+
 }  // namespace ft

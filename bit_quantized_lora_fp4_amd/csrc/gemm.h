@@ -16,6 +16,37 @@ namespace ft {
 //             D row j = up0 row j (j < up_split) or up1 row j - up_split, row strides
 //             up0_ld / up1_ld ([A; L1]: up0 = A, up1 = L1)
 // A and R are MXFP4 (codes + 32x32-block E8M0 scales).
+// The LoRA gradients' row-range sum: dA [r x K] and dB [N x r] from the S fp32 partials
+// k_lora_grad leaves (one [rp x q] tile per q output columns, dA tiles first; range sp
+// of tile t at (sp * ntiles + t) * rp * q floats). Run by k_lora_reduce, or by extra
+// workgroups appended to the backward GEMM's launch (which needs none of it and leaves
+// CUs idle when its tile count is not a multiple of 256).
+struct LoraReduce {
+  const float* partials;
+  float* dA;
+  float* dB;
+  int64_t K, N;
+  int r, S, rp, q, ntiles;
+  int64_t items;  // v4f outputs (tile elements / 4 over all tiles); 0: no reduction
+};
+
+// Output v4f i of the sum: the partials of all S ranges in range order.
+__device__ __forceinline__ void lora_reduce_item(const LoraReduce& t, int64_t i) {
+  const int ne4 = t.rp * t.q / 4;
+  const int tile = (int)(i / ne4), idx = 4 * (int)(i % ne4);
+  const int tilesA = (int)((t.K + t.q - 1) / t.q);
+  const bool jobA = tile < tilesA;
+  const int64_t q0 = (int64_t)(jobA ? tile : tile - tilesA) * t.q;
+  const int64_t nbig = jobA ? t.K : t.N;
+  int p, q;
+  if (jobA) { p = idx / t.q; q = idx % t.q; }
+  else { q = idx / t.rp; p = idx % t.rp; }
+  if (p >= t.r || q0 + q >= nbig) return;
+  const v4f s = sum_ranges(reinterpret_cast<const v4f*>(t.partials) + i, t.S, (int64_t)t.ntiles * ne4);
+  if (jobA) *reinterpret_cast<v4f*>(t.dA + (int64_t)p * t.K + q0 + q) = s;
+  else *reinterpret_cast<v4f*>(t.dB + (q0 + q) * t.r + p) = s;
+}
+
 struct GemmArgs {
   const uint8_t* a_codes;   // [M x Kred/2]
   const uint8_t* a_scales;  // [ceil(M/32) x Kred/32]
@@ -42,6 +73,8 @@ struct GemmArgs {
   uint8_t* q_codes;         // [M x N/2]
   uint8_t* q_scales;        // [ceil(M/32) x N/32]
   float* dbg;               // optional: the fp32 dP that Q(dP) quantized, [M x N]
+  // optional work for workgroups past the output tiles (backward only; items = 0: none)
+  LoraReduce tail;
 };
 
 enum { GEMM_EPI_NONE = 0, GEMM_EPI_DGELU_Q = 2 };
@@ -124,7 +157,9 @@ struct LoraGradArgs {
   int ntiles;
 };
 
-hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream);
+// With `deferred` non-null the row-range sum is not launched: *deferred describes it
+// (items = 0 when there is none), for the caller to hand to the backward GEMM.
+hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream, LoraReduce* deferred = nullptr);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 
 // 16-bit activation x 4-bit weight GEMM (precision variants W4A16 / G16):

@@ -216,8 +216,15 @@ __global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g
   const int wm = wave / NWN, wn = wave % NWN;  // wave's half of the tile rows, its column slice
   const int half = lane >> 5;               // which 32-element half of a 64-step this lane holds
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
+  const int ntile = tiles_m * tiles_n;
+  if ((int)blockIdx.x >= ntile) {
+    // a workgroup past the output tiles: its share of the LoRA-gradient row-range sum
+    const int64_t nthr = (int64_t)(gridDim.x - ntile) * NT;
+    for (int64_t i = (int64_t)(blockIdx.x - ntile) * NT + tid; i < g.tail.items; i += nthr) lora_reduce_item(g.tail, i);
+    return;
+  }
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_of(blockIdx.x, ntile, tiles_m, tiles_n, tm, tn);
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t Kred = g.Kred;
   const int KT = (int)((Kred + BK - 1) / BK);
@@ -855,6 +862,19 @@ __global__ __launch_bounds__(Waves<NWN>::NT, 1) void k_gemm_mx4(const GemmArgs g
 
 static_assert(GEMM_MAX_KRED == MAX_NKB * 32, "scale staging bound");
 
+// Workgroups appended for the LoRA-gradient sum: one per CU the tiles leave idle in
+// their last round (the tiles take one CU each; 256 CUs), so the sum runs beside the
+// tiles; when that leaves fewer than 16, up to 64 that run as tiles finish. At most one
+// output per thread.
+int tail_workgroups(int tiles, int64_t items) {
+  if (items <= 0) return 0;
+  constexpr int NUM_CU = 256;
+  const int idle = (NUM_CU - tiles % NUM_CU) % NUM_CU;
+  const int64_t need = (items + Waves<GEMM_NWN>::NT - 1) / Waves<GEMM_NWN>::NT;
+  const int64_t n = need < (idle >= 16 ? idle : 64) ? need : (idle >= 16 ? idle : 64);
+  return (int)(n < 1 ? 1 : n);
+}
+
 hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipStream_t stream) {
   if (g.M == 0 || g.N == 0) return hipSuccess;
   if (g.Kred < 1 || g.Kred > GEMM_MAX_KRED) return hipErrorInvalidValue;  // the last step is peeled: KT >= 1
@@ -862,7 +882,8 @@ hipError_t launch_gemm_mx4(const GemmArgs& g, bool trans_b, bool out_bf16, hipSt
                                  g.q_scales == nullptr || g.pre == nullptr))
     return hipErrorInvalidValue;
   const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
-  dim3 grid(tiles), block(Waves<GEMM_NWN>::NT);
+  if (g.tail.items > 0 && !trans_b) return hipErrorInvalidValue;
+  dim3 grid(tiles + tail_workgroups(tiles, g.tail.items)), block(Waves<GEMM_NWN>::NT);
   if (g.epi == GEMM_EPI_DGELU_Q) {
     hipLaunchKernelGGL((k_gemm_mx4<true, true, GEMM_EPI_DGELU_Q, GEMM_NWN>), grid, block, 0, stream, g);
   } else if (!trans_b) {

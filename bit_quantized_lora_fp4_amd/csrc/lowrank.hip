@@ -244,25 +244,9 @@ __global__ __launch_bounds__(256) void k_lora_grad(const LoraGradArgs a) {
 
 // Sum of the S row-range partials of every tile, in range order (same element order
 // as k_lora_grad's tiles), written to dA / dB.
-__global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs a, int S, int rp, int LG_Q) {
-  const int ne4 = rp * LG_Q / 4;
+__global__ __launch_bounds__(256) void k_lora_reduce(const LoraReduce t) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)a.ntiles * ne4) return;
-  const int tile = (int)(i / ne4), idx = 4 * (int)(i % ne4);
-  const int tilesA = (int)((a.K + LG_Q - 1) / LG_Q);
-  const bool jobA = tile < tilesA;
-  const int64_t q0 = (int64_t)(jobA ? tile : tile - tilesA) * LG_Q;
-  const int64_t nbig = jobA ? a.K : a.N;
-  int p, q;
-  if (jobA) { p = idx / LG_Q; q = idx % LG_Q; }
-  else { q = idx / rp; p = idx % rp; }
-  if (p >= a.r || q0 + q >= nbig) return;
-  const v4f* pv = reinterpret_cast<const v4f*>(a.partials);
-  const int64_t stride = (int64_t)a.ntiles * ne4;
-  v4f s = pv[i];
-  for (int sp = 1; sp < S; ++sp) s += pv[sp * stride + i];
-  if (jobA) *reinterpret_cast<v4f*>(a.dA + (int64_t)p * a.K + q0 + q) = s;
-  else *reinterpret_cast<v4f*>(a.dB + (q0 + q) * a.r + p) = s;
+  if (i < t.items) lora_reduce_item(t, i);
 }
 
 template <bool BIG_BF16>
@@ -335,7 +319,8 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream) {
+hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream, LoraReduce* deferred) {
+  if (deferred) *deferred = LoraReduce{};
   if (a.r == 0 || a.M == 0) return hipSuccess;
   const int S = lora_grad_splits(a.M, a.K, a.N, a.r);
   const int LG_Q = lg_q_for(a.M, a.r);
@@ -358,9 +343,23 @@ hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t stream) {
                  : launch_t<false>(b, LG_Q, dim3((unsigned)(tiles - tilesA), (unsigned)S), stream);
   }
   if (e != hipSuccess || S == 1) return e;
-  const int rp = (a.r + 31) / 32 * 32;
-  const int64_t items = (int64_t)tiles * rp * LG_Q / 4;
-  hipLaunchKernelGGL(k_lora_reduce, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, b, S, rp, LG_Q);
+  LoraReduce t{};
+  t.partials = a.partials;
+  t.dA = a.dA;
+  t.dB = a.dB;
+  t.K = a.K;
+  t.N = a.N;
+  t.r = a.r;
+  t.S = S;
+  t.rp = (a.r + 31) / 32 * 32;
+  t.q = LG_Q;
+  t.ntiles = tiles;
+  t.items = (int64_t)tiles * t.rp * LG_Q / 4;
+  if (deferred) {
+    *deferred = t;
+    return hipSuccess;
+  }
+  hipLaunchKernelGGL(k_lora_reduce, dim3((unsigned)((t.items + 255) / 256)), dim3(256), 0, stream, t);
   return hipGetLastError();
 }
 

@@ -1071,9 +1071,7 @@ __global__ __launch_bounds__(256) void k_sum_partials(const float* __restrict__ 
                                                       bf16_t* __restrict__ low) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one v4f of [M x rt]
   if (i >= n4) return;
-  const v4f* pv = reinterpret_cast<const v4f*>(partials);
-  v4f s = pv[i];
-  for (int sp = 1; sp < S; ++sp) s += pv[sp * n4 + i];
+  const v4f s = sum_ranges(reinterpret_cast<const v4f*>(partials) + i, S, n4);
   *reinterpret_cast<uint2*>(low + 4 * i) = make_uint2(pack_bf16x2(s.x, s.y), pack_bf16x2(s.z, s.w));
 }
 
