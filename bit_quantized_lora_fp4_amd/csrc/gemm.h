@@ -129,8 +129,8 @@ size_t quant_down_partial_bytes(int64_t M, int64_t K, int r0, int rt);
 // LoRA parameter gradients, reductions over the M rows (FourTune §3.2: parameter updates
 // only for the adapter):
 //   dA[r x K] = GB[:, :r]^T * bf16(X)      dB[N x r] = bf16(G)^T * XL[:, :r]
-// Split over M; each split writes fp32 partials and a second kernel sums them in a
-// fixed order (deterministic).
+// Split over M; each split writes fp32 partials, summed afterwards in a fixed order
+// (deterministic; LoraReduce).
 // X and G must each be smaller than 4 GiB (32-bit buffer offsets).
 struct LoraGradArgs {
   int64_t M;

@@ -14,7 +14,8 @@
 // row-major in m, but the MFMA reduces over m inside a lane, so a wave writes its slab
 // into a private LDS area and reads it back transposed (ds_read_b64_tr_b16). At the
 // end the four waves' sums meet in LDS in wave order; with S > 1 the range sums go to
-// an fp32 partial buffer and a second kernel adds the S partials in range order. The
+// an fp32 partial buffer and the S partials are added in range order afterwards, by
+// k_lora_reduce or by extra workgroups of the backward GEMM's launch (LoraReduce). The
 // result is independent of timing.
 #include "common.h"
 #include "gemm.h"
