@@ -7,9 +7,11 @@ the same gradient kernel and adds the partials with a launch of its own; both ad
 ranges in range order from the same partials, so dA and dB must agree bit for bit.
 
 Shapes: the GEMM's tiles (256 x 256 over M x K) leaving most CUs idle (the extra
-workgroups run beside the tiles), and exactly 256 tiles (none idle: the extra
-workgroups start as tiles finish). rank + stab_rank = 64 keeps both backward forms
-on the same down-projection kernel, so GB, and with it the partials, are identical.
+workgroups run beside the tiles), exactly 256 tiles (none idle: the extra workgroups
+start as tiles finish), the 128-column gradient tiles used from 8192 rows, and fp32 X
+with bf16 dY (the dA and dB tiles are then two launches sharing one sum). rank +
+stab_rank <= 64 keeps both backward forms on the same down-projection kernel, so GB,
+and with it the partials, are identical.
 The values themselves are checked against the oracle by the linear parity tests.
 """
 import numpy as np
@@ -24,18 +26,20 @@ from tests.sampling import _gpu_lin
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # m, n, k, r, s: the backward GEMM's tiles (m/256 x k/256) and the gradient split
-    (1024, 1024, 1024, 32, 32),   # 16 tiles, 240 CUs idle; 6 row ranges
-    (2048, 512, 8192, 32, 32),    # 256 tiles, none idle; 2 row ranges
+    # m, n, k, r, s, x dtype: the backward GEMM's tiles (m/256 x k/256) and the gradient split
+    (1024, 1024, 1024, 32, 32, "bf16"),   # 16 tiles, 240 CUs idle; 6 row ranges
+    (2048, 512, 8192, 32, 32, "bf16"),    # 256 tiles, none idle; 2 row ranges
+    (8192, 512, 1024, 32, 32, "bf16"),    # 128-column gradient tiles (from 8192 rows)
+    (1024, 512, 768, 16, 16, "fp32"),     # fp32 X, bf16 dY: dA and dB tiles in two launches
 ]
 
 
-@pytest.mark.parametrize("m,n,k,r,s", CASES)
-def test_lora_sum_in_gemm_launch_matches_own_launch(m, n, k, r, s):
-    log(f"lora-gradient sum in the GEMM launch: m={m} n={n} k={k} r={r} s={s}")
-    d = wl.random_linear(m, n, k, r, s, seed=7 + m + k)
+@pytest.mark.parametrize("m,n,k,r,s,xdt", CASES)
+def test_lora_sum_in_gemm_launch_matches_own_launch(m, n, k, r, s, xdt):
+    log(f"lora-gradient sum in the GEMM launch: m={m} n={n} k={k} r={r} s={s} x={xdt}")
+    d = wl.random_linear(m, n, k, r, s, seed=7 + m + k, x_dtype=xdt)
     L = _gpu_lin(d)
-    x, dy = dev(d["X"]), dev(d["dY"])
+    x, dy = dev(d["X"], xdt), dev(d["dY"])
     _, xl = abi.linear_forward(L, x)
     dx, da, db = abi.linear_backward(L, dy, x, xl)
 
